@@ -1,0 +1,440 @@
+"""Pins for the oracle codec against facts that do not come from the oracle itself:
+IEEE-754 field semantics, brute force on tiny inputs, a hand-worked tile, textbook
+Huffman (heap construction), exhaustive search for optimal length-limited codes, the
+Kraft equality, the entropy bound, and string-built bitstreams."""
+import heapq
+import itertools
+import math
+import os
+from collections import Counter
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+from oracle import codec
+from lossless_bf16_weight_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ------------------------------------------------------------------ field split
+def test_split_merge_exhaustive_bijection():
+    allw = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    e, sm = codec.split_fields(allw)
+    assert np.array_equal(codec.merge_fields(e, sm), allw)
+    # (e, sm) pairs are all distinct: the split is a bijection onto 256 x 256
+    assert len(np.unique(e.astype(np.uint32) * 256 + sm)) == 65536
+
+
+def test_split_matches_ieee_semantics():
+    """Exponent byte and sign against what float32 arithmetic says about the value."""
+    allw = np.arange(65536, dtype=np.uint32)
+    with np.errstate(invalid="ignore"):
+        v = (allw << 16).astype(np.uint32).view(np.float32).astype(np.float64)
+    e, sm = codec.split_fields(allw.astype(np.uint16))
+    sign = sm >> 7
+    finite = np.isfinite(v)
+    assert np.array_equal(sign[finite] == 1, np.signbit(v[finite]))
+    assert np.all(e[~finite] == 255)
+    normal = finite & (np.abs(v) >= 2.0 ** -126)
+    _, ex = np.frexp(np.abs(v[normal]))           # |v| = f * 2**ex, f in [0.5, 1)
+    assert np.array_equal(e[normal].astype(np.int64), ex + 126)
+    assert np.all(e[finite & ~normal] == 0)       # zeros and subnormals
+    # mantissa: |v| = (1 + m/128) * 2**(e-127) for normal values
+    m = (sm & 0x7F).astype(np.float64)
+    assert np.allclose(np.abs(v[normal]), (1 + m[normal] / 128) * 2.0 ** (e[normal].astype(np.float64) - 127), rtol=0)
+
+
+# ------------------------------------------------------------------ histogram / palette
+def test_histogram_matches_counter():
+    rng = np.random.default_rng(5)
+    e = rng.integers(0, 256, size=(37, 64)).astype(np.uint8)
+    h = codec.exponent_histogram(e)
+    c = Counter(e.ravel().tolist())
+    assert all(h[x] == c.get(x, 0) for x in range(256))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_palette_brute_force(seed):
+    """Chosen set has maximal coverage among all 16-subsets and, among those, the smallest
+    exponent sum (ties to smaller exponents); listed ascending."""
+    rng = np.random.default_rng(seed)
+    ndist = int(rng.integers(1, 21))
+    exps = rng.choice(256, size=ndist, replace=False)
+    counts = rng.integers(1, 5, size=ndist)          # many ties on purpose
+    hist = np.zeros(256, np.int64)
+    hist[exps] = counts
+    pal, index_of = codec.build_palette(hist)
+    assert list(pal) == sorted(pal)
+    assert len(pal) == min(16, ndist)
+    best_cov = max(sum(hist[list(s)]) for s in itertools.combinations(exps, len(pal)))
+    assert sum(hist[pal]) == best_cov
+    best_sum = min(sum(int(x) for x in s) for s in itertools.combinations(exps, len(pal))
+                   if sum(hist[list(s)]) == best_cov)
+    assert sum(int(x) for x in pal) == best_sum
+    for i, x in enumerate(pal):
+        assert index_of[x] == i
+    assert sum(index_of != codec.NONE) == len(pal)
+
+
+# ------------------------------------------------------------------ verbatim segments
+def _loops_verbatim(e, palette_set):
+    n, k = e.shape
+    return [[any(int(e[r, c]) not in palette_set for c in range(64 * j, 64 * j + 64))
+             for j in range(k // 64)] for r in range(n)]
+
+
+@pytest.mark.parametrize("n,k,seed", [(16, 64, 0), (21, 128, 1), (40, 192, 2), (5, 64, 3)])
+def test_verbatim_flags_brute_force(n, k, seed):
+    d = synth.small_gaussian(n, k, std=0.02, seed=seed, plant_frac=0.2)
+    w = d["w"]
+    a = codec.analyse(w, n, k)
+    pset = set(int(x) for x in a["palette"])
+    ref = _loops_verbatim(a["e"], pset)
+    assert a["verb"].tolist() == ref
+    T = codec.padded_rows(n) // 16
+    for t in range(T):
+        for b in range(k // 64):
+            expect = sum(1 << r for r in range(16) if 16 * t + r < n and ref[16 * t + r][b])
+            assert int(a["flags"][t, b]) == expect
+    # vprefix counts verbatim segments in earlier tiles
+    for t in range(T + 1):
+        expect = sum(ref[r][b] for r in range(min(16 * t, n)) for b in range(k // 64))
+        assert int(a["vprefix"][t]) == expect
+
+
+def test_verbatim_rate_matches_binomial():
+    """For i.i.d. exponents, P(segment verbatim) = 1 - (1 - q)**64 with q the fraction of
+    weights outside the palette."""
+    rng = np.random.default_rng(11)
+    w = synth.gaussian_bf16(rng, (2048, 1024), 0.02)
+    a = codec.analyse(w, 2048, 1024)
+    q = 1 - a["hist"][a["palette"]].sum() / w.size
+    p = 1 - (1 - q) ** 64
+    nseg = a["verb"].size
+    v = a["verb"].mean()
+    assert abs(v - p) < 5 * math.sqrt(p * (1 - p) / nseg) + 1e-4
+
+
+# ------------------------------------------------------------------ Huffman code lengths
+def heap_huffman_lengths(freqs):
+    """Textbook Huffman by repeatedly merging the two lightest trees."""
+    heap = [(f, i, (s,)) for i, (s, f) in enumerate((s, f) for s, f in enumerate(freqs) if f > 0)]
+    heapq.heapify(heap)
+    lengths = [0] * len(freqs)
+    if len(heap) == 1:
+        lengths[heap[0][2][0]] = 1
+        return lengths
+    uid = len(heap)
+    while len(heap) > 1:
+        f1, _, a = heapq.heappop(heap)
+        f2, _, b = heapq.heappop(heap)
+        for s in a + b:
+            lengths[s] += 1
+        heapq.heappush(heap, (f1 + f2, uid, a + b))
+        uid += 1
+    return lengths
+
+
+def cost(freqs, lengths):
+    return sum(f * L for f, L in zip(freqs, lengths))
+
+
+def kraft(lengths):
+    from fractions import Fraction
+    return sum(Fraction(1, 2 ** L) for L in lengths if L > 0)
+
+
+@settings(max_examples=300, deadline=None)
+@given(st.lists(st.integers(0, 10 ** 6), min_size=1, max_size=16))
+def test_package_merge_equals_heap_huffman_when_unconstrained(freqs):
+    if sum(1 for f in freqs if f > 0) == 0:
+        assert codec.package_merge_lengths(freqs) == [0] * len(freqs)
+        return
+    hl = heap_huffman_lengths(freqs)
+    pl = codec.package_merge_lengths(freqs, 13)
+    assert max(pl) <= 13
+    if max(hl) <= 13:
+        assert cost(freqs, pl) == cost(freqs, hl)
+    assert all((L > 0) == (f > 0) for L, f in zip(pl, freqs))
+    n = sum(1 for f in freqs if f > 0)
+    from fractions import Fraction
+    assert kraft(pl) == (1 if n >= 2 else Fraction(1, 2))
+
+
+def test_package_merge_binding_limit_exhaustive():
+    """Small alphabets and small limits: package-merge cost equals the minimum over every
+    length vector that satisfies Kraft <= 1 and the limit."""
+    rng = np.random.default_rng(3)
+    for trial in range(60):
+        n = int(rng.integers(2, 7))
+        lmax = int(rng.integers(max(2, math.ceil(math.log2(n))), 6))
+        freqs = [int(x) for x in rng.integers(1, 2 ** int(rng.integers(1, 12)), size=n)]
+        best = min(cost(freqs, ls) for ls in itertools.product(range(1, lmax + 1), repeat=n)
+                   if kraft(ls) <= 1)
+        pl = codec.package_merge_lengths(freqs, lmax)
+        assert max(pl) <= lmax and kraft(pl) <= 1
+        assert cost(freqs, pl) == best
+
+
+def test_geometric_frequencies_hit_the_limit():
+    freqs = [2 ** i for i in range(16)]              # unconstrained depth 15
+    assert max(heap_huffman_lengths(freqs)) == 15
+    pl = codec.package_merge_lengths(freqs, 13)
+    assert max(pl) == 13 and kraft(pl) == 1
+
+
+def test_entropy_bound():
+    """H(f) <= average code length < H(f) + 1 (Shannon) when the limit does not bind."""
+    rng = np.random.default_rng(7)
+    for _ in range(50):
+        freqs = [int(x) for x in rng.integers(1, 10 ** 5, size=int(rng.integers(2, 17)))]
+        pl = codec.package_merge_lengths(freqs)
+        tot = sum(freqs)
+        H = -sum(f / tot * math.log2(f / tot) for f in freqs)
+        avg = cost(freqs, pl) / tot
+        assert H - 1e-12 <= avg < H + 1
+
+
+# ------------------------------------------------------------------ canonical codes
+@settings(max_examples=200, deadline=None)
+@given(st.lists(st.integers(1, 10 ** 4), min_size=2, max_size=16))
+def test_canonical_codes_prefix_free(freqs):
+    L = codec.package_merge_lengths(freqs)
+    C = codec.canonical_codes(L)
+    strs = [format(c, "0%db" % l) for c, l in zip(C, L) if l > 0]
+    assert all(c < 2 ** l for c, l in zip(C, L))
+    for a, b in itertools.permutations(strs, 2):
+        assert not b.startswith(a)
+    # canonical: sorting by (length, symbol) sorts the codes as bit strings
+    order = sorted(range(len(L)), key=lambda s: (L[s], s))
+    as_str = [format(C[s], "0%db" % L[s]) for s in order]
+    assert as_str == sorted(as_str)
+
+
+# ------------------------------------------------------------------ bitstream
+@settings(max_examples=100, deadline=None)
+@given(st.lists(st.integers(0, 15), min_size=0, max_size=400), st.integers(0, 2 ** 31))
+def test_bitstream_vectorised_equals_string_built(symbols, seed):
+    rng = np.random.default_rng(seed)
+    freqs = [int(x) for x in rng.integers(1, 1000, size=16)]
+    L = codec.package_merge_lengths(freqs)
+    C = codec.canonical_codes(L)
+    w1, starts, t1 = codec.pack_bitstream(np.array(symbols, np.int64), L, C)
+    w2, t2 = codec.pack_bitstream_plain(symbols, L, C)
+    assert t1 == t2 and np.array_equal(w1, w2)
+    assert list(starts) == list(np.cumsum([0] + [L[s] for s in symbols])[:-1])
+    dec, end = codec.decode_sequential(w1, len(symbols), L, C)
+    assert list(dec) == list(symbols) and end == t1
+
+
+def test_lockstep_chunk_decode_equals_sequential():
+    rng = np.random.default_rng(9)
+    freqs = [int(x) for x in rng.integers(1, 5000, size=16)]
+    L = codec.package_merge_lengths(freqs)
+    C = codec.canonical_codes(L)
+    sym = rng.integers(0, 16, size=3000)
+    words, starts, total = codec.pack_bitstream(sym, L, C)
+    lens = np.array([512] * 5 + [3000 - 5 * 512])
+    off = np.concatenate([starts[np.arange(6) * 512], [total]])
+    out = codec.decode_chunks(words, off, lens, L)
+    assert np.array_equal(out, sym)
+    seq, _ = codec.decode_sequential(words, 3000, L, C)
+    assert np.array_equal(out, seq)
+    bad = off.copy()
+    bad[2] += 1
+    with pytest.raises(ValueError):
+        codec.decode_chunks(words, bad, lens, L)
+
+
+# ------------------------------------------------------------------ hand-worked tile
+def _read_golden(name):
+    out = {}
+    for line in open(os.path.join(GOLDEN, name)):
+        if line.startswith("#") or not line.strip():
+            continue
+        key, *vals = line.split()
+        out[key] = [int(v, 0) for v in vals]
+    return out
+
+
+def hand_tile():
+    w = np.zeros((16, 64), np.uint16)
+    for r in range(16):
+        for c in range(64):
+            if r < 15:
+                e = 120 if c < 32 else 121 if c < 48 else 122 if c < 56 else 123
+            else:
+                e = 100 + c if c < 17 else 116
+            sm = (7 * r + c) % 256
+            w[r, c] = ((sm >> 7) << 15) | (e << 7) | (sm & 0x7F)
+    return w
+
+
+def test_hand_worked_tile():
+    g = _read_golden("hand_tile.txt")
+    w = hand_tile()
+    enc = codec.encode(w, 16, 64, chunk=512)
+    assert list(enc["palette"]) == g["palette"]
+    assert list(enc["lengths"]) == g["lengths"]
+    assert list(enc["codes"]) == g["codes"]
+    assert int(enc["flags"][0, 0]) == g["flags"][0]
+    assert list(enc["vprefix"]) == g["vprefix"]
+    assert enc["n_verb"] == g["n_verb"][0] and enc["n_coded"] == g["n_coded"][0]
+    assert enc["total_bits"] == g["total_bits"][0] and len(enc["words"]) == g["n_words"][0]
+    assert list(enc["off"]) == g["off"] and list(enc["cbase"]) == g["cbase"]
+    assert list(enc["words"][:6]) == g["words_head"]
+    assert list(enc["vexp"]) == [100 + c if c < 17 else 116 for c in range(64)]
+    r, c, o = g["sm_offset"]
+    assert int(enc["sm"][o]) == (7 * r + c) % 256
+    blob = codec.serialize(enc)
+    r, c, byte, shift, val = g["idx_probe"]
+    idx = codec.transcode_blob(blob)
+    word = int.from_bytes(bytes(idx[byte: byte + 4]), "little")
+    assert (word >> shift) & 0xF == val
+    assert np.array_equal(codec.decode_blob(blob), w)
+
+
+# ------------------------------------------------------------------ layouts
+def test_tile_layout_offsets_by_loops():
+    rng = np.random.default_rng(2)
+    n_pad, k = 32, 128
+    a = rng.integers(0, 256, size=(n_pad, k)).astype(np.uint8)
+    flat = codec.tile_bytes(a)
+    for _ in range(200):
+        n, c = int(rng.integers(0, n_pad)), int(rng.integers(0, k))
+        off = ((n // 16 * (k // 16) + c // 16) * 16 + n % 16) * 16 + c % 16
+        assert flat[off] == a[n, c]
+    assert np.array_equal(codec.untile_bytes(flat, n_pad, k), a)
+
+
+def test_index_layout_by_loops():
+    rng = np.random.default_rng(4)
+    n_pad, k = 32, 192
+    idx = rng.integers(0, 16, size=(n_pad, k)).astype(np.uint8)
+    buf = codec.pack_indices(idx)
+    assert len(buf) == n_pad * k // 2
+    for n in range(n_pad):
+        for c in range(k):
+            t, r, j, cc = n // 16, n % 16, c // 16, c % 16
+            base = ((t * (k // 16) + j) * 16 + r) * 8 + 4 * (cc // 8)
+            word = int.from_bytes(bytes(buf[base: base + 4]), "little")
+            i = cc % 8
+            assert (word >> (4 * (i // 2) + 16 * (i % 2))) & 0xF == idx[n, c]
+    assert np.array_equal(codec.unpack_indices(buf, n_pad, k), idx)
+
+
+# ------------------------------------------------------------------ full codec round trips
+def special_matrix(n, k, seed):
+    """Every kind of BF16 value: +-0, subnormals, +-Inf, NaN payloads, extremes."""
+    rng = np.random.default_rng(seed)
+    w = synth.gaussian_bf16(rng, (n, k), 0.02)
+    specials = np.array([0x0000, 0x8000, 0x0001, 0x807F, 0x7F80, 0xFF80, 0x7FC0, 0xFFFF, 0x7F81,
+                         0x7F7F, 0xFF7F, 0x0080, 0x3F80], dtype=np.uint16)
+    pos = rng.choice(n * k, size=min(n * k, 40), replace=False)
+    w.reshape(-1)[pos] = specials[rng.integers(0, len(specials), size=len(pos))]
+    return w
+
+
+CASES = [
+    ("gauss_ragged", lambda: synth.small_gaussian(37, 192, seed=1, plant_frac=0.05)["w"]),
+    ("specials", lambda: special_matrix(19, 256, 2)),
+    ("single_exponent", lambda: np.full((16, 64), 0x3F80, np.uint16) | np.arange(64, dtype=np.uint16)[None, :]),
+    ("all_verbatim", lambda: np.arange(20 * 64, dtype=np.uint32).astype(np.uint16).reshape(20, 64) * 251),
+    ("one_row", lambda: synth.small_gaussian(1, 64, seed=3)["w"]),
+    ("wide_t", lambda: synth.student_t_bf16(np.random.default_rng(5), (48, 1024), 3, 0.02)),
+    ("uniform_bits", lambda: np.random.default_rng(6).integers(0, 65536, size=(33, 320)).astype(np.uint16)),
+]
+
+
+@pytest.mark.parametrize("name,make", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("chunk", [64, 512])
+def test_roundtrip(name, make, chunk):
+    w = make()
+    n, k = w.shape
+    enc = codec.encode(w, n, k, chunk=chunk)
+    blob = codec.serialize(enc)
+    assert np.array_equal(codec.decode_blob(blob), w)
+    d = codec.parse(blob)
+    # every chunk but a tile's last holds exactly `chunk` symbols
+    lens = codec.chunk_lengths(d)
+    assert lens.sum() == enc["n_coded"] and (len(lens) == 0 or lens.max() <= chunk)
+    # off[] is the prefix sum of code lengths at chunk starts (closed form)
+    L = np.array(enc["lengths"])
+    bits = np.concatenate([[0], np.cumsum(L[enc_symbols(w, n, k)])])
+    starts = np.concatenate([[0], np.cumsum(lens)])[:-1]
+    assert np.array_equal(enc["off"][:-1], bits[starts]) and enc["off"][-1] == enc["total_bits"]
+    # direct-palette reconstruction from the transcoded index stream
+    idx = codec.transcode_blob(blob)
+    w2 = codec.reconstruct_from_palette(d["sm"], idx, d["flags"], d["vprefix"], d["vexp"], d["palette"], n, k)
+    assert np.array_equal(w2, w)
+
+
+def enc_symbols(w, n, k):
+    return codec.analyse(w, n, k)["symbols"]
+
+
+def test_all_verbatim_has_empty_stream():
+    w = CASES[3][1]()
+    enc = codec.encode(w, 20, 64)
+    assert enc["n_coded"] == 0 and enc["total_bits"] == 0 and list(enc["off"]) == [0]
+    assert enc["n_verb"] == 20
+
+
+def test_transcode_and_exponent_streams_by_loops():
+    w = synth.small_gaussian(21, 128, seed=8, plant_frac=0.1)["w"]
+    n, k = w.shape
+    blob = codec.serialize(codec.encode(w, n, k, chunk=128))
+    a = codec.analyse(w, n, k)
+    pal = [int(x) for x in a["palette"]]
+    n_pad = codec.padded_rows(n)
+    idx = codec.unpack_indices(codec.transcode_blob(blob), n_pad, k)
+    ex = codec.untile_bytes(codec.exponent_stream_blob(blob), n_pad, k)
+    for r in range(n_pad):
+        for c in range(k):
+            if r >= n:
+                assert idx[r, c] == 0 and ex[r, c] == 0
+                continue
+            e = (int(w[r, c]) >> 7) & 0xFF
+            seg = [(int(w[r, cc]) >> 7) & 0xFF for cc in range(64 * (c // 64), 64 * (c // 64) + 64)]
+            verbatim = any(x not in pal for x in seg)
+            assert idx[r, c] == (0 if verbatim else pal.index(e))
+            assert ex[r, c] == e
+
+
+def test_config1_sizes_and_entropy():
+    """Config 1: lossless, exponent bits within one bit of the entropy of the coded
+    symbols, and the sizes follow the closed form of the section lengths."""
+    c = synth.config1()
+    w = c["w"]
+    enc = codec.encode(w, 1024, 1024)
+    blob = codec.serialize(enc)
+    assert np.array_equal(codec.decode_blob(blob), w)
+    f = np.array(enc["freqs"], np.float64)
+    p = f[f > 0] / f.sum()
+    H = -(p * np.log2(p)).sum()
+    avg = enc["total_bits"] / enc["n_coded"]
+    assert H <= avg < H + 1
+    # post: exponent information ~2.6 bits and top-16 coverage > 99 % (loose bands only)
+    a = codec.analyse(w, 1024, 1024)
+    assert 2.0 < H < 3.2
+    assert a["hist"][a["palette"]].sum() / w.size > 0.99
+    nk, T = 1024 * 1024, 1024 // 16
+    expect = (256 + nk + 2 * T * 16 + 4 * (T + 1) + 64 * enc["n_verb"] + 4 * (T + 1)
+              + 4 * len(enc["off"]) + 4 * ((enc["total_bits"] + 31) // 32 + 2))
+    assert codec.bundle_bytes(enc) == expect
+    # bits per weight: Huffman bundle below the resident palette format, both below 16
+    assert codec.bundle_bytes(enc) * 8 / nk < codec.resident_palette_bytes(enc) * 8 / nk < 16
+    assert c["planted"].size == 1
+
+
+def test_parse_rejects_corruption():
+    w = synth.small_gaussian(16, 64, seed=1)["w"]
+    blob = bytearray(codec.serialize(codec.encode(w, 16, 64)))
+    with pytest.raises(ValueError):
+        codec.parse(b"XXXX" + bytes(blob[4:]))
+    bad = bytearray(blob)
+    bad[128 + 16 * 6: 128 + 16 * 6 + 8] = (10 ** 9).to_bytes(8, "little")
+    with pytest.raises(ValueError):
+        codec.parse(bytes(bad))
