@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Benchmark: the direct-palette fused GEMV (lossless BF16 weights rebuilt on chip) on a
+Llama-3.1-8B gate_proj-shaped matrix (14336 x 4096, N(0, 0.02^2), 0.05 % rows with a
+planted out-of-palette exponent), M = 1, one MI355X.
+
+One step = one uw_gemm(direct palette) call: reads the resident compressed matrix
+(sign+mantissa bytes, 4-bit palette indices, verbatim flags and exponents) and X, writes
+Y = X W^T in fp32.  Inputs are resident in HBM before timing starts.  Launches rotate over
+R distinct copies of the matrix so the working set exceeds twice the 256 MB Infinity
+Cache and every step reads HBM.
+
+Prints one JSON line (stdout).  Diagnostics go to stderr.
+    python bench.py [--gpus 1] [--steps 500] [--warmup 50]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode GEMM eff. weight GB/s & % HBM peak; bits/weight (8B MLP, M=1-64)"
+HBM_PEAK_GBS = 8000.0
+ROTATE_BYTES = 512e6
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_direct_palette_gate14336x4096_m1_pmc.md")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("uw_device.hip", "uw_internal.h"):
+        h.update(open(os.path.join(ROOT, "lossless_bf16_weight_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile():
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it was taken on the
+    current kernel source; else None."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    text = open(PMC_SUMMARY).read()
+    m_hash = re.search(r"kernel source sha256\[:16\]:\s*([0-9a-f]{16})", text)
+    m_bytes = re.search(r"HBM bytes per launch \(fetch \+ write, calibrated\):\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def cpu_baseline(w, x, seconds=10.0):
+    """The oracle (numpy) doing the same step on a row sample: rebuild W from the
+    direct-palette format and multiply in fp64.  Single-threaded (BLAS limited to 1)."""
+    from threadpoolctl import threadpool_limits
+    from oracle import codec, gemm
+    rows = 448                                   # 28 tiles of 16 rows
+    ws = w[:rows]
+    enc = codec.encode(ws, rows, ws.shape[1])
+    blob = codec.serialize(enc)
+    d = codec.parse(blob)
+    idx = codec.transcode_blob(blob)
+    reps, t0 = 0, time.perf_counter()
+    with threadpool_limits(limits=1):
+        while True:
+            wr = codec.reconstruct_from_palette(d["sm"], idx, d["flags"], d["vprefix"], d["vexp"], d["palette"],
+                                                rows, ws.shape[1])
+            y, _ = gemm.gemm_ref(x, wr)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+    assert np.array_equal(wr, ws)
+    gbs = 2.0 * rows * ws.shape[1] * reps / el / 1e9
+    return dict(value=round(gbs, 4), unit="GB/s", cores=1, kind="oracle",
+                sample="%d of 14336 rows (%d tiles) x 4096, %d reps in %.1f s: oracle palette rebuild + fp64 GEMV, "
+                       "1 thread, uncompressed-equivalent bytes" % (rows, rows // 16, reps, el))
+
+
+def time_launches(fn, copies, steps, warmup, stream):
+    """fn(i) launches on `stream`.  Returns (total_ms, per-launch ms list)."""
+    import torch
+    for i in range(warmup):
+        fn(i % copies)
+    torch.cuda.synchronize()
+    # back-to-back launches, events around the whole run
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(steps):
+        fn(i % copies)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    total = e0.elapsed_time(e1)
+    # individual launches (for the spread)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(min(steps, 200))]
+    for i, (a, b) in enumerate(ev):
+        a.record(stream)
+        fn(i % copies)
+        b.record(stream)
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) for a, b in ev)
+    return total, per
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--variant", type=int, default=-1)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (--gpus %d refused)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import lossless_bf16_weight_amd as uw
+    from lossless_bf16_weight_amd import synth
+    from oracle import gemm as ogemm
+
+    assert torch.cuda.is_available(), "no GPU"
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    t0 = time.time()
+    c = synth.config2()
+    w, x = c["w"], c["x"]
+    n, k = w.shape
+    log("generated c2 %dx%d in %.1fs, sha %s" % (n, k, time.time() - t0, synth.digest(w, x)))
+    t0 = time.time()
+    blob = uw.uw_encode(w)
+    enc_s = time.time() - t0
+    info = uw.uw_blob_info(blob)
+    resident = int(info["resident_bytes"])
+    copies = max(2, int(np.ceil(ROTATE_BYTES / resident)))
+    log("encoded in %.2fs: bundle %.3f b/w, resident %.3f b/w, %d copies" % (
+        enc_s, 8 * blob.size / (n * k), 8 * resident / (n * k), copies))
+    mats = []
+    t_tc = []
+    for i in range(copies):
+        bd = torch.from_numpy(blob).to(dev)
+        idx = torch.empty(int(info["idx_bytes"]), dtype=torch.uint8, device=dev)
+        d = uw.DMat(blob, bd, idx)
+        ws = torch.zeros(64, dtype=torch.int32, device=dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        uw.uw_transcode_palette(d, idx, ws)              # load-time transcode (device kernel)
+        e1.record(stream)
+        uw.uw_check(ws)
+        t_tc.append(e0.elapsed_time(e1))
+        mats.append(d)
+    xd = torch.from_numpy(x.view(np.int16)).to(dev)
+    y = torch.empty((1, n), dtype=torch.float32, device=dev)
+
+    def step(i):
+        uw.uw_gemm_variant(mats[i], xd, y, 1, uw.UW_PIPE_DIRECT_PALETTE, args.variant)
+
+    # parity of the timed configuration on sampled rows
+    step(0)
+    torch.cuda.synchronize()
+    rows = np.random.default_rng(0).choice(n, 2048, replace=False)
+    rows = np.union1d(rows, c["planted"])
+    yr, s = ogemm.gemm_ref_rows(x, w, rows)
+    ok = ogemm.within_bound(y.cpu().numpy().astype(np.float64)[:, rows], yr, s)
+    assert ok.all(), "parity failure in the timed configuration"
+
+    total_ms, per = time_launches(step, copies, args.steps, args.warmup, stream)
+    us = total_ms * 1e3 / args.steps
+    med, p10, p90 = per[len(per) // 2] * 1e3, per[len(per) // 10] * 1e3, per[(9 * len(per)) // 10] * 1e3
+    eff_gbs = 2.0 * n * k / (us * 1e-6) / 1e9
+    alg_bytes = resident + 2 * k + 4 * n          # compressed W + X + Y per launch
+    achieved = alg_bytes / (us * 1e-6) / 1e9
+
+    # uncompressed comparators: own BF16 GEMV and torch (hipBLASLt) on BF16 W
+    wcopies = max(2, int(np.ceil(ROTATE_BYTES / (2 * n * k))))
+    wd = [torch.from_numpy(w.view(np.int16)).to(dev) for _ in range(wcopies)]
+    yb = torch.empty((1, n), dtype=torch.float32, device=dev)
+
+    def step_bf16(i):
+        uw.uw_gemm_bf16(wd[i], xd, yb, 1, -1)
+
+    tot_b, per_b = time_launches(step_bf16, wcopies, args.steps, args.warmup, stream)
+    us_b = tot_b * 1e3 / args.steps
+    wbf = [t.view(torch.bfloat16) for t in wd]
+    xbf = xd.view(torch.bfloat16)
+
+    def step_torch(i):
+        torch.matmul(xbf, wbf[i].t())
+
+    tot_t, _ = time_launches(step_torch, wcopies, args.steps, args.warmup, stream)
+    us_t = tot_t * 1e3 / args.steps
+    best_bf16_us = min(us_b, us_t)
+    log("direct palette %.2f us (median %.2f, p10 %.2f, p90 %.2f); own bf16 %.2f us; torch %.2f us" % (
+        us, med, p10, p90, us_b, us_t))
+
+    cpu = None if args.no_cpu else cpu_baseline(w, x)
+    traffic = traffic_from_profile()
+    out = {
+        "metric": METRIC,
+        "value": round(eff_gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "Llama-3.1-8B gate_proj 14336x4096 N(0,0.02^2), 0.05% rows planted, "
+                               "direct-palette fused GEMV M=1, fp32 out",
+                   "n": n, "k": k, "m": 1, "pipeline": "direct_palette", "variant": args.variant,
+                   "rotation_copies": copies, "global_batch": 1, "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+        "cpu_baseline": cpu,
+        "us_per_gemm": round(us, 3),
+        "us_per_gemm_single_launch": {"median": round(med, 3), "p10": round(p10, 3), "p90": round(p90, 3)},
+        "bits_per_weight": {"resident_direct_palette": round(8 * resident / (n * k), 4),
+                            "huffman_bundle": round(8 * blob.size / (n * k), 4)},
+        "compressed_bytes_per_launch": alg_bytes,
+        "verbatim_segment_fraction": round(info["n_verb"] / (n * k / 64), 5),
+        "bf16_gemv_us": {"own_hip": round(us_b, 3), "torch_hipblaslt": round(us_t, 3)},
+        "bf16_eff_gbs_best": round(2.0 * n * k / (best_bf16_us * 1e-6) / 1e9, 1),
+        "speedup_vs_best_bf16": round(best_bf16_us / us, 4),
+        "load_time_transcode_us": round(1e3 * float(np.median(t_tc)), 2),
+        "host_encode_s": round(enc_s, 3),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

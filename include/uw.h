@@ -1,0 +1,211 @@
+/*
+ * uw.h -- C ABI of libuw: lossless BF16 weight compression fused into the decode-time GEMM,
+ * for AMD MI355X (gfx950).
+ *
+ * Method: Cloudflare blog post "Unweight" (unweight-tensor-compression).
+ *  - BF16 anatomy paragraph: a BF16 weight is sign | 8-bit exponent | 7-bit mantissa; sign and
+ *    mantissa are stored unchanged (one "sm" byte per weight).
+ *  - Exponent-distribution paragraph and figure: the 16 most frequent exponents of a matrix
+ *    (its palette) cover more than 99 % of its weights.
+ *  - Huffman paragraph: the exponent alone is Huffman coded.
+ *  - Rare-exponent paragraph: a run of 64 weights of one row that holds an exponent outside
+ *    the palette is kept verbatim, so the hot path decides once per run, not per element.
+ *  - Four-pipeline paragraphs: full Huffman decode then a standard GEMM; exponent-only decode;
+ *    run-time transcode to 4-bit palette indices; direct palette (indices prepared at model
+ *    load, no per-step preprocessing).  The last three feed a matmul that rebuilds BF16 on
+ *    chip, so the rebuilt matrix never goes through HBM.
+ *  - Autotuning paragraphs: the pipeline is chosen per weight matrix and batch size by
+ *    measurement.
+ *
+ * Conventions (all entry points):
+ *  - Every function returns uw_status (0 = UW_OK); on failure uw_last_error() returns a message
+ *    (thread-local, valid until the next call on the same thread).
+ *  - All pointers are borrowed; the caller owns every buffer.  The library never allocates
+ *    device memory and keeps no device state.
+ *  - Host validation happens before any launch: a call that returns an error launched nothing.
+ *  - Device calls are asynchronous on the given stream and report launch errors only; data
+ *    errors found by a kernel (a corrupt bitstream) are recorded in the workspace's error word
+ *    and reported by uw_check().
+ *  - Shapes: W is [n, k] BF16 row-major (output x input, like a Linear weight), X is [m, k]
+ *    BF16 row-major, Y = X W^T is [m, n] fp32 row-major.  k must be a multiple of 64.
+ *
+ * Storage format "UW1" (little-endian; a reading of the post where it is silent):
+ *   Rows are grouped in tiles of 16 (np = n rounded up to 16, T = np/16 tiles); columns in
+ *   blocks of 64 (KB = k/64).  A segment is (tile t, block b, row r): 64 weights of row 16t+r.
+ *   Segments are enumerated in (t, b, r) order.
+ *   - palette: the min(16, #distinct) exponents with the highest whole-matrix counts (ties to the
+ *     smaller exponent), listed in ascending order; the palette index is the list position.
+ *   - sm:      np*k bytes, sign<<7 | mantissa, in 16x16 sub-tiles: byte (row, col) sits at
+ *              ((t*(k/16) + col/16)*16 + row%16)*16 + col%16.
+ *   - flags:   T*KB uint16; bit r of flags[t*KB + b] = segment (t, b, r) is verbatim.
+ *   - vprefix: T+1 uint32; verbatim segments in tiles before t.
+ *   - vexp:    64 raw exponent bytes per verbatim segment, in segment order.
+ *   - words:   Huffman stream of the palette indices of every non-verbatim segment (segment
+ *              order, column ascending), codes MSB-first in uint32 words, two zero words after.
+ *              Code: optimal length-limited (13 bits) prefix code, canonical.
+ *   - off:     uint32 start bit of every chunk, then the total bit count.  A chunk is `chunk`
+ *              coded symbols (a multiple of 64); chunks restart at every tile.
+ *   - cbase:   T+1 uint32; first chunk of every tile.
+ *   Direct-palette index stream (made by uw_transcode_palette, held by the caller): np*k/2 bytes;
+ *   row r of sub-tile (t, j) owns 8 bytes at ((t*(k/16) + j)*16 + r)*8 = two uint32 words, word w
+ *   holding columns 16j+8w+i (i = 0..7) at bit 4*(i/2) + 16*(i%2); verbatim segments and
+ *   padding rows hold 0.
+ */
+#ifndef UW_H
+#define UW_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t uw_status;
+enum {
+  UW_OK = 0,
+  UW_E_ARG = -1,       /* null pointer, bad enum, non-positive size */
+  UW_E_SHAPE = -2,     /* k % 64 != 0, m outside [1, UW_MAX_M], size limits */
+  UW_E_FORMAT = -3,    /* blob: bad magic/version/geometry, section bounds, inconsistent tables */
+  UW_E_NOMEM = -4,     /* host allocation failed */
+  UW_E_WORKSPACE = -5, /* workspace missing or too small */
+  UW_E_HIP = -6,       /* HIP launch or runtime error */
+  UW_E_DATA = -7       /* a kernel found a corrupt stream (reported by uw_check) */
+};
+enum {
+  UW_PIPE_AUTO = 0,           /* autotune table entry for (n, k, m), else DIRECT_PALETTE */
+  UW_PIPE_FULL_DECODE = 1,    /* Huffman -> BF16 W in workspace, then BF16 GEMM */
+  UW_PIPE_EXP_ONLY = 2,       /* Huffman -> exponent bytes in workspace, then sm+exp GEMM */
+  UW_PIPE_TRANSCODE = 3,      /* Huffman -> 4-bit indices in workspace, then palette GEMM */
+  UW_PIPE_DIRECT_PALETTE = 4  /* resident 4-bit indices (bound at uw_dmat_bind), palette GEMM */
+};
+#define UW_MAX_M 256
+#define UW_MAX_CHUNK 4096
+
+/* Message for the last failing call on this thread ("" if none). */
+const char* uw_last_error(void);
+/* Library version, major*10000 + minor*100 + patch. */
+int32_t uw_version(void);
+
+/* ------------------------------------------------------------------------------------------
+ * Host encoder (pure, thread-safe, host pointers only).
+ * ------------------------------------------------------------------------------------------ */
+typedef struct {
+  uint32_t n;               /* palette size, 1..16 */
+  uint8_t exp[16];          /* palette exponents, ascending; exp[i] for i >= n is 0 */
+  uint8_t index_of[256];    /* exponent -> palette index, 0xFF when outside the palette */
+  uint64_t hist[256];       /* whole-matrix exponent histogram */
+} uw_palette;
+
+/* Histogram and top-16 palette of W (exponent-distribution paragraph).
+ * w: host, n*k uint16 BF16 bit patterns, row-major.  Errors: UW_E_ARG, UW_E_SHAPE. */
+uw_status uw_build_palette(const uint16_t* w, int64_t n, int64_t k, uw_palette* out);
+
+/* Upper bound of the blob size for an n x k matrix (every segment coded at 13 bits). */
+uw_status uw_encode_bound(int64_t n, int64_t k, int32_t chunk, size_t* bytes);
+
+/* Encode W into a UW1 blob (Huffman, rare-exponent and four-pipeline paragraphs).
+ * w:      host, n*k BF16 bit patterns, row-major.
+ * chunk:  coded symbols per chunk, a multiple of 64 in [64, UW_MAX_CHUNK]; 0 = 512.
+ * blob:   host output of `cap` bytes; NULL asks for the exact size only (two-call pattern).
+ * used:   receives the blob size in bytes.
+ * Errors: UW_E_ARG (null w/used), UW_E_SHAPE (k % 64, stream >= 2^32 bits), UW_E_NOMEM,
+ *         UW_E_WORKSPACE (cap too small; *used holds the size needed). */
+uw_status uw_encode(const uint16_t* w, int64_t n, int64_t k, int32_t chunk,
+                    void* blob, size_t cap, size_t* used);
+
+/* Header fields of a blob, validated (host).  Sizes in bytes. */
+typedef struct {
+  int64_t n, k, np, tiles, kb;
+  int32_t chunk, lmax, n_pal, affine;      /* affine: palette[i] == palette[0] + i for all i */
+  int64_t n_verb, n_coded, total_bits, n_chunks, n_words;
+  uint8_t palette[16];
+  uint8_t code_len[16];
+  uint16_t code[16];
+  uint64_t sec_off[7], sec_size[7];         /* sm, flags, vprefix, vexp, cbase, off, words */
+  uint64_t blob_bytes;                      /* header + sections, as laid out */
+  uint64_t resident_bytes;                  /* sm + idx + flags + vprefix + vexp */
+  uint64_t idx_bytes;                       /* np*k/2, the direct-palette index stream */
+} uw_info;
+uw_status uw_blob_info(const void* blob_host, size_t bytes, uw_info* out);
+
+/* ------------------------------------------------------------------------------------------
+ * Device view of an encoded matrix.
+ * ------------------------------------------------------------------------------------------ */
+typedef struct uw_dmat uw_dmat;  /* opaque; the caller allocates uw_dmat_size() bytes */
+size_t uw_dmat_size(void);
+
+/* Validate the blob (host copy) and record the device addresses of its sections.
+ * blob_host: host copy of the blob (read during the call only); bytes: its size.
+ * blob_dev:  device copy of the same bytes (must stay valid while d is used).
+ * idx_dev:   device buffer of uw_info.idx_bytes for the direct-palette index stream, or NULL
+ *            (then UW_PIPE_DIRECT_PALETTE is refused with UW_E_ARG).
+ * Errors: UW_E_ARG, UW_E_FORMAT. */
+uw_status uw_dmat_bind(uw_dmat* d, const void* blob_host, size_t bytes, const void* blob_dev,
+                       void* idx_dev);
+uw_status uw_dmat_get_info(const uw_dmat* d, uw_info* out);
+
+/* Workspace bytes a call needs.  op: a UW_PIPE_* value for uw_gemm, or one of the decode
+ * targets below.  The first 256 bytes hold the error word; they must be zero before the first
+ * use (uw_check clears the word again). */
+enum { UW_OP_DECODE_FULL = 16, UW_OP_TRANSCODE = 17, UW_OP_DECODE_EXP = 18 };
+uw_status uw_workspace_size(const uw_dmat* d, int32_t m, int32_t op, size_t* bytes);
+
+/* Full Huffman decode (pipeline 1's preprocessing): w_out (device, n*k uint16, row-major) is
+ * bit-identical to the encoded W.  ws: workspace of uw_workspace_size(.., UW_OP_DECODE_FULL). */
+uw_status uw_decode_full(const uw_dmat* d, uint16_t* w_out, void* ws, size_t ws_bytes,
+                         hipStream_t s);
+
+/* Huffman -> 4-bit palette index stream (pipeline 3's preprocessing, and the load-time
+ * transcode of the direct-palette format): idx_out (device, uw_info.idx_bytes). */
+uw_status uw_transcode_palette(const uw_dmat* d, uint8_t* idx_out, void* ws, size_t ws_bytes,
+                               hipStream_t s);
+
+/* Huffman -> exponent bytes (pipeline 2's preprocessing): exp_out (device, np*k bytes, the sm
+ * sub-tile layout; verbatim segments get their raw exponents, padding rows 0). */
+uw_status uw_decode_exponents(const uw_dmat* d, uint8_t* exp_out, void* ws, size_t ws_bytes,
+                              hipStream_t s);
+
+/* Y = X W^T with W rebuilt on chip (reconstructive-matmul paragraphs).
+ * x: device [m, k] BF16; y: device [m, n] fp32; 1 <= m <= UW_MAX_M.
+ * pipeline: UW_PIPE_*; variant: kernel variant id (uw_variant_count), -1 = autotuned/default.
+ * ws: workspace of uw_workspace_size(d, m, pipeline) bytes (may be NULL when that size is 0).
+ * Errors: UW_E_ARG, UW_E_SHAPE, UW_E_WORKSPACE, UW_E_HIP. */
+uw_status uw_gemm(const uw_dmat* d, const uint16_t* x, float* y, int32_t m, int32_t pipeline,
+                  void* ws, size_t ws_bytes, hipStream_t s);
+uw_status uw_gemm_variant(const uw_dmat* d, const uint16_t* x, float* y, int32_t m,
+                          int32_t pipeline, int32_t variant, void* ws, size_t ws_bytes,
+                          hipStream_t s);
+
+/* Uncompressed baseline (the BF16 GEMM of pipeline 1): Y = X W^T for a plain BF16 W
+ * (device, [n, k] row-major).  variant: -1 = default. */
+uw_status uw_gemm_bf16(const uint16_t* w, int64_t n, int64_t k, const uint16_t* x, float* y,
+                       int32_t m, int32_t variant, hipStream_t s);
+
+/* Kernel variants: count, and a description string ("waves=4 unroll=2") of one. */
+int32_t uw_variant_count(void);
+const char* uw_variant_name(int32_t variant);
+
+/* Wait for s and report a data error recorded in ws (UW_E_DATA), clearing it. */
+uw_status uw_check(void* ws, hipStream_t s);
+
+/* Autotune table used by UW_PIPE_AUTO and variant -1 (autotuning paragraphs).
+ * Text file, one entry per line: "n k m pipeline variant"; '#' starts a comment.
+ * A missing entry means DIRECT_PALETTE with the default variant. */
+uw_status uw_autotune_load(const char* path);
+uw_status uw_autotune_set(int64_t n, int64_t k, int32_t m, int32_t pipeline, int32_t variant);
+uw_status uw_autotune_get(int64_t n, int64_t k, int32_t m, int32_t* pipeline, int32_t* variant);
+uw_status uw_autotune_clear(void);
+
+/* Glue of an MLP decode step (SwiGLU between up/gate and down):
+ * h[i] = bf16(silu(g[i]) * u[i]) in fp32, round to nearest even; count elements. */
+uw_status uw_swiglu(const float* g, const float* u, uint16_t* h, int64_t count, hipStream_t s);
+/* x[r, :] = bf16(y[r, :] / sqrt(mean(y[r, :]^2) + eps)) for rows r < m of an [m, n] fp32 y. */
+uw_status uw_rmsnorm(const float* y, uint16_t* x, int32_t m, int32_t n, float eps,
+                     hipStream_t s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* UW_H */

@@ -1,1 +1,309 @@
-"""Lossless BF16 weight compression fused into the decode-time GEMM, for MI355X (gfx950)."""
+"""Lossless BF16 weight compression fused into the decode-time GEMM, for MI355X (gfx950).
+
+Thin ctypes binding over libuw.so (include/uw.h): every function marshals arguments and
+calls the C ABI of the same name; all computation happens in the library (host codec in
+C++, everything on the device in hand-written HIP kernels).  PyTorch supplies device
+memory and streams only.  The library must be built first
+(``python -m lossless_bf16_weight_amd.build``); calls fail loudly when it is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import synth  # noqa: F401  (seeded workloads; no method arithmetic)
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libuw.so")
+
+UW_OK, UW_E_ARG, UW_E_SHAPE, UW_E_FORMAT, UW_E_NOMEM, UW_E_WORKSPACE, UW_E_HIP, UW_E_DATA = 0, -1, -2, -3, -4, -5, -6, -7
+UW_PIPE_AUTO, UW_PIPE_FULL_DECODE, UW_PIPE_EXP_ONLY, UW_PIPE_TRANSCODE, UW_PIPE_DIRECT_PALETTE = 0, 1, 2, 3, 4
+UW_OP_DECODE_FULL, UW_OP_TRANSCODE, UW_OP_DECODE_EXP = 16, 17, 18
+UW_MAX_M = 256
+PIPELINES = {"full": UW_PIPE_FULL_DECODE, "exp": UW_PIPE_EXP_ONLY, "transcode": UW_PIPE_TRANSCODE,
+             "direct": UW_PIPE_DIRECT_PALETTE}
+
+# Every symbol include/uw.h declares (checked by the CPU tests).
+EXPORTS = ("uw_last_error", "uw_version", "uw_build_palette", "uw_encode_bound", "uw_encode", "uw_blob_info",
+           "uw_dmat_size", "uw_dmat_bind", "uw_dmat_get_info", "uw_workspace_size", "uw_decode_full",
+           "uw_transcode_palette", "uw_decode_exponents", "uw_gemm", "uw_gemm_variant", "uw_gemm_bf16",
+           "uw_variant_count", "uw_variant_name", "uw_check", "uw_autotune_load", "uw_autotune_set",
+           "uw_autotune_get", "uw_autotune_clear", "uw_swiglu", "uw_rmsnorm")
+
+
+class UwError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__("uw status %d: %s" % (status, msg))
+        self.status = status
+
+
+class Palette(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_uint32), ("exp", ctypes.c_uint8 * 16), ("index_of", ctypes.c_uint8 * 256),
+                ("hist", ctypes.c_uint64 * 256)]
+
+
+class Info(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64), ("k", ctypes.c_int64), ("np", ctypes.c_int64), ("tiles", ctypes.c_int64),
+                ("kb", ctypes.c_int64), ("chunk", ctypes.c_int32), ("lmax", ctypes.c_int32),
+                ("n_pal", ctypes.c_int32), ("affine", ctypes.c_int32), ("n_verb", ctypes.c_int64),
+                ("n_coded", ctypes.c_int64), ("total_bits", ctypes.c_int64), ("n_chunks", ctypes.c_int64),
+                ("n_words", ctypes.c_int64), ("palette", ctypes.c_uint8 * 16), ("code_len", ctypes.c_uint8 * 16),
+                ("code", ctypes.c_uint16 * 16), ("sec_off", ctypes.c_uint64 * 7), ("sec_size", ctypes.c_uint64 * 7),
+                ("blob_bytes", ctypes.c_uint64), ("resident_bytes", ctypes.c_uint64), ("idx_bytes", ctypes.c_uint64)]
+
+    def as_dict(self):
+        out = {}
+        for name, _ in self._fields_:
+            v = getattr(self, name)
+            out[name] = list(v) if hasattr(v, "__len__") else v
+        return out
+
+
+_lib = None
+_P, _S, _I32, _I64, _F = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+
+
+def lib():
+    """Load libuw.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libuw.so is not built (%s); run: python -m lossless_bf16_weight_amd.build" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    sig = {
+        "uw_last_error": (ctypes.c_char_p, []),
+        "uw_version": (_I32, []),
+        "uw_build_palette": (_I32, [_P, _I64, _I64, ctypes.POINTER(Palette)]),
+        "uw_encode_bound": (_I32, [_I64, _I64, _I32, ctypes.POINTER(_S)]),
+        "uw_encode": (_I32, [_P, _I64, _I64, _I32, _P, _S, ctypes.POINTER(_S)]),
+        "uw_blob_info": (_I32, [_P, _S, ctypes.POINTER(Info)]),
+        "uw_dmat_size": (_S, []),
+        "uw_dmat_bind": (_I32, [_P, _P, _S, _P, _P]),
+        "uw_dmat_get_info": (_I32, [_P, ctypes.POINTER(Info)]),
+        "uw_workspace_size": (_I32, [_P, _I32, _I32, ctypes.POINTER(_S)]),
+        "uw_decode_full": (_I32, [_P, _P, _P, _S, _P]),
+        "uw_transcode_palette": (_I32, [_P, _P, _P, _S, _P]),
+        "uw_decode_exponents": (_I32, [_P, _P, _P, _S, _P]),
+        "uw_gemm": (_I32, [_P, _P, _P, _I32, _I32, _P, _S, _P]),
+        "uw_gemm_variant": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P, _S, _P]),
+        "uw_gemm_bf16": (_I32, [_P, _I64, _I64, _P, _P, _I32, _I32, _P]),
+        "uw_variant_count": (_I32, []),
+        "uw_variant_name": (ctypes.c_char_p, [_I32]),
+        "uw_check": (_I32, [_P, _P]),
+        "uw_autotune_load": (_I32, [ctypes.c_char_p]),
+        "uw_autotune_set": (_I32, [_I64, _I64, _I32, _I32, _I32]),
+        "uw_autotune_get": (_I32, [_I64, _I64, _I32, ctypes.POINTER(_I32), ctypes.POINTER(_I32)]),
+        "uw_autotune_clear": (_I32, []),
+        "uw_swiglu": (_I32, [_P, _P, _P, _I64, _P]),
+        "uw_rmsnorm": (_I32, [_P, _P, _I32, _I32, _F, _P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(status):
+    if status != UW_OK:
+        raise UwError(status, lib().uw_last_error().decode(errors="replace"))
+
+
+def _ptr(t):
+    """Device or host address of a torch tensor or numpy array (None -> NULL)."""
+    if t is None:
+        return None
+    if isinstance(t, np.ndarray):
+        return t.ctypes.data
+    return t.data_ptr()
+
+
+def _stream(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+# ----------------------------------------------------------------------------------------
+# Host encoder
+# ----------------------------------------------------------------------------------------
+def uw_version():
+    return lib().uw_version()
+
+
+def uw_build_palette(w):
+    w = np.ascontiguousarray(w, dtype=np.uint16)
+    p = Palette()
+    _check(lib().uw_build_palette(w.ctypes.data, w.shape[0], w.shape[1], ctypes.byref(p)))
+    return dict(n=p.n, exp=list(p.exp)[: p.n], index_of=np.array(p.index_of, np.uint8),
+                hist=np.array(p.hist, np.int64))
+
+
+def uw_encode_bound(n, k, chunk=0):
+    out = ctypes.c_size_t()
+    _check(lib().uw_encode_bound(n, k, chunk, ctypes.byref(out)))
+    return out.value
+
+
+def uw_encode(w, chunk=0):
+    """Encode a [n, k] uint16 BF16 matrix; returns the blob as a uint8 numpy array."""
+    w = np.ascontiguousarray(w, dtype=np.uint16)
+    n, k = w.shape
+    used = ctypes.c_size_t()
+    _check(lib().uw_encode(w.ctypes.data, n, k, chunk, None, 0, ctypes.byref(used)))
+    blob = np.zeros(used.value, np.uint8)
+    _check(lib().uw_encode(w.ctypes.data, n, k, chunk, blob.ctypes.data, blob.size, ctypes.byref(used)))
+    return blob
+
+
+def uw_blob_info(blob):
+    blob = np.ascontiguousarray(blob, dtype=np.uint8)
+    info = Info()
+    _check(lib().uw_blob_info(blob.ctypes.data, blob.size, ctypes.byref(info)))
+    return info.as_dict()
+
+
+# ----------------------------------------------------------------------------------------
+# Device view and kernels
+# ----------------------------------------------------------------------------------------
+class DMat:
+    """A bound uw_dmat plus the tensors it borrows (kept alive here)."""
+
+    def __init__(self, blob_host, blob_dev, idx_dev=None):
+        self.buf = ctypes.create_string_buffer(lib().uw_dmat_size())
+        self.blob_host = np.ascontiguousarray(blob_host, dtype=np.uint8)
+        self.blob_dev = blob_dev
+        self.idx = idx_dev
+        _check(lib().uw_dmat_bind(self.buf, self.blob_host.ctypes.data, self.blob_host.size, _ptr(blob_dev),
+                                  _ptr(idx_dev)))
+        info = Info()
+        _check(lib().uw_dmat_get_info(self.buf, ctypes.byref(info)))
+        self.info = info.as_dict()
+
+    @property
+    def handle(self):
+        return self.buf
+
+
+def uw_dmat_bind(blob_host, blob_dev, idx_dev=None):
+    return DMat(blob_host, blob_dev, idx_dev)
+
+
+def uw_workspace_size(d, m, op):
+    out = ctypes.c_size_t()
+    _check(lib().uw_workspace_size(d.handle, m, op, ctypes.byref(out)))
+    return out.value
+
+
+def uw_decode_full(d, w_out, ws, stream=None):
+    _check(lib().uw_decode_full(d.handle, _ptr(w_out), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def uw_transcode_palette(d, idx_out, ws, stream=None):
+    _check(lib().uw_transcode_palette(d.handle, _ptr(idx_out), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def uw_decode_exponents(d, exp_out, ws, stream=None):
+    _check(lib().uw_decode_exponents(d.handle, _ptr(exp_out), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def uw_gemm(d, x, y, m, pipeline=UW_PIPE_AUTO, ws=None, stream=None):
+    _check(lib().uw_gemm(d.handle, _ptr(x), _ptr(y), m, pipeline, _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def uw_gemm_variant(d, x, y, m, pipeline, variant, ws=None, stream=None):
+    _check(lib().uw_gemm_variant(d.handle, _ptr(x), _ptr(y), m, pipeline, variant, _ptr(ws), _nbytes(ws),
+                                 _stream(stream)))
+
+
+def uw_gemm_bf16(w, x, y, m, variant=-1, stream=None):
+    n, k = w.shape
+    _check(lib().uw_gemm_bf16(_ptr(w), n, k, _ptr(x), _ptr(y), m, variant, _stream(stream)))
+
+
+def uw_variant_count():
+    return lib().uw_variant_count()
+
+
+def uw_variant_name(v):
+    return lib().uw_variant_name(v).decode()
+
+
+def uw_check(ws, stream=None):
+    _check(lib().uw_check(_ptr(ws), _stream(stream)))
+
+
+def uw_autotune_load(path):
+    _check(lib().uw_autotune_load(path.encode()))
+
+
+def uw_autotune_set(n, k, m, pipeline, variant):
+    _check(lib().uw_autotune_set(n, k, m, pipeline, variant))
+
+
+def uw_autotune_get(n, k, m):
+    p, v = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().uw_autotune_get(n, k, m, ctypes.byref(p), ctypes.byref(v)))
+    return p.value, v.value
+
+
+def uw_autotune_clear():
+    _check(lib().uw_autotune_clear())
+
+
+def uw_swiglu(g, u, h, stream=None):
+    _check(lib().uw_swiglu(_ptr(g), _ptr(u), _ptr(h), g.numel(), _stream(stream)))
+
+
+def uw_rmsnorm(y, x, eps=1e-5, stream=None):
+    m, n = y.shape
+    _check(lib().uw_rmsnorm(_ptr(y), _ptr(x), m, n, eps, _stream(stream)))
+
+
+# ----------------------------------------------------------------------------------------
+# Convenience: a compressed matrix resident on the GPU
+# ----------------------------------------------------------------------------------------
+class CompressedMatrix:
+    """Encode W on the host (C++), copy the blob to the device, bind it and run the
+    load-time transcode to the direct-palette index stream (a device kernel)."""
+
+    def __init__(self, w, chunk=0, device="cuda", blob=None, keep_index=True):
+        import torch
+        self.blob = uw_encode(w, chunk) if blob is None else np.ascontiguousarray(blob, np.uint8)
+        self.blob_dev = torch.from_numpy(self.blob).to(device)
+        info = uw_blob_info(self.blob)
+        self.idx = torch.empty(int(info["idx_bytes"]), dtype=torch.uint8, device=device) if keep_index else None
+        self.d = DMat(self.blob, self.blob_dev, self.idx)
+        self.info = self.d.info
+        self.n, self.k = int(info["n"]), int(info["k"])
+        self.err = torch.zeros(64, dtype=torch.int32, device=device)
+        if keep_index:
+            uw_transcode_palette(self.d, self.idx, self.err)
+
+    def workspace(self, m, pipeline):
+        import torch
+        size = uw_workspace_size(self.d, m, pipeline)
+        return torch.zeros(max(size, 256), dtype=torch.uint8, device=self.blob_dev.device) if size else None
+
+    def gemm(self, x, y=None, pipeline=UW_PIPE_DIRECT_PALETTE, ws=None, variant=-1, stream=None):
+        import torch
+        m = x.shape[0]
+        if y is None:
+            y = torch.empty((m, self.n), dtype=torch.float32, device=x.device)
+        if ws is None and pipeline not in (UW_PIPE_DIRECT_PALETTE,):
+            ws = self.workspace(m, pipeline)
+        uw_gemm_variant(self.d, x, y, m, pipeline, variant, ws, stream)
+        return y
+
+    def resident_bytes(self):
+        return int(self.info["resident_bytes"])
+
+    def bundle_bytes(self):
+        return int(self.blob.size)

@@ -1,0 +1,240 @@
+"""GPU parity: every device entry point of libuw against the CPU oracle, through the C ABI.
+
+Bar: bit-exact for decode / transcode / exponent streams (byte work); for GEMMs
+|y_gpu - y_ref| <= 1e-3 * sum_k |x_k w_k| per element (y_ref accumulated in fp64);
+SwiGLU / RMS-norm glue within one BF16 ulp of the oracle."""
+import numpy as np
+import pytest
+
+import lossless_bf16_weight_amd as uw
+from lossless_bf16_weight_amd import synth
+from oracle import codec, gemm
+
+pytestmark = pytest.mark.gpu
+
+ALL_PIPES = [uw.UW_PIPE_DIRECT_PALETTE, uw.UW_PIPE_TRANSCODE, uw.UW_PIPE_EXP_ONLY, uw.UW_PIPE_FULL_DECODE]
+
+
+def torch():
+    import torch as t
+    return t
+
+
+def dev_u16(a):
+    t = torch()
+    return t.from_numpy(np.ascontiguousarray(a, np.uint16).view(np.int16)).cuda()
+
+
+def host_u16(t_):
+    return t_.cpu().numpy().view(np.uint16)
+
+
+def check_gemm(y_dev, x, w, rows=None):
+    y = y_dev.cpu().numpy().astype(np.float64)
+    if rows is None:
+        y_ref, s = gemm.gemm_ref(x, w)
+    else:
+        y_ref, s = gemm.gemm_ref_rows(x, w, rows)
+        y = y[:, rows]
+    ok = gemm.within_bound(y, y_ref, s)
+    bad = np.argwhere(~ok)
+    assert ok.all(), "%d/%d outside bound, first %s: gpu %r ref %r S %r" % (
+        len(bad), ok.size, bad[:3].tolist(), y[tuple(bad[0])], y_ref[tuple(bad[0])], s[tuple(bad[0])])
+
+
+def err_ws():
+    return torch().zeros(64, dtype=torch().int32, device="cuda")
+
+
+CASES = {
+    "ragged_37x192": lambda: synth.small_gaussian(37, 192, seed=1, plant_frac=0.05)["w"],
+    "tiles_160x1024": lambda: synth.small_gaussian(160, 1024, seed=4, plant_frac=0.02)["w"],
+    "student_t_48x1024": lambda: synth.student_t_bf16(np.random.default_rng(5), (48, 1024), 3, 0.02),
+    "one_row_1x64": lambda: synth.small_gaussian(1, 64, seed=3)["w"],
+    "all_verbatim_20x128": lambda: every_segment_verbatim(20, 128, 8),
+    "single_exponent_16x128": lambda: np.full((16, 128), 0x3F80, np.uint16) | (np.arange(128, dtype=np.uint16)[None, :] & 0x7F),
+    "bimodal_lut_96x512": lambda: bimodal(96, 512, 6),
+}
+
+
+# Non-finite patterns (NaN payloads, +-Inf) only go through the byte-exact decoders.
+DECODE_ONLY = {
+    "every_bit_pattern_1024x64": lambda: np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(1024, 64),
+}
+
+
+def every_segment_verbatim(n, k, seed):
+    """Gaussian weights with one rare (finite, large) exponent planted in every segment:
+    each planted exponent is used once, so none enters the palette."""
+    rng = np.random.default_rng(seed)
+    w = synth.gaussian_bf16(rng, (n, k), 0.02)
+    e = 140
+    for r in range(n):
+        for b in range(k // 64):
+            w[r, 64 * b + int(rng.integers(0, 64))] = (e << 7) | int(rng.integers(0, 128))
+            e = 140 + (e - 139) % 100
+    return w
+
+
+def bimodal(n, k, seed):
+    """Two magnitude scales far apart: the top-16 exponents are not consecutive, so the
+    palette is not affine and the kernels take the table-lookup path."""
+    rng = np.random.default_rng(seed)
+    a = rng.standard_normal((n, k)).astype(np.float32)
+    scale = np.where(rng.random((n, k)) < 0.5, np.float32(1e-4), np.float32(30.0))
+    return synth.f32_to_bf16_bits(a * scale)
+
+
+@pytest.mark.parametrize("name", list(CASES) + list(DECODE_ONLY))
+@pytest.mark.parametrize("chunk", [64, 512])
+def test_decoders_bit_exact(name, chunk):
+    t = torch()
+    w = {**CASES, **DECODE_ONLY}[name]()
+    n, k = w.shape
+    blob = uw.uw_encode(w, chunk)
+    ref_blob = codec.serialize(codec.encode(w, n, k, chunk=chunk))
+    assert blob.tobytes() == ref_blob
+    cm = uw.CompressedMatrix(w, chunk=chunk, blob=blob)
+    ws = err_ws()
+    out = t.empty((n, k), dtype=t.int16, device="cuda")
+    uw.uw_decode_full(cm.d, out, ws)
+    uw.uw_check(ws)
+    assert np.array_equal(host_u16(out), w)
+    idx = t.empty(int(cm.info["idx_bytes"]), dtype=t.uint8, device="cuda")
+    uw.uw_transcode_palette(cm.d, idx, ws)
+    uw.uw_check(ws)
+    assert idx.cpu().numpy().tobytes() == codec.transcode_blob(ref_blob).tobytes()
+    assert cm.idx.cpu().numpy().tobytes() == codec.transcode_blob(ref_blob).tobytes()
+    ex = t.empty(int(cm.info["np"]) * k, dtype=t.uint8, device="cuda")
+    uw.uw_decode_exponents(cm.d, ex, ws)
+    uw.uw_check(ws)
+    assert ex.cpu().numpy().tobytes() == codec.exponent_stream_blob(ref_blob).tobytes()
+
+
+@pytest.mark.parametrize("name", list(CASES))
+@pytest.mark.parametrize("m", [1, 5, 16, 17, 40, 128, 200])
+def test_gemm_all_pipelines(name, m):
+    t = torch()
+    w = CASES[name]()
+    n, k = w.shape
+    x = synth.gaussian_bf16(np.random.default_rng(100 + m), (m, k), 1.0)
+    cm = uw.CompressedMatrix(w, chunk=128)
+    xd = dev_u16(x)
+    for pipe in ALL_PIPES:
+        ws = cm.workspace(m, pipe)
+        y = t.full((m, n), float("nan"), dtype=t.float32, device="cuda")
+        uw.uw_gemm(cm.d, xd, y, m, pipe, ws)
+        if ws is not None:
+            uw.uw_check(ws)
+        check_gemm(y, x, w)
+
+
+@pytest.mark.parametrize("variant", range(10))
+def test_gemm_every_variant(variant):
+    t = torch()
+    w = synth.small_gaussian(200, 2048, seed=11, plant_frac=0.05)["w"]
+    cm = uw.CompressedMatrix(w)
+    for m in (1, 24, 70):
+        x = synth.gaussian_bf16(np.random.default_rng(m), (m, 2048), 1.0)
+        y = t.empty((m, 200), dtype=t.float32, device="cuda")
+        uw.uw_gemm_variant(cm.d, dev_u16(x), y, m, uw.UW_PIPE_DIRECT_PALETTE, variant)
+        check_gemm(y, x, w)
+        yb = t.empty((m, 200), dtype=t.float32, device="cuda")
+        uw.uw_gemm_bf16(dev_u16(w), dev_u16(x), yb, m, variant)
+        check_gemm(yb, x, w)
+
+
+def test_bf16_gemm_ragged_rows():
+    t = torch()
+    w = synth.small_gaussian(45, 320, seed=2)["w"]
+    x = synth.gaussian_bf16(np.random.default_rng(3), (3, 320), 1.0)
+    y = t.empty((3, 45), dtype=t.float32, device="cuda")
+    uw.uw_gemm_bf16(dev_u16(w), dev_u16(x), y, 3)
+    check_gemm(y, x, w)
+
+
+def test_config1_end_to_end():
+    """Config 1: encode -> decode (bit-exact) -> GEMV, fp32 output."""
+    t = torch()
+    c = synth.config1()
+    w, x = c["w"], c["x"]
+    cm = uw.CompressedMatrix(w)
+    ws = err_ws()
+    out = t.empty((1024, 1024), dtype=t.int16, device="cuda")
+    uw.uw_decode_full(cm.d, out, ws)
+    uw.uw_check(ws)
+    assert np.array_equal(host_u16(out), w)
+    for pipe in ALL_PIPES:
+        y = cm.gemm(dev_u16(x), pipeline=pipe)
+        check_gemm(y, x, w)
+    assert cm.info["n_verb"] > 0 and cm.info["affine"] == 1
+
+
+def test_corrupt_stream_matches_oracle():
+    """Flipped stream bits (tables intact, every read in bounds).  Where the oracle's
+    chunk-end check detects the corruption the GPU must report UW_E_DATA; where a flip
+    resynchronises undetected, the GPU must produce exactly the oracle's decode of the
+    corrupted blob."""
+    t = torch()
+    w = synth.small_gaussian(64, 1024, seed=21)["w"]
+    blob = uw.uw_encode(w, 256)
+    info = uw.uw_blob_info(blob)
+    wo = int(info["sec_off"][6])
+    seen = {True: 0, False: 0}
+    for pos, bit in [(40, 0x10), (41, 0x01), (300, 0x80), (1000, 0x04), (1501, 0x40), (2222, 0x02), (3000, 0x08)]:
+        bad = blob.copy()
+        bad[wo + pos] ^= bit
+        try:
+            ref = codec.decode_blob(bad.tobytes())
+            detected = False
+        except ValueError:
+            detected = True
+        seen[detected] += 1
+        d = uw.DMat(bad, t.from_numpy(bad).cuda())
+        ws = err_ws()
+        out = t.empty((64, 1024), dtype=t.int16, device="cuda")
+        uw.uw_decode_full(d, out, ws)
+        if detected:
+            with pytest.raises(uw.UwError) as ei:
+                uw.uw_check(ws)
+            assert ei.value.status == uw.UW_E_DATA
+            uw.uw_check(ws)  # the error word was cleared
+        else:
+            uw.uw_check(ws)
+            assert np.array_equal(host_u16(out), ref)
+    assert seen[True] >= 1
+
+
+def test_argument_errors_launch_nothing():
+    t = torch()
+    w = synth.small_gaussian(32, 128, seed=1)["w"]
+    cm = uw.CompressedMatrix(w)
+    x = dev_u16(synth.gaussian_bf16(np.random.default_rng(1), (1, 128), 1.0))
+    y = t.empty((1, 32), dtype=t.float32, device="cuda")
+    for m in (0, uw.UW_MAX_M + 1):
+        with pytest.raises(uw.UwError) as ei:
+            uw.uw_gemm(cm.d, x, y, m, uw.UW_PIPE_DIRECT_PALETTE)
+        assert ei.value.status == uw.UW_E_SHAPE
+    with pytest.raises(uw.UwError) as ei:
+        uw.uw_gemm(cm.d, x, y, 1, uw.UW_PIPE_TRANSCODE, None)
+    assert ei.value.status == uw.UW_E_WORKSPACE
+    d2 = uw.DMat(cm.blob, cm.blob_dev, None)
+    with pytest.raises(uw.UwError) as ei:
+        uw.uw_gemm(d2, x, y, 1, uw.UW_PIPE_DIRECT_PALETTE)
+    assert ei.value.status == uw.UW_E_ARG
+
+
+def test_glue_kernels():
+    t = torch()
+    rng = np.random.default_rng(4)
+    g = (rng.standard_normal((16, 1000)) * 3).astype(np.float32)
+    u = rng.standard_normal((16, 1000)).astype(np.float32)
+    h = t.empty((16, 1000), dtype=t.int16, device="cuda")
+    uw.uw_swiglu(t.from_numpy(g).cuda(), t.from_numpy(u).cuda(), h)
+    ref = gemm.swiglu_ref(g, u).astype(np.int32)
+    assert np.abs(host_u16(h).astype(np.int32) - ref).max() <= 1
+    y = (rng.standard_normal((16, 4096)) * 5).astype(np.float32)
+    xo = t.empty((16, 4096), dtype=t.int16, device="cuda")
+    uw.uw_rmsnorm(t.from_numpy(y).cuda(), xo)
+    ref = gemm.rmsnorm_ref(y).astype(np.int32)
+    assert np.abs(host_u16(xo).astype(np.int32) - ref).max() <= 1

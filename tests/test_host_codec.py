@@ -1,0 +1,173 @@
+"""CPU tests of libuw's host side: every declared symbol is exported, the C++ encoder's
+blob is byte-identical to the oracle's, the palette matches, and malformed inputs are
+rejected with the documented status codes.  No GPU needed (nothing here launches)."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import lossless_bf16_weight_amd as uw
+from lossless_bf16_weight_amd import synth
+from oracle import codec
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "uw.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(uw_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = uw.lib()
+    names = declared_functions()
+    assert len(names) >= 20
+    for name in names:
+        assert hasattr(L, name), name
+    assert sorted(uw.EXPORTS) == names
+    assert uw.uw_version() == 10000
+
+
+def oracle_blob(w, chunk=512):
+    n, k = w.shape
+    return np.frombuffer(codec.serialize(codec.encode(w, n, k, chunk=chunk)), np.uint8)
+
+
+CASES = [
+    ("gauss_ragged", lambda: synth.small_gaussian(37, 192, seed=1, plant_frac=0.05)["w"]),
+    ("gauss_tiles", lambda: synth.small_gaussian(160, 512, seed=4, plant_frac=0.02)["w"]),
+    ("specials", lambda: np.random.default_rng(2).choice(
+        np.array([0, 0x8000, 1, 0x807F, 0x7F80, 0xFF80, 0x7FC0, 0xFFFF, 0x3F80, 0x0080], np.uint16), size=(19, 256))),
+    ("single_exponent", lambda: np.full((16, 64), 0x3F80, np.uint16) | np.arange(64, dtype=np.uint16)[None, :]),
+    ("all_verbatim", lambda: (np.arange(20 * 64, dtype=np.uint32) * 251).astype(np.uint16).reshape(20, 64)),
+    ("one_row", lambda: synth.small_gaussian(1, 64, seed=3)["w"]),
+    ("student_t", lambda: synth.student_t_bf16(np.random.default_rng(5), (48, 1024), 3, 0.02)),
+    ("uniform_bits", lambda: np.random.default_rng(6).integers(0, 65536, size=(33, 320)).astype(np.uint16)),
+]
+
+
+@pytest.mark.parametrize("name,make", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("chunk", [64, 512, 4096])
+def test_encoder_blob_equals_oracle(name, make, chunk):
+    w = make()
+    blob = uw.uw_encode(w, chunk)
+    ref = oracle_blob(w, chunk)
+    assert blob.size == ref.size
+    assert np.array_equal(blob, ref)
+
+
+@pytest.mark.parametrize("threads", ["1", "3", "8"])
+def test_encoder_independent_of_thread_count(threads, monkeypatch):
+    monkeypatch.setenv("UW_HOST_THREADS", threads)
+    w = synth.small_gaussian(257, 1024, seed=9, plant_frac=0.01)["w"]
+    assert np.array_equal(uw.uw_encode(w, 256), oracle_blob(w, 256))
+
+
+def test_config1_blob_equals_oracle():
+    w = synth.config1()["w"]
+    assert np.array_equal(uw.uw_encode(w), oracle_blob(w))
+
+
+def test_palette_matches_oracle():
+    w = synth.small_gaussian(64, 640, seed=7, plant_frac=0.1)["w"]
+    p = uw.uw_build_palette(w)
+    e, _ = codec.split_fields(w)
+    hist = codec.exponent_histogram(e)
+    pal, index_of = codec.build_palette(hist)
+    assert p["exp"] == list(pal) and p["n"] == len(pal)
+    assert np.array_equal(p["index_of"], index_of)
+    assert np.array_equal(p["hist"], hist)
+
+
+def test_blob_info_fields():
+    w = synth.small_gaussian(50, 256, seed=3, plant_frac=0.05)["w"]
+    blob = uw.uw_encode(w)
+    info = uw.uw_blob_info(blob)
+    enc = codec.encode(w, 50, 256)
+    assert info["n"] == 50 and info["k"] == 256 and info["np"] == 64 and info["tiles"] == 4 and info["kb"] == 4
+    assert info["n_verb"] == enc["n_verb"] and info["n_coded"] == enc["n_coded"]
+    assert info["total_bits"] == enc["total_bits"]
+    assert info["palette"][: info["n_pal"]] == list(enc["palette"])
+    assert info["resident_bytes"] == codec.resident_palette_bytes(enc)
+    assert info["idx_bytes"] == 64 * 256 // 2
+    assert info["blob_bytes"] == blob.size
+    assert info["affine"] == int(all(enc["palette"][i] == enc["palette"][0] + i for i in range(len(enc["palette"]))))
+
+
+def test_encode_bound_covers_worst_case():
+    for w in (CASES[7][1](), CASES[4][1](), synth.small_gaussian(40, 128, seed=1)["w"]):
+        n, k = w.shape
+        assert uw.uw_encode(w).size <= uw.uw_encode_bound(n, k)
+
+
+# ------------------------------------------------------------------ error paths
+def status_of(fn, *args):
+    with pytest.raises(uw.UwError) as ei:
+        fn(*args)
+    return ei.value.status
+
+
+def test_shape_errors():
+    assert status_of(uw.uw_encode, np.zeros((4, 100), np.uint16)) == uw.UW_E_SHAPE
+    assert status_of(uw.uw_encode, np.zeros((4, 32), np.uint16)) == uw.UW_E_ARG
+    assert status_of(uw.uw_encode, np.zeros((4, 64), np.uint16), 100) == uw.UW_E_ARG
+    assert status_of(uw.uw_build_palette, np.zeros((4, 130), np.uint16)) == uw.UW_E_SHAPE
+
+
+def corrupt(blob, offset, data):
+    b = blob.copy()
+    b[offset: offset + len(data)] = np.frombuffer(bytes(data), np.uint8)
+    return b
+
+
+def test_blob_validation_rejects_corruption():
+    w = synth.small_gaussian(40, 256, seed=5, plant_frac=0.1)["w"]
+    blob = uw.uw_encode(w, 128)
+    info = uw.uw_blob_info(blob)
+    bad = [
+        corrupt(blob, 0, b"XXXX"),                                        # magic
+        corrupt(blob, 4, (2).to_bytes(4, "little")),                       # version
+        corrupt(blob, 12, (100).to_bytes(4, "little")),                    # k not a multiple of 64
+        corrupt(blob, 24, (100).to_bytes(4, "little")),                    # chunk
+        corrupt(blob, 80, bytes([1, 1, 1] + [0] * 13)),                     # Kraft violated
+        corrupt(blob, 96, (5).to_bytes(2, "little")),                      # non-canonical code
+        corrupt(blob, 128 + 16 * 6 + 8, (10 ** 9).to_bytes(8, "little")),  # words section size
+        blob[: blob.size - 512],                                           # truncated
+    ]
+    vp = int(info["sec_off"][2])
+    bad.append(corrupt(blob, vp + 4, (999).to_bytes(4, "little")))         # vprefix vs flags
+    off = int(info["sec_off"][5])
+    bad.append(corrupt(blob, off + 4, (3).to_bytes(4, "little")))           # chunk offset span
+    cb = int(info["sec_off"][4])
+    bad.append(corrupt(blob, cb + 4, (77).to_bytes(4, "little")))          # cbase
+    fl = int(info["sec_off"][1])
+    last_tile_flags = fl + 2 * 4 * (info["tiles"] - 1)
+    bad.append(corrupt(blob, last_tile_flags, (0x8000).to_bytes(2, "little")))  # flag on a padding row
+    for b in bad:
+        assert status_of(uw.uw_blob_info, b) == uw.UW_E_FORMAT
+
+
+def test_autotune_table_roundtrip(tmp_path):
+    uw.uw_autotune_clear()
+    assert uw.uw_autotune_get(14336, 4096, 1) == (uw.UW_PIPE_DIRECT_PALETTE, -1)
+    uw.uw_autotune_set(14336, 4096, 1, uw.UW_PIPE_TRANSCODE, 3)
+    assert uw.uw_autotune_get(14336, 4096, 1) == (uw.UW_PIPE_TRANSCODE, 3)
+    p = tmp_path / "tune.txt"
+    p.write_text("# n k m pipeline variant\n4096 14336 8 1 2\n\n4096 14336 64 4 -1  # comment\n")
+    uw.uw_autotune_clear()
+    uw.uw_autotune_load(str(p))
+    assert uw.uw_autotune_get(4096, 14336, 8) == (uw.UW_PIPE_FULL_DECODE, 2)
+    assert uw.uw_autotune_get(4096, 14336, 64) == (uw.UW_PIPE_DIRECT_PALETTE, -1)
+    p.write_text("4096 14336 8 9 0\n")
+    assert status_of(uw.uw_autotune_load, str(p)) == uw.UW_E_ARG
+    assert status_of(uw.uw_autotune_set, 1, 64, 1, uw.UW_PIPE_AUTO, 0) == uw.UW_E_ARG
+    uw.uw_autotune_clear()
+
+
+def test_variant_names():
+    n = uw.uw_variant_count()
+    assert n >= 4
+    assert all(uw.uw_variant_name(v).startswith("waves=") for v in range(n))
+    assert uw.uw_variant_name(n) == ""
