@@ -118,7 +118,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--variant", type=int, default=-1)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run three device copies of 512 MiB (HBM counter calibration) and exit")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        src = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device="cuda:0").fill_(1)
+        for _ in range(3):
+            src.clone()
+        torch.cuda.synchronize()
+        print("copied 3 x 512 MiB", file=sys.stderr)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (--gpus %d refused)" % args.gpus,
               file=sys.stderr)
