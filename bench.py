@@ -30,7 +30,7 @@ sys.path.insert(0, ROOT)
 METRIC = "decode GEMM eff. weight GB/s & % HBM peak; bits/weight (8B MLP, M=1-64)"
 HBM_PEAK_GBS = 8000.0
 ROTATE_BYTES = 512e6
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_direct_palette_gate14336x4096_m1_pmc.md")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_direct_palette_gate14336x4096_m1_pmc.txt")
 
 
 def log(*a):
@@ -117,7 +117,7 @@ def main():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--variant", type=int, default=-1)
+    ap.add_argument("--variant", type=int, default=-1, help="fused-kernel variant id (default: autotuned)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run three device copies of 512 MiB (HBM counter calibration) and exit")
     args = ap.parse_args()
@@ -136,7 +136,7 @@ def main():
 
     import torch
     import lossless_bf16_weight_amd as uw
-    from lossless_bf16_weight_amd import synth
+    from lossless_bf16_weight_amd import autotune, synth
     from oracle import gemm as ogemm
 
     assert torch.cuda.is_available(), "no GPU"
@@ -152,28 +152,33 @@ def main():
     enc_s = time.time() - t0
     info = uw.uw_blob_info(blob)
     resident = int(info["resident_bytes"])
-    copies = max(2, int(np.ceil(ROTATE_BYTES / resident)))
+    # Rotated device copies (compressed and uncompressed), each cache-cold per launch, and the
+    # per-(shape, M) variant choice by measurement for both the fused kernel and the BF16 GEMV.
+    tuner = autotune.Tuner(w, blob=blob, rotate_bytes=ROTATE_BYTES)
+    copies, mats = tuner.copies, tuner.mats
     log("encoded in %.2fs: bundle %.3f b/w, resident %.3f b/w, %d copies" % (
         enc_s, 8 * blob.size / (n * k), 8 * resident / (n * k), copies))
-    mats = []
+    table = tuner.tune([1], pipelines=(uw.UW_PIPE_DIRECT_PALETTE,), bf16=True)
+    table.apply()
+    pal_variant = uw.uw_autotune_get_variant(n, k, 1, uw.UW_PIPE_DIRECT_PALETTE) if args.variant < 0 else args.variant
+    bf16_variant = uw.uw_autotune_get_variant(n, k, 1, uw.UW_PIPE_BF16)
+    log("autotuned: direct palette variant %d (%s), bf16 variant %d (%s)" % (
+        pal_variant, uw.uw_variant_name(pal_variant), bf16_variant, uw.uw_variant_name(bf16_variant)))
+    # load-time transcode (Huffman -> 4-bit indices), timed on the copies
     t_tc = []
-    for i in range(copies):
-        bd = torch.from_numpy(blob).to(dev)
-        idx = torch.empty(int(info["idx_bytes"]), dtype=torch.uint8, device=dev)
-        d = uw.DMat(blob, bd, idx)
-        ws = torch.zeros(64, dtype=torch.int32, device=dev)
+    ws = torch.zeros(64, dtype=torch.int32, device=dev)
+    for d in mats:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        uw.uw_transcode_palette(d, idx, ws)              # load-time transcode (device kernel)
+        uw.uw_transcode_palette(d, d.idx, ws)
         e1.record(stream)
         uw.uw_check(ws)
         t_tc.append(e0.elapsed_time(e1))
-        mats.append(d)
     xd = torch.from_numpy(x.view(np.int16)).to(dev)
     y = torch.empty((1, n), dtype=torch.float32, device=dev)
 
     def step(i):
-        uw.uw_gemm_variant(mats[i], xd, y, 1, uw.UW_PIPE_DIRECT_PALETTE, args.variant)
+        uw.uw_gemm_variant(mats[i], xd, y, 1, uw.UW_PIPE_DIRECT_PALETTE, pal_variant)
 
     # parity of the timed configuration on sampled rows
     step(0)
@@ -192,12 +197,11 @@ def main():
     achieved = alg_bytes / (us * 1e-6) / 1e9
 
     # uncompressed comparators: own BF16 GEMV and torch (hipBLASLt) on BF16 W
-    wcopies = max(2, int(np.ceil(ROTATE_BYTES / (2 * n * k))))
-    wd = [torch.from_numpy(w.view(np.int16)).to(dev) for _ in range(wcopies)]
+    wcopies, wd = tuner.wcopies, tuner.wd
     yb = torch.empty((1, n), dtype=torch.float32, device=dev)
 
     def step_bf16(i):
-        uw.uw_gemm_bf16(wd[i], xd, yb, 1, -1)
+        uw.uw_gemm_bf16(wd[i], xd, yb, 1, bf16_variant)
 
     tot_b, per_b = time_launches(step_bf16, wcopies, args.steps, args.warmup, stream)
     us_b = tot_b * 1e3 / args.steps
@@ -230,7 +234,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": "Llama-3.1-8B gate_proj 14336x4096 N(0,0.02^2), 0.05% rows planted, "
                                "direct-palette fused GEMV M=1, fp32 out",
-                   "n": n, "k": k, "m": 1, "pipeline": "direct_palette", "variant": args.variant,
+                   "n": n, "k": k, "m": 1, "pipeline": "direct_palette",
+                   "variant": uw.uw_variant_name(pal_variant), "bf16_variant": uw.uw_variant_name(bf16_variant),
                    "rotation_copies": copies, "global_batch": 1, "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),

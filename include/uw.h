@@ -78,7 +78,8 @@ enum {
   UW_PIPE_FULL_DECODE = 1,    /* Huffman -> BF16 W in workspace, then BF16 GEMM */
   UW_PIPE_EXP_ONLY = 2,       /* Huffman -> exponent bytes in workspace, then sm+exp GEMM */
   UW_PIPE_TRANSCODE = 3,      /* Huffman -> 4-bit indices in workspace, then palette GEMM */
-  UW_PIPE_DIRECT_PALETTE = 4  /* resident 4-bit indices (bound at uw_dmat_bind), palette GEMM */
+  UW_PIPE_DIRECT_PALETTE = 4, /* resident 4-bit indices (bound at uw_dmat_bind), palette GEMM */
+  UW_PIPE_BF16 = 5            /* autotune key of the uncompressed uw_gemm_bf16 (not a uw_gemm pipeline) */
 };
 #define UW_MAX_M 256
 #define UW_MAX_CHUNK 4096
@@ -169,7 +170,8 @@ uw_status uw_decode_exponents(const uw_dmat* d, uint8_t* exp_out, void* ws, size
 
 /* Y = X W^T with W rebuilt on chip (reconstructive-matmul paragraphs).
  * x: device [m, k] BF16; y: device [m, n] fp32; 1 <= m <= UW_MAX_M.
- * pipeline: UW_PIPE_*; variant: kernel variant id (uw_variant_count), -1 = autotuned/default.
+ * pipeline: UW_PIPE_AUTO..UW_PIPE_DIRECT_PALETTE; variant: kernel variant id (uw_variant_count),
+ * -1 = the autotune table's variant for (n, k, m, pipeline), else the built-in default.
  * ws: workspace of uw_workspace_size(d, m, pipeline) bytes (may be NULL when that size is 0).
  * Errors: UW_E_ARG, UW_E_SHAPE, UW_E_WORKSPACE, UW_E_HIP. */
 uw_status uw_gemm(const uw_dmat* d, const uint16_t* x, float* y, int32_t m, int32_t pipeline,
@@ -179,7 +181,7 @@ uw_status uw_gemm_variant(const uw_dmat* d, const uint16_t* x, float* y, int32_t
                           hipStream_t s);
 
 /* Uncompressed baseline (the BF16 GEMM of pipeline 1): Y = X W^T for a plain BF16 W
- * (device, [n, k] row-major).  variant: -1 = default. */
+ * (device, [n, k] row-major).  variant: -1 = the UW_PIPE_BF16 autotune entry, else default. */
 uw_status uw_gemm_bf16(const uint16_t* w, int64_t n, int64_t k, const uint16_t* x, float* y,
                        int32_t m, int32_t variant, hipStream_t s);
 
@@ -190,12 +192,25 @@ const char* uw_variant_name(int32_t variant);
 /* Wait for s and report a data error recorded in ws (UW_E_DATA), clearing it. */
 uw_status uw_check(void* ws, hipStream_t s);
 
-/* Autotune table used by UW_PIPE_AUTO and variant -1 (autotuning paragraphs).
- * Text file, one entry per line: "n k m pipeline variant"; '#' starts a comment.
- * A missing entry means DIRECT_PALETTE with the default variant. */
+/* Autotune table (autotuning paragraphs: the pipeline and kernel are chosen per weight shape
+ * and batch size by measurement).  Two kinds of entry, keyed by (n, k, m):
+ *  - the pipeline UW_PIPE_AUTO runs, with its variant (uw_autotune_set; it also records that
+ *    variant for that pipeline);
+ *  - the variant a concrete pipeline, or UW_PIPE_BF16 for uw_gemm_bf16, runs with when called
+ *    with variant -1 (uw_autotune_set_variant; variant -1 deletes the entry).
+ * Missing entries: AUTO runs DIRECT_PALETTE; variant -1 takes the built-in default.
+ * Text file for uw_autotune_load, one entry per line, '#' starts a comment:
+ *     n k m pipeline variant             (AUTO entry)
+ *     variant n k m pipeline variant     (per-pipeline variant)
+ * The file is parsed and checked whole before any entry is applied (UW_E_ARG on a bad line).
+ * The table is process-wide and guarded by a mutex. */
 uw_status uw_autotune_load(const char* path);
 uw_status uw_autotune_set(int64_t n, int64_t k, int32_t m, int32_t pipeline, int32_t variant);
 uw_status uw_autotune_get(int64_t n, int64_t k, int32_t m, int32_t* pipeline, int32_t* variant);
+uw_status uw_autotune_set_variant(int64_t n, int64_t k, int32_t m, int32_t pipeline,
+                                  int32_t variant);
+uw_status uw_autotune_get_variant(int64_t n, int64_t k, int32_t m, int32_t pipeline,
+                                  int32_t* variant);
 uw_status uw_autotune_clear(void);
 
 /* Glue of an MLP decode step (SwiGLU between up/gate and down):

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libuw.so")
 
 UW_OK, UW_E_ARG, UW_E_SHAPE, UW_E_FORMAT, UW_E_NOMEM, UW_E_WORKSPACE, UW_E_HIP, UW_E_DATA = 0, -1, -2, -3, -4, -5, -6, -7
 UW_PIPE_AUTO, UW_PIPE_FULL_DECODE, UW_PIPE_EXP_ONLY, UW_PIPE_TRANSCODE, UW_PIPE_DIRECT_PALETTE = 0, 1, 2, 3, 4
+UW_PIPE_BF16 = 5
 UW_OP_DECODE_FULL, UW_OP_TRANSCODE, UW_OP_DECODE_EXP = 16, 17, 18
 UW_MAX_M = 256
 PIPELINES = {"full": UW_PIPE_FULL_DECODE, "exp": UW_PIPE_EXP_ONLY, "transcode": UW_PIPE_TRANSCODE,
@@ -29,7 +30,8 @@ EXPORTS = ("uw_last_error", "uw_version", "uw_build_palette", "uw_encode_bound",
            "uw_dmat_size", "uw_dmat_bind", "uw_dmat_get_info", "uw_workspace_size", "uw_decode_full",
            "uw_transcode_palette", "uw_decode_exponents", "uw_gemm", "uw_gemm_variant", "uw_gemm_bf16",
            "uw_variant_count", "uw_variant_name", "uw_check", "uw_autotune_load", "uw_autotune_set",
-           "uw_autotune_get", "uw_autotune_clear", "uw_swiglu", "uw_rmsnorm")
+           "uw_autotune_get", "uw_autotune_set_variant", "uw_autotune_get_variant", "uw_autotune_clear", "uw_swiglu",
+           "uw_rmsnorm")
 
 
 class UwError(RuntimeError):
@@ -95,6 +97,8 @@ def lib():
         "uw_autotune_load": (_I32, [ctypes.c_char_p]),
         "uw_autotune_set": (_I32, [_I64, _I64, _I32, _I32, _I32]),
         "uw_autotune_get": (_I32, [_I64, _I64, _I32, ctypes.POINTER(_I32), ctypes.POINTER(_I32)]),
+        "uw_autotune_set_variant": (_I32, [_I64, _I64, _I32, _I32, _I32]),
+        "uw_autotune_get_variant": (_I32, [_I64, _I64, _I32, _I32, ctypes.POINTER(_I32)]),
         "uw_autotune_clear": (_I32, []),
         "uw_swiglu": (_I32, [_P, _P, _P, _I64, _P]),
         "uw_rmsnorm": (_I32, [_P, _P, _I32, _I32, _F, _P]),
@@ -252,6 +256,16 @@ def uw_autotune_get(n, k, m):
     p, v = ctypes.c_int32(), ctypes.c_int32()
     _check(lib().uw_autotune_get(n, k, m, ctypes.byref(p), ctypes.byref(v)))
     return p.value, v.value
+
+
+def uw_autotune_set_variant(n, k, m, pipeline, variant):
+    _check(lib().uw_autotune_set_variant(n, k, m, pipeline, variant))
+
+
+def uw_autotune_get_variant(n, k, m, pipeline):
+    v = ctypes.c_int32()
+    _check(lib().uw_autotune_get_variant(n, k, m, pipeline, ctypes.byref(v)))
+    return v.value
 
 
 def uw_autotune_clear():

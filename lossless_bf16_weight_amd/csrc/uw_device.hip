@@ -1005,6 +1005,7 @@ uw_status uw_gemm_variant(const uw_dmat* d, const uint16_t* x, float* y, int32_t
     }
   }
   if (pipeline < UW_PIPE_FULL_DECODE || pipeline > UW_PIPE_DIRECT_PALETTE) return fail(UW_E_ARG, "bad pipeline %d", pipeline);
+  if (variant < 0) variant = autotune_variant(d->info.n, d->info.k, m, pipeline);
   size_t need = 0;
   st = uw_workspace_size(d, m, pipeline, &need);
   if (st) return st;
@@ -1055,6 +1056,7 @@ uw_status uw_gemm_bf16(const uint16_t* w, int64_t n, int64_t k, const uint16_t* 
   if (k % 64 || k > kMaxK) return fail(UW_E_SHAPE, "k=%lld must be a multiple of 64 up to %lld", (long long)k, (long long)kMaxK);
   if (m < 1 || m > UW_MAX_M) return fail(UW_E_SHAPE, "m=%d outside [1, %d]", m, UW_MAX_M);
   if (variant < -1 || variant >= kNumVariants) return fail(UW_E_ARG, "bad variant %d", variant);
+  if (variant < 0) variant = autotune_variant(n, k, m, UW_PIPE_BF16);
   GemmArgs a;
   std::memset(&a, 0, sizeof(a));
   a.aux = reinterpret_cast<const uint8_t*>(w);

@@ -539,8 +539,11 @@ uw_status validate_blob(const void* blob, size_t bytes, uw_info* info) {
 // ---------------------------------------------------------------------------------------
 // Autotune table
 // ---------------------------------------------------------------------------------------
+// Two maps: the pipeline UW_PIPE_AUTO takes for (n, k, m), and the variant each concrete
+// pipeline (and the uncompressed UW_PIPE_BF16 key) runs with when called with variant -1.
 static std::mutex g_tune_mu;
 static std::map<std::tuple<int64_t, int64_t, int32_t>, std::pair<int32_t, int32_t>> g_tune;
+static std::map<std::tuple<int64_t, int64_t, int32_t, int32_t>, int32_t> g_tune_var;
 
 bool autotune_lookup(int64_t n, int64_t k, int32_t m, int32_t* pipeline, int32_t* variant) {
   std::lock_guard<std::mutex> lk(g_tune_mu);
@@ -549,6 +552,12 @@ bool autotune_lookup(int64_t n, int64_t k, int32_t m, int32_t* pipeline, int32_t
   *pipeline = it->second.first;
   *variant = it->second.second;
   return true;
+}
+
+int32_t autotune_variant(int64_t n, int64_t k, int32_t m, int32_t pipeline) {
+  std::lock_guard<std::mutex> lk(g_tune_mu);
+  auto it = g_tune_var.find(std::make_tuple(n, k, m, pipeline));
+  return it == g_tune_var.end() ? -1 : it->second;
 }
 
 }  // namespace uw
@@ -611,13 +620,34 @@ uw_status uw_blob_info(const void* blob_host, size_t bytes, uw_info* out) {
   }
 }
 
+static uw_status check_tune_key(int64_t n, int64_t k, int32_t m, int32_t variant) {
+  if (variant < -1 || variant >= uw_variant_count()) return fail(UW_E_ARG, "bad variant %d", variant);
+  if (n < 1 || k < 1 || m < 1 || m > UW_MAX_M) return fail(UW_E_ARG, "bad key");
+  return UW_OK;
+}
+
 uw_status uw_autotune_set(int64_t n, int64_t k, int32_t m, int32_t pipeline, int32_t variant) {
   if (pipeline < UW_PIPE_FULL_DECODE || pipeline > UW_PIPE_DIRECT_PALETTE)
     return fail(UW_E_ARG, "pipeline %d is not a concrete pipeline", pipeline);
-  if (variant < -1 || variant >= uw_variant_count()) return fail(UW_E_ARG, "bad variant %d", variant);
-  if (n < 1 || k < 1 || m < 1 || m > UW_MAX_M) return fail(UW_E_ARG, "bad key");
+  uw_status st = check_tune_key(n, k, m, variant);
+  if (st) return st;
   std::lock_guard<std::mutex> lk(g_tune_mu);
   g_tune[std::make_tuple(n, k, m)] = std::make_pair(pipeline, variant);
+  if (variant >= 0) g_tune_var[std::make_tuple(n, k, m, pipeline)] = variant;
+  clear_error();
+  return UW_OK;
+}
+
+uw_status uw_autotune_set_variant(int64_t n, int64_t k, int32_t m, int32_t pipeline, int32_t variant) {
+  if (pipeline < UW_PIPE_FULL_DECODE || pipeline > UW_PIPE_BF16)
+    return fail(UW_E_ARG, "pipeline %d has no variant of its own", pipeline);
+  uw_status st = check_tune_key(n, k, m, variant);
+  if (st) return st;
+  std::lock_guard<std::mutex> lk(g_tune_mu);
+  if (variant < 0)
+    g_tune_var.erase(std::make_tuple(n, k, m, pipeline));
+  else
+    g_tune_var[std::make_tuple(n, k, m, pipeline)] = variant;
   clear_error();
   return UW_OK;
 }
@@ -632,9 +662,19 @@ uw_status uw_autotune_get(int64_t n, int64_t k, int32_t m, int32_t* pipeline, in
   return UW_OK;
 }
 
+uw_status uw_autotune_get_variant(int64_t n, int64_t k, int32_t m, int32_t pipeline, int32_t* variant) {
+  if (!variant) return fail(UW_E_ARG, "null argument");
+  if (pipeline < UW_PIPE_FULL_DECODE || pipeline > UW_PIPE_BF16)
+    return fail(UW_E_ARG, "pipeline %d has no variant of its own", pipeline);
+  *variant = autotune_variant(n, k, m, pipeline);
+  clear_error();
+  return UW_OK;
+}
+
 uw_status uw_autotune_clear(void) {
   std::lock_guard<std::mutex> lk(g_tune_mu);
   g_tune.clear();
+  g_tune_var.clear();
   clear_error();
   return UW_OK;
 }
@@ -645,21 +685,42 @@ uw_status uw_autotune_load(const char* path) {
   if (!in) return fail(UW_E_ARG, "cannot open %s", path);
   std::string line;
   int lineno = 0;
-  std::vector<std::tuple<int64_t, int64_t, int32_t, int32_t, int32_t>> rows;
+  // (is_variant_line, n, k, m, pipeline, variant); applied only once the whole file parsed.
+  std::vector<std::tuple<bool, int64_t, int64_t, int32_t, int32_t, int32_t>> rows;
   while (std::getline(in, line)) {
     ++lineno;
     const size_t hash = line.find('#');
     if (hash != std::string::npos) line.resize(hash);
     std::istringstream ss(line);
+    std::string first;
+    if (!(ss >> first)) continue;
+    const bool var_line = first == "variant";
     long long n, k;
     int m, p, v;
-    if (!(ss >> n)) continue;
-    if (!(ss >> k >> m >> p >> v)) return fail(UW_E_ARG, "%s:%d: expected 'n k m pipeline variant'", path, lineno);
-    rows.emplace_back(n, k, m, p, v);
+    if (var_line) {
+      if (!(ss >> n)) return fail(UW_E_ARG, "%s:%d: expected 'variant n k m pipeline variant'", path, lineno);
+    } else {
+      char* end = nullptr;
+      n = std::strtoll(first.c_str(), &end, 10);
+      if (!end || *end) return fail(UW_E_ARG, "%s:%d: expected 'n k m pipeline variant'", path, lineno);
+    }
+    std::string rest;
+    if (!(ss >> k >> m >> p >> v) || (ss >> rest))
+      return fail(UW_E_ARG, "%s:%d: expected 'n k m pipeline variant'", path, lineno);
+    rows.emplace_back(var_line, n, k, m, p, v);
   }
   for (auto& r : rows) {
-    uw_status st = uw_autotune_set(std::get<0>(r), std::get<1>(r), std::get<2>(r), std::get<3>(r), std::get<4>(r));
+    const int32_t p = std::get<4>(r);
+    uw_status st = check_tune_key(std::get<1>(r), std::get<2>(r), std::get<3>(r), std::get<5>(r));
     if (st) return st;
+    const int32_t hi = std::get<0>(r) ? UW_PIPE_BF16 : UW_PIPE_DIRECT_PALETTE;
+    if (p < UW_PIPE_FULL_DECODE || p > hi) return fail(UW_E_ARG, "%s: pipeline %d not allowed here", path, p);
+  }
+  for (auto& r : rows) {
+    if (std::get<0>(r))
+      uw_autotune_set_variant(std::get<1>(r), std::get<2>(r), std::get<3>(r), std::get<4>(r), std::get<5>(r));
+    else
+      uw_autotune_set(std::get<1>(r), std::get<2>(r), std::get<3>(r), std::get<4>(r), std::get<5>(r));
   }
   clear_error();
   return UW_OK;

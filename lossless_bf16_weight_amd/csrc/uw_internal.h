@@ -74,4 +74,6 @@ constexpr uint64_t kDmatMagic = 0x3130544D44575555ull;  // "UUWDMT01"
 namespace uw {
 // Autotune table (host): lookup for (n, k, m).
 bool autotune_lookup(int64_t n, int64_t k, int32_t m, int32_t* pipeline, int32_t* variant);
+// Variant recorded for one pipeline (or UW_PIPE_BF16) at (n, k, m); -1 when none.
+int32_t autotune_variant(int64_t n, int64_t k, int32_t m, int32_t pipeline);
 }  // namespace uw

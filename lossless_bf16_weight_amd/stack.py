@@ -1,0 +1,85 @@
+"""A stack of LLM MLP layers served from compressed weights: one decode step.
+
+Per layer l with input x_l [m, hidden] (BF16):
+    g = x_l gate^T, u = x_l up^T        (fused reconstruct GEMMs, fp32 out)
+    h = bf16(silu(g) * u)               (SwiGLU, uw_swiglu)
+    y = h down^T                        (fused reconstruct GEMM, fp32 out)
+    x_{l+1} = bf16(y / sqrt(mean(y^2) + eps))   (weightless RMS norm, uw_rmsnorm)
+
+The Unweight post compresses the MLP projections of Llama-3.1-8B (gate, up, down) and runs
+them through its reconstructive matmul; the SwiGLU and the norm between layers are the
+model's own glue, kept here so a multi-layer step stays finite.  Every step runs in libuw's
+kernels on one stream; this class only holds the buffers and issues the calls.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import UW_PIPE_AUTO, CompressedMatrix, uw_check, uw_gemm, uw_rmsnorm, uw_swiglu, uw_workspace_size
+
+
+class MLPStack:
+    def __init__(self, m, hidden, inter, device="cuda:0", eps=1e-5):
+        import torch
+        self.m, self.hidden, self.inter, self.eps = m, hidden, inter, eps
+        self.dev = torch.device(device)
+        self.layers = []                                  # [(gate, up, down) CompressedMatrix]
+        self.g = torch.empty((m, inter), dtype=torch.float32, device=self.dev)
+        self.u = torch.empty((m, inter), dtype=torch.float32, device=self.dev)
+        self.h = torch.empty((m, inter), dtype=torch.int16, device=self.dev)
+        self.y = torch.empty((m, hidden), dtype=torch.float32, device=self.dev)
+        self.xs = [torch.empty((m, hidden), dtype=torch.int16, device=self.dev) for _ in range(2)]
+        self.ws = None
+        self.ws_bytes = 0
+
+    def add_layer(self, gate, up, down, chunk=0):
+        """gate, up: [inter, hidden]; down: [hidden, inter] BF16 bit patterns (host uint16),
+        or CompressedMatrix objects already on this device."""
+        mats = []
+        for w, shape in ((gate, (self.inter, self.hidden)), (up, (self.inter, self.hidden)),
+                         (down, (self.hidden, self.inter))):
+            cm = w if isinstance(w, CompressedMatrix) else CompressedMatrix(w, chunk=chunk, device=self.dev)
+            if (cm.n, cm.k) != shape:
+                raise ValueError("layer matrix is %dx%d, expected %dx%d" % (cm.n, cm.k, *shape))
+            mats.append(cm)
+        self.layers.append(tuple(mats))
+
+    def _workspace(self, pipeline):
+        import torch
+        need = max(uw_workspace_size(cm.d, self.m, pipeline) for lay in self.layers for cm in lay)
+        if need > self.ws_bytes:
+            self.ws = torch.zeros(need, dtype=torch.uint8, device=self.dev)
+            self.ws_bytes = need
+        return self.ws if need else None
+
+    def step(self, x, pipeline=UW_PIPE_AUTO, trace=None):
+        """x: device int16 [m, hidden] (BF16 bits).  Returns the device tensor holding the last
+        layer's output (one of two ping-pong buffers).  trace: optional list that receives,
+        per layer, host copies (x_in, g, u, h, y, x_out) -- for tests; it synchronises."""
+        ws = self._workspace(pipeline)
+        cur = x
+        for i, (gate, up, down) in enumerate(self.layers):
+            out = self.xs[i % 2]
+            uw_gemm(gate.d, cur, self.g, self.m, pipeline, ws)
+            uw_gemm(up.d, cur, self.u, self.m, pipeline, ws)
+            uw_swiglu(self.g, self.u, self.h)
+            uw_gemm(down.d, self.h, self.y, self.m, pipeline, ws)
+            uw_rmsnorm(self.y, out, self.eps)
+            if trace is not None:
+                trace.append(tuple(t.cpu().numpy().copy() for t in (cur, self.g, self.u, self.h, self.y, out)))
+            cur = out
+        if ws is not None:
+            uw_check(ws)
+        return cur
+
+    def resident_bytes(self):
+        return sum(cm.resident_bytes() for lay in self.layers for cm in lay)
+
+    def weight_count(self):
+        return sum(cm.n * cm.k for lay in self.layers for cm in lay)
+
+
+def as_bf16_bits(t):
+    """Host uint16 view of a device or host int16 tensor/array."""
+    a = t if isinstance(t, np.ndarray) else t.cpu().numpy()
+    return a.view(np.uint16)

@@ -27,7 +27,12 @@ import numpy as np
 def f32_to_bf16_bits(a):
     """fp32 -> BF16 bit patterns, round to nearest even (finite inputs)."""
     b = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
-    return ((b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
+    r = b >> np.uint32(16)                # in place from here: one temporary for any size
+    r &= np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += b
+    r >>= np.uint32(16)
+    return r.astype(np.uint16)
 
 
 def gaussian_bf16(rng, shape, std):
@@ -100,24 +105,38 @@ def config5(seed=4):
     return dict(w=w, x=x)
 
 
-def config4(seed=3, layers=32, m=16, threads=16, hidden=4096, inter=14336):
-    """Stack of `layers` MLP layers.  SeedSequence(seed) spawns 1 + 3*layers children:
-    child 0 draws the per-layer std (U[0.01, 0.03]) then X; child 1 + 3l + j draws matrix
-    j (0 gate [inter, hidden], 1 up [inter, hidden], 2 down [hidden, inter]) of layer l.
-    Matrices are drawn in parallel threads (each from its own child generator)."""
+C4_SHAPES = ((14336, 4096), (14336, 4096), (4096, 14336))   # gate, up [inter, hidden]; down [hidden, inter]
+
+
+def config4_meta(seed=3, layers=32, m=16, hidden=4096):
+    """Per-layer std and X of the MLP stack.  SeedSequence(seed) spawns 1 + 3*layers children:
+    child 0 draws the per-layer std (U[0.01, 0.03]) then X; child 1 + 3l + j draws matrix j
+    (0 gate, 1 up, 2 down) of layer l (config4_matrix)."""
     kids = np.random.SeedSequence(seed).spawn(1 + 3 * layers)
     rng0 = np.random.default_rng(kids[0])
     stds = rng0.uniform(0.01, 0.03, size=layers)
     x = gaussian_bf16(rng0, (m, hidden), 1.0)
-    shapes = [(inter, hidden), (inter, hidden), (hidden, inter)]
+    return dict(stds=stds, x=x, kids=kids)
+
+
+def config4_matrix(meta, l, j, shapes=C4_SHAPES):
+    """Matrix j (0 gate, 1 up, 2 down) of layer l, from its own child generator."""
+    return gaussian_bf16(np.random.default_rng(meta["kids"][1 + 3 * l + j]), shapes[j], meta["stds"][l])
+
+
+def config4(seed=3, layers=32, m=16, threads=16, hidden=4096, inter=14336):
+    """The whole stack at once (about 11 GB of BF16 at full size): matrices are drawn in
+    parallel threads, each from its own child generator, so the values do not depend on
+    the thread count."""
+    meta = config4_meta(seed, layers, m, hidden)
+    shapes = ((inter, hidden), (inter, hidden), (hidden, inter))
 
     def make(i):
-        l, j = divmod(i, 3)
-        return gaussian_bf16(np.random.default_rng(kids[1 + i]), shapes[j], stds[l])
+        return config4_matrix(meta, i // 3, i % 3, shapes)
 
     with ThreadPoolExecutor(max_workers=threads) as ex:
         mats = list(ex.map(make, range(3 * layers)))
-    return dict(stds=stds, x=x, layers=[tuple(mats[3 * l: 3 * l + 3]) for l in range(layers)])
+    return dict(stds=meta["stds"], x=meta["x"], layers=[tuple(mats[3 * l: 3 * l + 3]) for l in range(layers)])
 
 
 def small_gaussian(n, k, m=1, std=0.02, seed=0, plant_frac=0.0):

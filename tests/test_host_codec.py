@@ -166,6 +166,39 @@ def test_autotune_table_roundtrip(tmp_path):
     uw.uw_autotune_clear()
 
 
+def test_autotune_variant_entries(tmp_path):
+    uw.uw_autotune_clear()
+    assert uw.uw_autotune_get_variant(14336, 4096, 1, uw.UW_PIPE_BF16) == -1
+    # an AUTO entry also records the variant of its pipeline
+    uw.uw_autotune_set(14336, 4096, 1, uw.UW_PIPE_DIRECT_PALETTE, 6)
+    assert uw.uw_autotune_get_variant(14336, 4096, 1, uw.UW_PIPE_DIRECT_PALETTE) == 6
+    assert uw.uw_autotune_get_variant(14336, 4096, 1, uw.UW_PIPE_TRANSCODE) == -1
+    uw.uw_autotune_set_variant(14336, 4096, 1, uw.UW_PIPE_BF16, 2)
+    assert uw.uw_autotune_get_variant(14336, 4096, 1, uw.UW_PIPE_BF16) == 2
+    assert uw.uw_autotune_get(14336, 4096, 1) == (uw.UW_PIPE_DIRECT_PALETTE, 6)   # AUTO entry untouched
+    uw.uw_autotune_set_variant(14336, 4096, 1, uw.UW_PIPE_BF16, -1)                # deletes
+    assert uw.uw_autotune_get_variant(14336, 4096, 1, uw.UW_PIPE_BF16) == -1
+    assert status_of(uw.uw_autotune_set_variant, 1, 64, 1, uw.UW_PIPE_AUTO, 0) == uw.UW_E_ARG
+    assert status_of(uw.uw_autotune_set_variant, 1, 64, 1, 6, 0) == uw.UW_E_ARG
+    assert status_of(uw.uw_autotune_set_variant, 1, 64, 1, uw.UW_PIPE_BF16, uw.uw_variant_count()) == uw.UW_E_ARG
+    p = tmp_path / "tune.txt"
+    p.write_text("4096 14336 8 2 1\nvariant 4096 14336 8 5 3\nvariant 4096 14336 8 4 0  # palette\n")
+    uw.uw_autotune_clear()
+    uw.uw_autotune_load(str(p))
+    assert uw.uw_autotune_get(4096, 14336, 8) == (uw.UW_PIPE_EXP_ONLY, 1)
+    assert uw.uw_autotune_get_variant(4096, 14336, 8, uw.UW_PIPE_EXP_ONLY) == 1
+    assert uw.uw_autotune_get_variant(4096, 14336, 8, uw.UW_PIPE_BF16) == 3
+    assert uw.uw_autotune_get_variant(4096, 14336, 8, uw.UW_PIPE_DIRECT_PALETTE) == 0
+    # a bad line anywhere rejects the whole file and applies nothing
+    uw.uw_autotune_clear()
+    for bad in ("variant 4096 14336 8 0 1\n", "variant 4096 14336 8 5\n", "4096 14336 8 4 1 7\n",
+                "4096x 14336 8 4 1\n", "4096 14336 8 4 1\nvariant 1 64 1 5 99\n"):
+        p.write_text(bad)
+        assert status_of(uw.uw_autotune_load, str(p)) == uw.UW_E_ARG, bad
+        assert uw.uw_autotune_get(4096, 14336, 8) == (uw.UW_PIPE_DIRECT_PALETTE, -1)
+    uw.uw_autotune_clear()
+
+
 def test_variant_names():
     n = uw.uw_variant_count()
     assert n >= 4
