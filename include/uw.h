@@ -43,8 +43,9 @@
  *   - words:   Huffman stream of the palette indices of every non-verbatim segment (segment
  *              order, column ascending), codes MSB-first in uint32 words, two zero words after.
  *              Code: optimal length-limited (13 bits) prefix code, canonical.
- *   - off:     uint32 start bit of every chunk, then the total bit count.  A chunk is `chunk`
- *              coded symbols (a multiple of 64); chunks restart at every tile.
+ *   - off:     uint32 start bit of every chunk, then the total bit count.  A chunk is at most
+ *              `chunk` coded symbols (a multiple of 64); chunks restart at every 64-column
+ *              block of every tile, so block b of a tile holds ceil(64*coded rows/chunk).
  *   - cbase:   T+1 uint32; first chunk of every tile.
  *   Direct-palette index stream (made by uw_transcode_palette, held by the caller): np*k/2 bytes;
  *   row r of sub-tile (t, j) owns 8 bytes at ((t*(k/16) + j)*16 + r)*8 = two uint32 words, word w
@@ -108,7 +109,8 @@ uw_status uw_encode_bound(int64_t n, int64_t k, int32_t chunk, size_t* bytes);
 
 /* Encode W into a UW1 blob (Huffman, rare-exponent and four-pipeline paragraphs).
  * w:      host, n*k BF16 bit patterns, row-major.
- * chunk:  coded symbols per chunk, a multiple of 64 in [64, UW_MAX_CHUNK]; 0 = 512.
+ * chunk:  coded symbols per chunk, a multiple of 64 in [64, UW_MAX_CHUNK]; 0 = 512 (a block
+ *         holds at most 1024 coded symbols, so values above 1024 act as 1024).
  * blob:   host output of `cap` bytes; NULL asks for the exact size only (two-call pattern).
  * used:   receives the blob size in bytes.
  * Errors: UW_E_ARG (null w/used), UW_E_SHAPE (k % 64, stream >= 2^32 bits), UW_E_NOMEM,

@@ -485,14 +485,28 @@ __global__ __launch_bounds__((MaxThreads<CT, U>::v)) void k_gemm(GemmArgs a) {
 // =========================================================================================
 // Huffman decoder.
 //
-// One workgroup (one wave) per (tile, group of 64 chunks); lane i decodes chunk
-// cbase[t] + 64*part + i serially.  Chunks restart at every tile and cover whole segments,
-// so a lane places its output from the tile's verbatim flags alone: a wave-level prefix sum
-// of per-block verbatim counts (LDS) gives each block's first coded-segment rank, a binary
-// search finds the chunk's first segment, and the lane then walks forward, skipping verbatim
-// rows.  Workgroup part 0 also writes the verbatim segments and the padding rows.
+// Chunks restart at every 64-column block of every tile, so the work splits into units of
+// whole blocks: one workgroup (one wave) per (tile, group of `nb` blocks), lane i decoding one
+// chunk of the unit (lane = block-in-unit * cpb + chunk-in-block).  A wave-level prefix sum
+// of the blocks' chunk counts places each chunk in the offset table.
+//   1. The unit's slice of the bitstream (contiguous: its chunks are consecutive) is staged
+//      in LDS with coalesced 16-byte loads, so the serial decode never waits on HBM.
+//   2. A 2^10-entry table (LDS) decodes up to four symbols per lookup: entry = symbol count,
+//      first length, total length, four 4-bit symbols.  A window whose first code is longer
+//      than 10 bits (rare: symbols below 2^-10 frequency) points to a block of a secondary
+//      table indexed by the next 3 bits.  The loop body is branch-free apart from that case:
+//      the refill word is read every step and used or not, and every step stores a word
+//      (to the image when 8 indices are ready, else to a per-lane dummy slot).
+//   3. Decoded 4-bit indices go to an LDS image of the unit's output (the direct-palette
+//      index layout), and the workgroup then writes the image with full-line stores; the
+//      exponent and BF16 modes convert the image while writing (palette lookup, verbatim
+//      segments from vexp, sign+mantissa merge for BF16).
 // =========================================================================================
 enum DecMode { DEC_IDX = 0, DEC_EXP = 1, DEC_BF16 = 2 };
+
+constexpr int kDecWin = 10;                 // lookup window, bits
+constexpr int kDecLut = 1 << kDecWin;       // primary entries
+constexpr int kDecSec = 16 * 8;             // secondary entries: 16 blocks of 8 (block 0: invalid)
 
 struct DecArgs {
   const uint32_t* words;
@@ -505,67 +519,55 @@ struct DecArgs {
   uint8_t* out;
   uint32_t* err;
   uint32_t words_cap;
-  int32_t n, k, kb, chunk;
-  uint8_t pal[16];
+  int32_t n, k, kb;
+  int32_t spc, cpb, nb;    // coded segments per chunk, max chunks per block, blocks per unit
+  uint32_t stage_words;    // LDS words for one unit's bitstream slice (host bound)
+  uint32_t tab[4];         // palette, 16 bytes
   uint8_t len[16];
   uint16_t code[16];
+  uint32_t pbase;          // first 10-bit prefix of a code longer than 10 bits
+  uint32_t pmask;          // bit i: prefix pbase + i starts a long code (its block is i + 1)
+  uint32_t sec[kDecSec];   // secondary entries (same format as the primary ones)
 };
 
-struct BitReader {
-  const uint32_t* words;
-  uint32_t cap;
-  u32x4 qa, qb;   // words [base, base+4) and [base+4, base+8)
-  uint32_t base;
-  int ci;         // next word of qa to hand out
-  uint64_t buf;   // stream bits, left aligned
-  int avail;      // valid bits in buf
-  uint32_t pos;   // stream position of buf's top bit
+// Image of a unit's index output: one block is 128 words (4 sub-tiles x 16 rows x 2 words),
+// stored kImgBlk words apart so that lanes writing the same (sub-tile, row) of different
+// blocks hit different LDS banks.
+constexpr int kImgBlk = 132;
 
-  __device__ __forceinline__ u32x4 load4(uint32_t i) const {
-    if (i + 4 <= cap) return *reinterpret_cast<const u32x4*>(words + i);
-    u32x4 v = {0, 0, 0, 0};
-    if (i < cap) v.x = words[i];
-    if (i + 1 < cap) v.y = words[i + 1];
-    if (i + 2 < cap) v.z = words[i + 2];
-    if (i + 3 < cap) v.w = words[i + 3];
-    return v;
-  }
-  __device__ __forceinline__ uint32_t take() {
-    const uint32_t v = ci == 0 ? qa.x : ci == 1 ? qa.y : ci == 2 ? qa.z : qa.w;
-    if (++ci == 4) {
-      qa = qb;
-      base += 4;
-      qb = load4(base + 4);
-      ci = 0;
-    }
-    return v;
-  }
-  __device__ __forceinline__ void init(uint32_t bit) {
-    const uint32_t wi = bit >> 5;
-    base = wi & ~3u;
-    qa = load4(base);
-    qb = load4(base + 4);
-    ci = (int)(wi - base);
-    const uint64_t hi = take(), lo = take();
-    const int o = (int)(bit & 31);
-    buf = ((hi << 32) | lo) << o;
-    avail = 64 - o;
-    pos = bit;
-  }
-  // Next symbol via the 2^13-entry table; returns -1 on an invalid code.
-  __device__ __forceinline__ int next(const uint8_t* lut) {
-    const uint32_t e = lut[(uint32_t)(buf >> 51)];
-    const int L = (int)(e >> 4);
-    buf <<= L;
-    avail -= L;
-    pos += (uint32_t)L;
-    if (avail < 32) {
-      buf |= (uint64_t)take() << (32 - avail);
-      avail += 32;
-    }
-    return L ? (int)(e & 15u) : -1;
-  }
+struct DecLds {            // offsets (bytes) into the dynamic LDS block
+  uint32_t lut, image, stage, blk, total;
 };
+
+// stage_words: a multiple of 256 (the bitstream slice is staged in 1 KB DMA steps).
+__host__ __device__ inline DecLds dec_lds(int nb, uint32_t stage_words) {
+  DecLds L;
+  L.lut = 0;
+  L.image = (kDecLut + kDecSec) * 4;
+  const uint32_t img = std::max<uint32_t>((uint32_t)nb * kImgBlk * 4u, kDecLut * 2u);  // also holds the build table
+  L.stage = L.image + ((img + 15u) & ~15u);
+  L.blk = L.stage + stage_words * 4;
+  L.total = L.blk + 3u * 64u * 4u;   // block flags, verbatim ranks, per-lane dummy slots
+  return L;
+}
+
+__device__ __forceinline__ uint32_t nibbles_to_index_word(uint32_t v) {
+  // Sequential nibbles n0..n7 (n_i at bits 4i) -> index-stream word (even columns in the low
+  // half, odd columns in the high half: n_i at bit 4*(i/2) + 16*(i%2)).
+  uint32_t x = v & 0x0F0F0F0Fu, y = (v >> 4) & 0x0F0F0F0Fu;
+  x = (x | (x >> 4)) & 0x00FF00FFu;
+  y = (y | (y >> 4)) & 0x00FF00FFu;
+  x = (x | (x >> 8)) & 0x0000FFFFu;
+  y = (y | (y >> 8)) & 0x0000FFFFu;
+  return x | (y << 16);
+}
+
+__device__ __forceinline__ u32x2 index_word_to_exps(uint32_t iw, const uint32_t tab[4]) {
+  // 8 indices of one index-stream word -> 8 exponent bytes in column order.
+  const uint32_t e04 = lookup16(iw & 0x0F0F0F0Fu, tab);          // E0 E4 E1 E5
+  const uint32_t e26 = lookup16((iw >> 4) & 0x0F0F0F0Fu, tab);   // E2 E6 E3 E7
+  return u32x2{perm(e26, e04, 0x06040200u), perm(e26, e04, 0x07050301u)};
+}
 
 __device__ __forceinline__ uint32_t bf16_pairs_from(uint32_t s, uint32_t e, int half) {
   // s, e: 4 sign+mantissa bytes and 4 exponent bytes; half 0 -> weights 0,1; 1 -> 2,3.
@@ -574,130 +576,212 @@ __device__ __forceinline__ uint32_t bf16_pairs_from(uint32_t s, uint32_t e, int 
   return (sp & 0x807F807Fu) | ep;
 }
 
-template <int MODE>
-__device__ __forceinline__ void write_segment(const DecArgs& a, int t, int b, int r, int g, const uint32_t v[4],
-                                              bool zero) {
-  // v: for DEC_IDX two nibble words in v[0..1]; otherwise 16 exponent bytes in v[0..3].
-  const size_t sub = ((size_t)t * (a.k / 16) + 4 * b + g) * 16 + r;
-  if constexpr (MODE == DEC_IDX) {
-    u32x2 o = zero ? u32x2{0, 0} : u32x2{v[0], v[1]};
-    *reinterpret_cast<u32x2*>(a.out + sub * 8) = o;
-  } else if constexpr (MODE == DEC_EXP) {
-    u32x4 o = zero ? u32x4{0, 0, 0, 0} : u32x4{v[0], v[1], v[2], v[3]};
-    *reinterpret_cast<u32x4*>(a.out + sub * 16) = o;
-  } else {
-    const u32x4 s = *reinterpret_cast<const u32x4*>(a.sm + sub * 16);
-    const uint32_t ss[4] = {s.x, s.y, s.z, s.w};
-    uint32_t o[8];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      o[2 * q] = bf16_pairs_from(ss[q], v[q], 0);
-      o[2 * q + 1] = bf16_pairs_from(ss[q], v[q], 1);
-    }
-    u32x4* dst = reinterpret_cast<u32x4*>(a.out + ((size_t)(t * 16 + r) * a.k + 64 * b + 16 * g) * 2);
-    dst[0] = u32x4{o[0], o[1], o[2], o[3]};
-    dst[1] = u32x4{o[4], o[5], o[6], o[7]};
+// Build the multi-symbol table.  tmp (kDecLut u16): first-symbol table, entry = symbol |
+// length << 4 | 0x100 for every window whose first code has length <= kDecWin.
+__device__ void build_dec_lut(const DecArgs& a, uint32_t* lut, uint16_t* tmp, int lane) {
+  for (int i = lane; i < kDecLut / 2; i += 64) reinterpret_cast<uint32_t*>(tmp)[i] = 0;
+  __syncthreads();
+  for (int s = 0; s < 16; ++s) {
+    const int L = a.len[s];
+    if (L == 0 || L > kDecWin) continue;
+    const uint32_t lo = (uint32_t)a.code[s] << (kDecWin - L), cnt = 1u << (kDecWin - L);
+    for (uint32_t i = lane; i < cnt; i += 64) tmp[lo + i] = (uint16_t)(s | (L << 4) | 0x100);
   }
+  __syncthreads();
+#pragma unroll 4
+  for (int w = lane; w < kDecLut; w += 64) {
+    const uint32_t e0 = tmp[w];
+    uint32_t entry = 0;
+    if (e0 & 0x100u) {
+      const uint32_t l0 = (e0 >> 4) & 15u;
+      uint32_t used = l0, n = 1, syms = e0 & 15u;
+#pragma unroll
+      for (int j = 1; j < 4; ++j) {
+        const uint32_t ej = tmp[(w << used) & (kDecLut - 1)];
+        const uint32_t lj = (ej >> 4) & 15u;
+        const bool ok = (n == (uint32_t)j) && (ej & 0x100u) && used + lj <= (uint32_t)kDecWin;
+        syms |= ok ? (ej & 15u) << (4 * j) : 0u;
+        used += ok ? lj : 0u;
+        n += ok ? 1u : 0u;
+      }
+      entry = n | (l0 << 3) | (used << 7) | (syms << 16);
+    } else {
+      const uint32_t i = (uint32_t)w - a.pbase;                // long code: secondary block i + 1
+      entry = (i < 15u && ((a.pmask >> i) & 1u)) ? (i + 1u) << 16 : 0u;
+    }
+    lut[w] = entry;
+  }
+  for (int i = lane; i < kDecSec; i += 64) lut[kDecLut + i] = a.sec[i];
+  __syncthreads();
 }
 
 template <int MODE>
 __global__ __launch_bounds__(64) void k_decode(DecArgs a) {
-  __shared__ uint8_t lut[1 << kLmax];
-  __shared__ uint32_t vpre[kMaxK / kSeg + 1];
-  const int t = blockIdx.x, part = blockIdx.y, lane = threadIdx.x;
+  extern __shared__ __align__(16) uint8_t dsh[];
+  const DecLds Ls = dec_lds(a.nb, a.stage_words);
+  uint32_t* lut = reinterpret_cast<uint32_t*>(dsh + Ls.lut);
+  uint32_t* img = reinterpret_cast<uint32_t*>(dsh + Ls.image);
+  uint32_t* stage = reinterpret_cast<uint32_t*>(dsh + Ls.stage);
+  uint32_t* blk_f = reinterpret_cast<uint32_t*>(dsh + Ls.blk);       // flags per block of the unit
+  uint32_t* blk_v = blk_f + 64;                                       // verbatim rank of the block's first
+  const int lane = threadIdx.x;
+  const int t = blockIdx.y;
+  const int bA = blockIdx.x * a.nb;
+  const int nbu = min(a.nb, a.kb - bA);
   const int rows = min(16, a.n - 16 * t);
   const uint32_t realmask = rows == 16 ? 0xFFFFu : ((1u << rows) - 1u);
   const uint16_t* flg = a.flags + (size_t)t * a.kb;
 
-  for (int i = lane; i < (1 << kLmax) / 4; i += 64) reinterpret_cast<uint32_t*>(lut)[i] = 0;
-  __syncthreads();
-  for (int s = 0; s < 16; ++s) {
-    const int L = a.len[s];
-    if (!L) continue;
-    const uint32_t lo = (uint32_t)a.code[s] << (kLmax - L), cnt = 1u << (kLmax - L);
-    for (uint32_t i = lane; i < cnt; i += 64) lut[lo + i] = (uint8_t)(s | (L << 4));
-  }
-  // Exclusive prefix of verbatim segments per block (wave-level scan, 64 blocks a step).
-  uint32_t carry = 0;
-  for (int base = 0; base < a.kb; base += 64) {
-    const int b = base + lane;
-    const uint32_t v = b < a.kb ? (uint32_t)__popc(flg[b]) : 0u;
-    const uint32_t incl = wave_incl_scan(v, lane);
-    if (b < a.kb) vpre[b] = carry + incl - v;
-    carry += __shfl(incl, 63, 64);
-  }
-  if (lane == 0) vpre[a.kb] = carry;
-  __syncthreads();
-
-  const uint32_t c0 = a.cbase[t], c1 = a.cbase[t + 1];
-  const uint32_t c = c0 + (uint32_t)part * 64 + lane;
-  if (c < c1) {
-    const uint32_t nsym_tile = ((uint32_t)rows * a.kb - carry) * 64;
-    const uint32_t ci = c - c0;
-    const uint32_t nseg = min((uint32_t)a.chunk, nsym_tile - ci * a.chunk) / 64;
-    const uint32_t q = ci * (uint32_t)(a.chunk / 64);
-    // last block b with coded-before(b) = rows*b - vpre[b] <= q
-    int lo = 0, hi = a.kb - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if ((uint32_t)rows * mid - vpre[mid] <= q) lo = mid; else hi = mid - 1;
-    }
-    int b = lo;
-    uint32_t cm = realmask & ~(uint32_t)flg[b];
-    for (uint32_t j = q - ((uint32_t)rows * b - vpre[b]); j > 0; --j) cm &= cm - 1;
-    int r = __ffs(cm) - 1;
-
-    BitReader br;
-    br.words = a.words;
-    br.cap = a.words_cap;
-    br.init(a.off[c]);
-    bool bad = false;
-    for (uint32_t sgi = 0; sgi < nseg && !bad; ++sgi) {
-      for (int g = 0; g < 4; ++g) {
-        uint32_t v[4] = {0, 0, 0, 0};
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int sym = br.next(lut);
-          if (sym < 0) bad = true;
-          const uint32_t s = (uint32_t)sym & 15u;
-          if constexpr (MODE == DEC_IDX) {
-            const int ii = i & 7;
-            v[i >> 3] |= s << (4 * (ii >> 1) + 16 * (ii & 1));
-          } else {
-            v[i >> 2] |= (uint32_t)a.pal[s] << (8 * (i & 3));
-          }
-        }
-        write_segment<MODE>(a, t, b, r, g, v, false);
-      }
-      uint32_t m2 = realmask & ~(uint32_t)flg[b] & ~((2u << r) - 1u);
-      while (!m2 && b + 1 < a.kb) {
-        ++b;
-        m2 = realmask & ~(uint32_t)flg[b];
-      }
-      r = m2 ? __ffs(m2) - 1 : 0;
-    }
-    if (bad || br.pos != a.off[c + 1]) atomicOr(a.err, 1u);
-  }
-
-  if (part == 0) {
-    const uint32_t vt = a.vprefix[t];
-    const uint32_t zero4[4] = {0, 0, 0, 0};
-    for (int b = lane; b < a.kb; b += 64) {
+  // Chunks and verbatim segments of the tile's blocks before this unit.
+  uint32_t ch_before = 0, v_before = 0;
+  for (int b0 = 0; b0 < bA; b0 += 64) {
+    const int b = b0 + lane;
+    uint32_t nch = 0, nv = 0;
+    if (b < bA) {
       const uint32_t f = flg[b];
-      uint32_t vr = vt + vpre[b];
-      for (int rr = 0; rr < 16; ++rr) {
-        if (rr < rows && ((f >> rr) & 1u)) {
-          const u32x4* src = reinterpret_cast<const u32x4*>(a.vexp + (size_t)vr * 64);
-          ++vr;
-          for (int g = 0; g < 4; ++g) {
-            const u32x4 e = src[g];
-            const uint32_t v[4] = {e.x, e.y, e.z, e.w};
-            write_segment<MODE>(a, t, b, rr, g, v, MODE == DEC_IDX);
-          }
-        } else if (rr >= rows && MODE != DEC_BF16) {
-          for (int g = 0; g < 4; ++g) write_segment<MODE>(a, t, b, rr, g, zero4, true);
-        }
+      nch = ((uint32_t)__popc(realmask & ~f) + a.spc - 1) / a.spc;
+      nv = __popc(f);
+    }
+    ch_before += wave_sum(nch);
+    v_before += wave_sum(nv);
+  }
+  // This unit's blocks: flags, chunk counts, exclusive prefixes (lane = block in unit).
+  uint32_t f = 0, nch = 0, nv = 0;
+  if (lane < nbu) {
+    f = flg[bA + lane];
+    nch = ((uint32_t)__popc(realmask & ~f) + a.spc - 1) / a.spc;
+    nv = __popc(f);
+  }
+  const uint32_t ch_incl = wave_incl_scan(nch, lane), v_incl = wave_incl_scan(nv, lane);
+  const uint32_t unit_chunks = __shfl(ch_incl, 63, 64);
+  if (lane < nbu) {
+    blk_f[lane] = f;
+    blk_v[lane] = a.vprefix[t] + v_before + v_incl - nv;
+  }
+  const uint32_t c_first = a.cbase[t] + ch_before;
+  const uint32_t ch_pre = ch_incl - nch;                       // per block lane
+
+  // Stage the unit's bitstream slice in 1 KB LDS-DMA steps (no VGPRs, no waits until the
+  // barrier; words past the stream read as zero), and build the table meanwhile.
+  uint32_t wb = 0, nst = 0;
+  if (unit_chunks) {
+    wb = (a.off[c_first] >> 5) & ~3u;
+    const uint32_t we = (a.off[c_first + unit_chunks] >> 5) + 3u;
+    nst = min((we - wb + 255u) & ~255u, a.stage_words);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.words, a.words_cap * 4u);
+    for (uint32_t i = 0; i < nst; i += 256u)
+      lds_dma16(rs, reinterpret_cast<uint8_t*>(stage + i), (wb + i) * 4u + (uint32_t)lane * 16u);
+  }
+  build_dec_lut(a, lut, reinterpret_cast<uint16_t*>(img), lane);
+  // Zero the image: verbatim and padding rows stay zero in the index layout.
+  for (int i = lane * 4; i < nbu * kImgBlk; i += 256) *reinterpret_cast<u32x4*>(img + i) = u32x4{0, 0, 0, 0};
+  __syncthreads();
+
+  // Decode: lane -> (block in unit, chunk in block).
+  const int bl = lane / a.cpb, j = lane % a.cpb;
+  const uint32_t bf = __shfl(f, bl < 64 ? bl : 0, 64);
+  const uint32_t bpre = __shfl(ch_pre, bl < 64 ? bl : 0, 64);
+  uint32_t cm = realmask & ~bf;                                 // coded rows of the block
+  const int ncoded = __popc(cm);
+  bool bad = false;
+  if (bl < nbu && j * a.spc < ncoded) {
+    for (int s = 0; s < j * a.spc; ++s) cm &= cm - 1u;          // skip earlier chunks' rows
+    int r = __ffs(cm) - 1;
+    uint32_t rem = (uint32_t)min(a.spc, ncoded - j * a.spc) * 64u;
+    const uint32_t c = c_first + bpre + (uint32_t)j;
+    const uint32_t p0 = a.off[c] - wb * 32u, p1 = a.off[c + 1] - wb * 32u;
+    uint32_t wi = p0 >> 5;
+    auto word = [&](uint32_t i) -> uint32_t { return i < nst ? stage[i] : 0u; };
+    uint64_t buf = (((uint64_t)word(wi) << 32) | word(wi + 1)) << (p0 & 31u);
+    int avail = 64 - (int)(p0 & 31u);
+    wi += 2;
+    uint64_t acc = 0;
+    uint32_t accn = 0, sw = 0;
+    const uint32_t blk_img = (uint32_t)(bl * kImgBlk);
+    uint32_t* dummy = blk_f + 128 + lane;
+    const uint32_t wlast = nst ? nst - 1 : 0;
+    while (rem) {
+      const uint32_t hi = (uint32_t)(buf >> 32);
+      uint32_t e = lut[hi >> (32 - kDecWin)];
+      const uint32_t v = stage[min(wi, wlast)];                 // refill candidate
+      if ((e & 7u) == 0u) e = lut[kDecLut + ((e >> 16) << 3) + ((hi >> (32 - 13)) & 7u)];
+      const uint32_t nf = e & 7u;
+      const bool all = nf != 0 && nf <= rem;
+      bad |= nf == 0;
+      const uint32_t n = all ? nf : 1u;
+      const uint32_t L = all ? (e >> 7) & 15u : (e >> 3) & 15u;
+      const uint32_t syms = all ? e >> 16 : (e >> 16) & 15u;
+      acc |= (uint64_t)syms << (4 * accn);
+      accn += n;
+      rem -= n;
+      buf <<= L;
+      avail -= (int)L;
+      const bool need = avail < 32;
+      buf |= need ? (uint64_t)v << (32 - avail) : 0ull;
+      avail += need ? 32 : 0;
+      wi += need ? 1u : 0u;
+      // 8 indices ready: store the index word (sub-tile sw / 2, half sw % 2 of row r).
+      const bool flush = accn >= 8;
+      const uint32_t word_i = blk_img + (uint32_t)r * 2u + (sw >> 1) * 32u + (sw & 1u);
+      *(flush ? img + word_i : dummy) = nibbles_to_index_word((uint32_t)acc);
+      acc = flush ? acc >> 32 : acc;
+      accn -= flush ? 8u : 0u;
+      sw += flush ? 1u : 0u;
+      const bool adv = sw == 8u;
+      cm = adv ? cm & (cm - 1u) : cm;
+      sw = adv ? 0u : sw;
+      r = cm ? __ffs(cm) - 1 : 0;
+    }
+    const uint32_t pos = wi * 32u - (uint32_t)avail;          // bits consumed from the slice start
+    if (pos != p1) bad = true;
+  }
+  if (bad) atomicOr(a.err, 1u);
+  __syncthreads();
+
+  // Write the unit's output with whole-line stores.
+  if constexpr (MODE == DEC_IDX) {
+    u32x4* dst = reinterpret_cast<u32x4*>(a.out + ((size_t)t * a.kb + bA) * 512);
+    for (int i = lane; i < nbu * 32; i += 64)
+      dst[i] = *reinterpret_cast<const u32x4*>(img + (i >> 5) * kImgBlk + (i & 31) * 4);
+  } else if constexpr (MODE == DEC_EXP) {
+    // 16-byte piece p: block p / 64, sub-tile (p / 16) % 4, row p % 16.
+    u32x4* dst = reinterpret_cast<u32x4*>(a.out + ((size_t)t * a.kb + bA) * 1024);
+    for (int p = lane; p < nbu * 64; p += 64) {
+      const int b = p >> 6, g = (p >> 4) & 3, r = p & 15;
+      const uint32_t fb = blk_f[b];
+      u32x4 o = {0, 0, 0, 0};
+      if ((fb >> r) & 1u) {
+        const uint32_t v = blk_v[b] + __popc(fb & ((1u << r) - 1u));
+        o = *reinterpret_cast<const u32x4*>(a.vexp + (size_t)v * 64 + g * 16);
+      } else if (r < rows) {
+        const u32x2 iw = *reinterpret_cast<const u32x2*>(img + b * kImgBlk + (g * 16 + r) * 2);
+        const u32x2 lo = index_word_to_exps(iw.x, a.tab), hi = index_word_to_exps(iw.y, a.tab);
+        o = u32x4{lo.x, lo.y, hi.x, hi.y};
       }
+      dst[p] = o;
+    }
+  } else {
+    // BF16 rows: 16-byte piece p = 8 weights; row p / (nbu*8), then block, sub-tile, half.
+    const int per_row = nbu * 8;
+    for (int p = lane; p < rows * per_row; p += 64) {
+      const int r = p / per_row, q = p - r * per_row;
+      const int b = q >> 3, g = (q >> 1) & 3, h = q & 1;
+      const uint32_t fb = blk_f[b];
+      u32x2 e;
+      if ((fb >> r) & 1u) {
+        const uint32_t v = blk_v[b] + __popc(fb & ((1u << r) - 1u));
+        e = *reinterpret_cast<const u32x2*>(a.vexp + (size_t)v * 64 + g * 16 + h * 8);
+      } else {
+        e = index_word_to_exps(img[b * kImgBlk + (g * 16 + r) * 2 + h], a.tab);
+      }
+      const size_t sub = ((size_t)t * a.kb * 4 + (size_t)(bA + b) * 4 + g) * 16 + r;
+      const u32x2 s = *reinterpret_cast<const u32x2*>(a.sm + sub * 16 + h * 8);
+      u32x4 o;
+      o.x = bf16_pairs_from(s.x, e.x, 0);
+      o.y = bf16_pairs_from(s.x, e.x, 1);
+      o.z = bf16_pairs_from(s.y, e.y, 0);
+      o.w = bf16_pairs_from(s.y, e.y, 1);
+      *reinterpret_cast<u32x4*>(a.out + ((size_t)(t * 16 + r) * a.k + (size_t)(bA + b) * 64 + g * 16 + h * 8) * 2) = o;
     }
   }
 }
@@ -839,6 +923,7 @@ static uw_status run_decode(const uw_dmat* d, int mode, uint8_t* out, void* ws, 
   if (!out) return fail(UW_E_ARG, "null output");
   if (!ws || ws_bytes < (size_t)kErrBytes) return fail(UW_E_WORKSPACE, "decode needs a %d-byte workspace", kErrBytes);
   DecArgs a;
+  std::memset(&a, 0, sizeof(a));
   a.words = d->words;
   a.off = d->off;
   a.cbase = d->cbase;
@@ -852,16 +937,43 @@ static uw_status run_decode(const uw_dmat* d, int mode, uint8_t* out, void* ws, 
   a.n = (int32_t)d->info.n;
   a.k = (int32_t)d->info.k;
   a.kb = (int32_t)d->info.kb;
-  a.chunk = d->info.chunk;
-  std::memset(a.pal, 0, 16);
-  std::memcpy(a.pal, d->info.palette, 16);
+  a.spc = d->dec_spc;
+  a.cpb = d->dec_cpb;
+  a.nb = d->dec_nb;
+  a.stage_words = d->dec_stage_words;
+  std::memcpy(a.tab, d->info.palette, 16);
   std::memcpy(a.len, d->info.code_len, 16);
   std::memcpy(a.code, d->info.code, 32);
-  const dim3 grid((unsigned)d->info.tiles, (unsigned)std::max(1, (d->max_tile_chunks + 63) / 64));
+  // Codes longer than the lookup window: their 10-bit prefixes (consecutive in a canonical
+  // code) each get a block of 8 secondary entries indexed by the next 3 bits.
+  const uint32_t invalid = (1u << 3) | (1u << 7);               // n = 0, length 1
+  for (int i = 0; i < kDecSec; ++i) a.sec[i] = invalid;
+  a.pbase = kDecLut;
+  for (int sym = 0; sym < 16; ++sym) {
+    const int L = d->info.code_len[sym];
+    if (L > kDecWin) a.pbase = std::min<uint32_t>(a.pbase, (uint32_t)d->info.code[sym] >> (L - kDecWin));
+  }
+  for (int sym = 0; sym < 16; ++sym) {
+    const int L = d->info.code_len[sym];
+    if (L <= kDecWin) continue;
+    const uint32_t code = d->info.code[sym], pre = code >> (L - kDecWin), blk = pre - a.pbase;
+    if (blk >= 15) return fail(UW_E_FORMAT, "long codes span too many prefixes");
+    a.pmask |= 1u << blk;
+    const uint32_t low = (code << (13 - L)) & 7u, cnt = 1u << (13 - L);
+    for (uint32_t q = 0; q < cnt; ++q) a.sec[(blk + 1) * 8 + low + q] = 1u | ((uint32_t)L << 3) | ((uint32_t)L << 7) | ((uint32_t)sym << 16);
+  }
+  const DecLds L = dec_lds(a.nb, a.stage_words);
+  int dev = 0, lds_max = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+    return fail(UW_E_HIP, "cannot query the LDS size");
+  if (L.total > (uint32_t)lds_max)
+    return fail(UW_E_SHAPE, "decoder unit needs %u bytes of LDS (device allows %d)", L.total, lds_max);
+  const dim3 grid((unsigned)((d->info.kb + a.nb - 1) / a.nb), (unsigned)d->info.tiles);
   switch (mode) {
-    case DEC_IDX: hipLaunchKernelGGL(k_decode<DEC_IDX>, grid, dim3(64), 0, s, a); break;
-    case DEC_EXP: hipLaunchKernelGGL(k_decode<DEC_EXP>, grid, dim3(64), 0, s, a); break;
-    default: hipLaunchKernelGGL(k_decode<DEC_BF16>, grid, dim3(64), 0, s, a); break;
+    case DEC_IDX: hipLaunchKernelGGL(k_decode<DEC_IDX>, grid, dim3(64), L.total, s, a); break;
+    case DEC_EXP: hipLaunchKernelGGL(k_decode<DEC_EXP>, grid, dim3(64), L.total, s, a); break;
+    default: hipLaunchKernelGGL(k_decode<DEC_BF16>, grid, dim3(64), L.total, s, a); break;
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(UW_E_HIP, "decode launch: %s", hipGetErrorString(e));
@@ -914,14 +1026,36 @@ uw_status uw_dmat_bind(uw_dmat* d, const void* blob_host, size_t bytes, const vo
   const uint64_t avail = (bytes > info.sec_off[SEC_WORDS] ? bytes - info.sec_off[SEC_WORDS] : 0) / 4;
   d->words_cap = (uint32_t)std::min<uint64_t>(avail, 0xFFFFFFFFull);
   d->idx = reinterpret_cast<uint8_t*>(idx_dev);
-  const uint32_t* cb = reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(blob_host) + info.sec_off[SEC_CBASE]);
-  int32_t mx = 0;
-  for (int64_t t = 0; t < info.tiles; ++t) mx = std::max<int32_t>(mx, (int32_t)(cb[t + 1] - cb[t]));
-  d->max_tile_chunks = mx;
-  const uint32_t* vp = reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(blob_host) + info.sec_off[SEC_VPREFIX]);
+  const uint8_t* hb = reinterpret_cast<const uint8_t*>(blob_host);
+  const uint32_t* cb = reinterpret_cast<const uint32_t*>(hb + info.sec_off[SEC_CBASE]);
+  const uint32_t* vp = reinterpret_cast<const uint32_t*>(hb + info.sec_off[SEC_VPREFIX]);
+  const uint32_t* of = reinterpret_cast<const uint32_t*>(hb + info.sec_off[SEC_OFF]);
+  const uint16_t* fl = reinterpret_cast<const uint16_t*>(hb + info.sec_off[SEC_FLAGS]);
   int32_t mv = 0;
   for (int64_t t = 0; t < info.tiles; ++t) mv = std::max<int32_t>(mv, (int32_t)(vp[t + 1] - vp[t]));
   d->max_tile_verb = mv;
+  // Decoder units: whole blocks whose chunks fill at most one wave, and the largest
+  // bitstream slice any unit stages.
+  d->dec_spc = info.chunk / kSeg;
+  d->dec_cpb = (kTileRows + d->dec_spc - 1) / d->dec_spc;
+  d->dec_nb = 64 / d->dec_cpb;
+  uint32_t stage = 256;
+  for (int64_t t = 0; t < info.tiles; ++t) {
+    const int rows = (int)std::min<int64_t>(kTileRows, info.n - t * kTileRows);
+    const uint32_t realmask = rows == kTileRows ? 0xFFFFu : ((1u << rows) - 1u);
+    uint32_t c = cb[t];
+    for (int64_t b0 = 0; b0 < info.kb; b0 += d->dec_nb) {
+      uint32_t nch = 0;
+      for (int64_t b = b0; b < std::min<int64_t>(b0 + d->dec_nb, info.kb); ++b)
+        nch += ((uint32_t)__builtin_popcount(realmask & ~(uint32_t)fl[t * info.kb + b]) + d->dec_spc - 1) / d->dec_spc;
+      if (nch) {
+        const uint32_t wb = (of[c] >> 5) & ~3u, we = (of[c + nch] >> 5) + 3u;
+        stage = std::max(stage, (we - wb + 255u) & ~255u);
+      }
+      c += nch;
+    }
+  }
+  d->dec_stage_words = stage;
   d->magic = kDmatMagic;
   clear_error();
   return UW_OK;

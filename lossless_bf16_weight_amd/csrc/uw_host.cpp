@@ -245,6 +245,22 @@ struct BitWriter {
   }
 };
 
+static int tile_rows(int64_t n, int64_t t) { return (int)std::min<int64_t>(kTileRows, n - t * kTileRows); }
+
+// Non-verbatim real rows of one (tile, block).
+static int block_coded_rows(uint32_t flags, int rows) {
+  const uint32_t realmask = rows == kTileRows ? 0xFFFFu : ((1u << rows) - 1u);
+  return __builtin_popcount(realmask & ~flags);
+}
+
+// Chunks of one tile: chunks restart at every 64-column block, so block b holds
+// ceil(64 * coded rows of b / chunk) of them.
+static uint32_t tile_chunks(const uint16_t* flags, int64_t kb, int rows, int chunk) {
+  uint64_t c = 0;
+  for (int64_t b = 0; b < kb; ++b) c += ((uint64_t)block_coded_rows(flags[b], rows) * kSeg + chunk - 1) / chunk;
+  return (uint32_t)c;
+}
+
 static uw_status encode_impl(const uint16_t* w, int64_t n, int64_t k, int32_t chunk, uint8_t* blob, size_t cap,
                              size_t* used) {
   uw_status st = check_shape(n, k);
@@ -318,7 +334,7 @@ static uw_status encode_impl(const uint16_t* w, int64_t n, int64_t k, int32_t ch
     vprefix[t + 1] = vprefix[t] + tile_verb[t];
     tile_bit0[t + 1] = tile_bit0[t] + bits;
     tile_sym0[t + 1] = tile_sym0[t] + syms;
-    cbase[t + 1] = cbase[t] + (uint32_t)((syms + chunk - 1) / chunk);
+    cbase[t + 1] = cbase[t] + tile_chunks(flags.data() + t * L.kb, L.kb, tile_rows(n, t), chunk);
   }
   const uint64_t total_bits = tile_bit0[L.T];
   const uint64_t n_coded = tile_sym0[L.T];
@@ -380,10 +396,10 @@ static uw_status encode_impl(const uint16_t* w, int64_t n, int64_t k, int32_t ch
         }
       }
       uint64_t vrank = vprefix[t];
-      uint64_t sym = 0;                 // coded symbols emitted in this tile
       uint64_t chunk_id = cbase[t];
       for (int64_t b = 0; b < L.kb; ++b) {
         const uint16_t f = flags[(size_t)(t * L.kb + b)];
+        uint64_t sym = 0;               // coded symbols emitted in this block (chunks restart here)
         for (int r = 0; r < rows; ++r) {
           const uint16_t* sg = w + (size_t)(t * kTileRows + r) * k + b * kSeg;
           if ((f >> r) & 1) {
@@ -478,7 +494,9 @@ uw_status validate_blob(const void* blob, size_t bytes, uw_info* info) {
     }
     if ((uint64_t)vprefix[t + 1] != vprefix[t] + nv) return fail(UW_E_FORMAT, "vprefix inconsistent with flags");
     const uint64_t nsy = ((uint64_t)rows * kb - nv) * kSeg;
-    if ((uint64_t)cbase[t + 1] != cbase[t] + (nsy + h->chunk - 1) / h->chunk) return fail(UW_E_FORMAT, "cbase inconsistent");
+    if ((uint64_t)cbase[t + 1] < cbase[t] ||
+        (uint64_t)cbase[t + 1] - cbase[t] != tile_chunks(flags + t * kb, kb, rows, (int)h->chunk))
+      return fail(UW_E_FORMAT, "cbase inconsistent");
     coded_total += nsy;
   }
   if (vprefix[T] != h->n_verb) return fail(UW_E_FORMAT, "verbatim count mismatch");
@@ -493,13 +511,16 @@ uw_status validate_blob(const void* blob, size_t bytes, uw_info* info) {
   if (off[h->n_chunks] != h->total_bits) return fail(UW_E_FORMAT, "last offset != total bits");
   // Every chunk spans between minlen and maxlen bits per symbol: bounds every decoder read.
   for (int64_t t = 0; t < T; ++t) {
-    const int rows = (int)std::min<int64_t>(kTileRows, n - t * kTileRows);
-    const uint64_t nsy = ((uint64_t)rows * kb - (vprefix[t + 1] - vprefix[t])) * kSeg;
-    for (uint32_t c = cbase[t]; c < cbase[t + 1]; ++c) {
-      const uint64_t cnt = std::min<uint64_t>(h->chunk, nsy - (uint64_t)(c - cbase[t]) * h->chunk);
-      const uint64_t span = (uint64_t)off[c + 1] - off[c];
-      if (off[c + 1] < off[c] || span < cnt * minlen || span > cnt * maxlen)
-        return fail(UW_E_FORMAT, "chunk %u offsets inconsistent", c);
+    const int rows = tile_rows(n, t);
+    uint32_t c = cbase[t];
+    for (int64_t b = 0; b < kb; ++b) {
+      const uint64_t nsy = (uint64_t)block_coded_rows(flags[t * kb + b], rows) * kSeg;
+      for (uint64_t s0 = 0; s0 < nsy; s0 += h->chunk, ++c) {
+        const uint64_t cnt = std::min<uint64_t>(h->chunk, nsy - s0);
+        const uint64_t span = (uint64_t)off[c + 1] - off[c];
+        if (off[c + 1] < off[c] || span < cnt * minlen || span > cnt * maxlen)
+          return fail(UW_E_FORMAT, "chunk %u offsets inconsistent", c);
+      }
     }
   }
   if (h->n_chunks && off[0] != 0) return fail(UW_E_FORMAT, "first chunk must start at bit 0");
@@ -593,7 +614,7 @@ uw_status uw_encode_bound(int64_t n, int64_t k, int32_t chunk, size_t* bytes) {
   L.T = L.np / kTileRows;
   L.kb = k / kSeg;
   const uint64_t nk = (uint64_t)n * k;
-  const uint64_t chunks = (uint64_t)L.T * ((kTileRows * (uint64_t)k + chunk - 1) / chunk);
+  const uint64_t chunks = (uint64_t)L.T * L.kb * ((kTileRows * kSeg + chunk - 1) / chunk);
   const uint64_t nverb = (uint64_t)n * L.kb;
   layout_sections(L, nverb, chunks, (nk * kLmax + 31) / 32 + 2);
   *bytes = L.total;

@@ -32,10 +32,12 @@ Readings taken where the post is silent or garbled (each is repeated where it is
       entry table, the post's "up to 16 KB" LUT at 2 bytes an entry), built by
       package-merge with fixed tie rules, then made canonical.
   R6  Bits are written MSB-first into 32-bit little-endian words.
-  R7  The stream is cut into chunks of S coded symbols (S a multiple of 64) so chunks can
-      be decoded in parallel; chunks restart at every 16-row tile so a decoder can place
-      outputs from the tile's verbatim flags alone (per-chunk start bit offsets "off",
-      per-tile first chunk "cbase").
+  R7  The stream is cut into chunks of at most S coded symbols (S a multiple of 64) so
+      chunks can be decoded in parallel (per-chunk start bit offsets "off"); chunks restart
+      at every 64-column block of every 16-row tile, so a chunk's output never leaves one
+      block and a decoder places it from that block's verbatim flags alone (per-tile first
+      chunk "cbase"; inside a tile, block b holds ceil(64 * coded segments of b / S)
+      chunks).
   R8  Layout: weights are grouped in tiles of 16 rows; inside a tile the sign+mantissa,
       exponent and index streams are stored as 16x16 sub-tiles (row-major inside the
       sub-tile) ordered by K; segments are enumerated in (tile, 64-column block, row) order.
@@ -303,19 +305,24 @@ def analyse(w, n, k):
     freqs = np.bincount(symbols, minlength=PALETTE_SIZE)[:PALETTE_SIZE] if len(symbols) else np.zeros(16, np.int64)
     return dict(n=n, k=k, e=e, sm=sm, hist=hist, palette=palette, index_of=index_of, verb=verb,
                 flags=flags, vprefix=vprefix, vexp=vexp, coded=coded, symbols=symbols, freqs=freqs,
-                coded_per_tile=coded.reshape(T, -1).sum(axis=1))
+                coded_per_block=coded.sum(axis=2))
 
 
-def chunk_starts(coded_per_tile, chunk):
-    """Symbol index of every chunk start (chunks restart at each tile, R7) and the first
-    chunk of each tile (cbase, T+1 entries)."""
+def chunk_starts(coded_per_block, chunk):
+    """Symbol index of every chunk start and the first chunk of each tile (cbase, T+1
+    entries).  coded_per_block [T, KB]: coded segments of each (tile, block).  Chunks
+    restart at every block of every tile (R7): block (t, b) with c coded segments holds
+    ceil(64 c / S) chunks, all of S symbols but the last."""
     starts, cbase, base = [], [0], 0
-    for segs in coded_per_tile:
-        nsym = int(segs) * SEG
-        nch = -(-nsym // chunk)
-        starts.extend(base + c * chunk for c in range(nch))
-        cbase.append(cbase[-1] + nch)
-        base += nsym
+    for tile in coded_per_block:
+        nch_tile = 0
+        for segs in tile:
+            nsym = int(segs) * SEG
+            nch = -(-nsym // chunk)
+            starts.extend(base + c * chunk for c in range(nch))
+            nch_tile += nch
+            base += nsym
+        cbase.append(cbase[-1] + nch_tile)
     return np.array(starts, dtype=np.int64), np.array(cbase, dtype=np.uint32)
 
 
@@ -329,7 +336,7 @@ def encode(w, n, k, chunk=DEFAULT_CHUNK, lmax=LMAX):
     words, sym_start, total = pack_bitstream(a["symbols"], lengths, codes)
     if total >= 1 << 32:
         raise ValueError("stream longer than 2**32 bits")
-    cstart, cbase = chunk_starts(a["coded_per_tile"], chunk)
+    cstart, cbase = chunk_starts(a["coded_per_block"], chunk)
     off = np.concatenate([sym_start[cstart], [total]]).astype(np.uint32) if len(cstart) else np.array([total], np.uint32)
     n_pad = padded_rows(n)
     sm_t = tile_bytes(pad_rows(a["sm"], n_pad))
@@ -480,17 +487,14 @@ def decode_chunks(words, off, chunk_len, lengths):
 
 
 def chunk_lengths(d):
-    """Symbols per chunk, from the per-tile chunk table and the tile's coded segments."""
-    n_pad = padded_rows(d["n"])
-    T = n_pad // TILE_ROWS
-    kb = d["k"] // SEG
+    """Symbols per chunk, in chunk order, from the verbatim flags (R7: chunks of S symbols
+    restarting at every block of every tile; a block's last chunk holds the rest)."""
+    coded, _, _ = _coded_and_verbatim_masks(d)
     lens = []
-    for t in range(T):
-        rows = min(TILE_ROWS, d["n"] - TILE_ROWS * t)
-        nsym = (rows * kb - int(d["vprefix"][t + 1] - d["vprefix"][t])) * SEG
-        nch = int(d["cbase"][t + 1] - d["cbase"][t])
-        for c in range(nch):
-            lens.append(min(d["chunk"], nsym - c * d["chunk"]))
+    for tile in coded.sum(axis=2):
+        for segs in tile:
+            nsym = int(segs) * SEG
+            lens.extend(min(d["chunk"], nsym - c) for c in range(0, nsym, d["chunk"]))
     return np.array(lens, dtype=np.int64)
 
 
@@ -514,6 +518,10 @@ def decode_symbols(d):
     lens = chunk_lengths(d)
     if len(lens) and int(lens.sum()) != d["n_coded"]:
         raise ValueError("chunk table inconsistent with coded symbol count")
+    coded, _, _ = _coded_and_verbatim_masks(d)
+    per_tile = [sum(-(-int(c) * SEG // d["chunk"]) for c in tile) for tile in coded.sum(axis=2)]
+    if len(lens) != d["n_chunks"] or not np.array_equal(np.diff(d["cbase"].astype(np.int64)), per_tile):
+        raise ValueError("chunk table inconsistent with the verbatim flags")
     return decode_chunks(d["words"], d["off"], lens, d["lengths"])
 
 

@@ -248,6 +248,54 @@ def test_lockstep_chunk_decode_equals_sequential():
         codec.decode_chunks(words, bad, lens, L)
 
 
+@pytest.mark.parametrize("chunk", [64, 192, 512, 1024, 4096])
+def test_chunks_restart_at_every_block(chunk):
+    """Brute force over a matrix with verbatim rows, several blocks, two tiles and a ragged
+    tail: chunk c, decoded bit by bit from off[c], must give exactly the next (at most S)
+    coded symbols of one (tile, block) -- that block's non-verbatim rows in row order --
+    and end where off[c+1] starts; every block holds ceil(64 * coded rows / S) chunks."""
+    w = synth.small_gaussian(29, 256, seed=12, plant_frac=0.2)["w"]
+    n, k = w.shape
+    enc = codec.encode(w, n, k, chunk=chunk)
+    pal = [int(p) for p in enc["palette"]]
+    table = {(int(L), int(c)): sym for sym, (L, c) in enumerate(zip(enc["lengths"], enc["codes"])) if L}
+    words = [int(x) for x in enc["words"]]
+    e = (w >> 7) & 0xFF
+
+    def bit(pos):
+        return (words[pos >> 5] >> (31 - (pos & 31))) & 1
+
+    c = 0
+    for t in range(2):
+        for b in range(k // 64):
+            expected = []
+            for r in range(16):
+                row = 16 * t + r
+                if row >= n:
+                    continue
+                seg = [int(v) for v in e[row, 64 * b: 64 * b + 64]]
+                if all(v in pal for v in seg):
+                    expected += [pal.index(v) for v in seg]
+            assert len(expected) % 64 == 0
+            nch = -(-len(expected) // chunk)
+            for j in range(nch):
+                want = expected[j * chunk:(j + 1) * chunk]
+                pos = int(enc["off"][c])
+                got = []
+                for _ in want:
+                    code, L = 0, 0
+                    while (L, code) not in table:
+                        code, L = (code << 1) | bit(pos), L + 1
+                        pos += 1
+                    got.append(table[(L, code)])
+                assert got == want, (t, b, j)
+                assert pos == int(enc["off"][c + 1])
+                c += 1
+        assert int(enc["cbase"][t + 1]) == c
+    assert c == len(enc["off"]) - 1
+    assert 0 < enc["n_verb"]
+
+
 # ------------------------------------------------------------------ hand-worked tile
 def _read_golden(name):
     out = {}
