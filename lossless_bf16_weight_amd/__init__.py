@@ -298,10 +298,13 @@ class CompressedMatrix:
         self.info = self.d.info
         self.n, self.k = int(info["n"]), int(info["k"])
         self.err = torch.zeros(64, dtype=torch.int32, device=device)
+        self._ws = {}
         if keep_index:
             uw_transcode_palette(self.d, self.idx, self.err)
 
     def workspace(self, m, pipeline):
+        """A zeroed workspace of uw_workspace_size bytes (error word, decoded operand of
+        pipelines 1-3, K-slice partial sums of the multi-tile kernel)."""
         import torch
         size = uw_workspace_size(self.d, m, pipeline)
         return torch.zeros(max(size, 256), dtype=torch.uint8, device=self.blob_dev.device) if size else None
@@ -311,8 +314,11 @@ class CompressedMatrix:
         m = x.shape[0]
         if y is None:
             y = torch.empty((m, self.n), dtype=torch.float32, device=x.device)
-        if ws is None and pipeline not in (UW_PIPE_DIRECT_PALETTE,):
-            ws = self.workspace(m, pipeline)
+        if ws is None:
+            key = (m, pipeline)
+            if key not in self._ws:
+                self._ws[key] = self.workspace(m, pipeline)
+            ws = self._ws[key]
         uw_gemm_variant(self.d, x, y, m, pipeline, variant, ws, stream)
         return y
 

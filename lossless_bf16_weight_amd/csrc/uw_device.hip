@@ -483,6 +483,250 @@ __global__ __launch_bounds__((MaxThreads<CT, U>::v)) void k_gemm(GemmArgs a) {
 }
 
 // =========================================================================================
+// Reconstructive GEMM for wider batches (multi-tile kernel).
+//
+// At M > 16 the per-tile kernel above re-reads the X columns for every 16-row tile, so X
+// traffic from L2 grows with M x (n / 16) and dominates.  Here one workgroup of R waves
+// holds R row tiles (one per wave) and a K-slice of the blocks; X is staged once per
+// workgroup in LDS, in batches of U blocks (double-buffered LDS-DMA, no VGPRs), and every
+// wave multiplies its rebuilt tile against it.  The K-slices of a row group (grid.y) write
+// partial sums to the workspace when there are several, and a reduction kernel adds them
+// in slice order (deterministic).
+// LDS X batch: row m of 16*CT, U*8 granules of 16 bytes (8 bf16), granule q stored at
+// position q ^ (m & 15 & (U*8-1)) of its row, so the 16 rows a B-operand load touches fall
+// in distinct bank groups.
+// =========================================================================================
+template <int CT, int U>
+struct MtCfg {
+  static constexpr int kGpr = U * 8;                      // granules per X row of a batch
+  static constexpr int kSwz = (kGpr - 1) < 15 ? (kGpr - 1) : 15;
+  static constexpr int kRows = 16 * CT;
+  static constexpr int kBufBytes = kRows * kGpr * 16;     // one X batch
+  static constexpr int kDmas = kRows * kGpr / 64;         // 1 KB LDS-DMA instructions per batch
+};
+
+// Rebuild the lane's 16 weights of one block as two bf16x8 MFMA operands.
+template <int SRC>
+__device__ __forceinline__ void rebuild_block(const GemmArgs& a, const WRegs<SRC>& w, uint32_t f, int r,
+                                              const u32x4& ev, u32x4& A0, u32x4& A1) {
+  if constexpr (SRC == SRC_BF16) {
+    A0 = w.w0;
+    A1 = w.w1;
+  } else {
+    uint32_t T0[4], T1[4];
+    if constexpr (SRC == SRC_PAL_AFFINE) {
+      exps_affine(w.i.x, a.base2, a.m0, a.m1, T0);
+      exps_affine(w.i.y, a.base2, a.m0, a.m1, T1);
+    } else if constexpr (SRC == SRC_PAL_LUT) {
+      exps_lut(w.i.x, a.tab, T0);
+      exps_lut(w.i.y, a.tab, T1);
+    } else {
+      exps_raw(w.e.x, w.e.y, T0);
+      exps_raw(w.e.z, w.e.w, T1);
+    }
+    if constexpr (SRC <= SRC_PAL_LUT) {
+      if (f) {  // uniform: some row of this tile has a verbatim segment in this block
+        uint32_t R0[4], R1[4];
+        exps_raw(ev.x, ev.y, R0);
+        exps_raw(ev.z, ev.w, R1);
+        const uint32_t keep = ((f >> r) & 1u) ? 0u : ~0u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          T0[j] = (T0[j] & keep) | (R0[j] & ~keep);
+          T1[j] = (T1[j] & keep) | (R1[j] & ~keep);
+        }
+      }
+    }
+    uint32_t P0[4], P1[4];
+    spread_sm(w.s.x, w.s.y, P0);
+    spread_sm(w.s.z, w.s.w, P1);
+    A0 = u32x4{(P0[0] & 0x807F807Fu) | T0[0], (P0[1] & 0x807F807Fu) | T0[1], (P0[2] & 0x807F807Fu) | T0[2],
+               (P0[3] & 0x807F807Fu) | T0[3]};
+    A1 = u32x4{(P1[0] & 0x807F807Fu) | T1[0], (P1[1] & 0x807F807Fu) | T1[1], (P1[2] & 0x807F807Fu) | T1[2],
+               (P1[3] & 0x807F807Fu) | T1[3]};
+  }
+}
+
+template <int SRC>
+struct MtSlot {
+  WRegs<SRC> w;
+  u32x4 ev;
+};
+
+// part: S partial [m, n] fp32 planes (S > 1), or null to write y directly.
+template <int SRC, int CT, int U, int R>
+__global__ __launch_bounds__(64 * R) void k_gemm_mt(GemmArgs a, float* part, int S) {
+  using C = MtCfg<CT, U>;
+  static_assert(C::kDmas % R == 0, "every wave issues the same number of X DMAs");
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  constexpr bool kPal = SRC <= SRC_PAL_LUT;
+  constexpr int kRowsPerDma = 64 / C::kGpr;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const int tiles = (a.n + 15) >> 4;
+  const int t = blockIdx.x * R + wave;
+  const bool tile_ok = t < tiles;
+  const int s = blockIdx.y;
+  const int bs = (int)((int64_t)s * a.kb / S), be = (int)((int64_t)(s + 1) * a.kb / S);
+  const int nbatch = (be - bs + U - 1) / U;
+  const int mcol0 = blockIdx.z * 16 * CT;
+  const int mv = min(16 * CT, a.m - mcol0);
+
+  // X batches: DMA j of a batch fills rows j*kRowsPerDma .. with granules permuted by row.
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.x + (size_t)mcol0 * a.k, (uint32_t)mv * a.k * 2);
+  auto issue_x = [&](int batch, uint8_t* buf) {
+    const int bb = bs + batch * U;
+#pragma unroll
+    for (int jj = 0; jj < C::kDmas / R; ++jj) {
+      const int j = wave + jj * R;
+      const int m = j * kRowsPerDma + lane / C::kGpr;
+      const int q = (lane % C::kGpr) ^ (m & C::kSwz);
+      const int blk = bb + (q >> 3);
+      const uint32_t voff = (m < mv && blk < be) ? (uint32_t)(m * a.k + blk * 64 + (q & 7) * 8) * 2 : kOob;
+      lds_dma16(xrs, buf + j * 1024, voff);
+    }
+  };
+
+  // Weight streams of this wave's tile (bounds-checked; a missing tile reads zeros).
+  const size_t tile_bytes = (size_t)t * a.k * 16;
+  __amdgpu_buffer_rsrc_t wrs0, wrs1;
+  uint32_t woff0 = kOob, woff1 = kOob;
+  if constexpr (SRC == SRC_BF16) {
+    const int rows = tile_ok ? min(16, a.n - t * 16) : 0;
+    wrs0 = make_rsrc(a.aux + (tile_ok ? tile_bytes * 2 : 0), (uint32_t)rows * a.k * 2);
+    wrs1 = wrs0;
+    if (tile_ok && t * 16 + r < a.n) woff0 = (uint32_t)(r * a.k + g * 16) * 2;
+  } else {
+    wrs0 = make_rsrc(a.sm + (tile_ok ? tile_bytes : 0), tile_ok ? (uint32_t)a.k * 16 : 0u);
+    if (tile_ok) woff0 = lane * 16;
+    if constexpr (SRC == SRC_EXP) {
+      wrs1 = make_rsrc(a.aux + (tile_ok ? tile_bytes : 0), tile_ok ? (uint32_t)a.k * 16 : 0u);
+      if (tile_ok) woff1 = lane * 16;
+    } else {
+      wrs1 = make_rsrc(a.aux + (tile_ok ? tile_bytes / 2 : 0), tile_ok ? (uint32_t)a.k * 8 : 0u);
+      if (tile_ok) woff1 = lane * 8;
+    }
+  }
+
+  // Verbatim bookkeeping of this slice: flags of block bs + j in lane j, and the tile-relative
+  // rank of its first verbatim segment.
+  uint32_t wfl = 0, wvp = 0;
+  __amdgpu_buffer_rsrc_t vrs = make_rsrc(a.vexp, 0);
+  if constexpr (kPal) {
+    if (tile_ok) {
+      const uint16_t* fl = a.flags + (size_t)t * a.kb;
+      uint32_t before = 0;
+      for (int j = lane; j < bs; j += 64) before += (uint32_t)__popc((uint32_t)fl[j]);
+      before = wave_sum(before);
+      wfl = lane < be - bs ? (uint32_t)fl[bs + lane] : 0u;
+      const uint32_t v = (uint32_t)__popc(wfl);
+      wvp = before + wave_incl_scan(v, lane) - v;
+      const uint32_t v0 = a.vprefix[t];
+      vrs = make_rsrc(a.vexp + (size_t)v0 * 64, (a.vprefix[t + 1] - v0) * 64);
+    }
+  }
+
+  auto load_block = [&](int b, MtSlot<SRC>& sl) {
+    const bool ok = b < be;
+    const uint32_t o0 = ok ? woff0 : kOob;
+    if constexpr (SRC == SRC_BF16) {
+      sl.w.w0 = bload16_nt(wrs0, o0, b * 128);
+      sl.w.w1 = bload16_nt(wrs0, o0 == kOob ? kOob : o0 + 16, b * 128);
+    } else if constexpr (SRC == SRC_EXP) {
+      sl.w.s = bload16_nt(wrs0, o0, b * 1024);
+      sl.w.e = bload16_nt(wrs1, ok ? woff1 : kOob, b * 1024);
+    } else {
+      sl.w.s = bload16_nt(wrs0, o0, b * 1024);
+      sl.w.i = bload8_nt(wrs1, ok ? woff1 : kOob, b * 512);
+      const int jb = ok ? b - bs : 0;
+      const uint32_t f = __builtin_amdgcn_readlane(wfl, jb);
+      const uint32_t rank = __builtin_amdgcn_readlane(wvp, jb) + (uint32_t)__popc(f & ((1u << r) - 1u));
+      sl.ev = bload16(vrs, (ok && ((f >> r) & 1u)) ? rank * 64 + g * 16 : kOob);
+    }
+  };
+
+  constexpr bool kTwo = CT <= 2;   // a second accumulator set keeps back-to-back MFMAs independent
+  floatx4 acc[CT], acc2[kTwo ? CT : 1];
+#pragma unroll
+  for (int c = 0; c < CT; ++c) acc[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < (kTwo ? CT : 1); ++c) acc2[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const int sw = r & C::kSwz;
+
+  issue_x(0, smem);
+  MtSlot<SRC> sl[U];
+  for (int i = 0; i < nbatch; ++i) {
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's X DMAs for batch i have landed
+    __syncthreads();                 // ... and everyone's; batch i-1's buffer is free again
+    const int b = bs + i * U;
+#pragma unroll
+    for (int u = 0; u < U; ++u) load_block(b + u, sl[u]);
+    if (i + 1 < nbatch) issue_x(i + 1, smem + ((i + 1) & 1) * C::kBufBytes);
+    const uint8_t* xbuf = smem + (i & 1) * C::kBufBytes;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (b + u >= be) break;
+      uint32_t f = 0;
+      if constexpr (kPal) f = __builtin_amdgcn_readlane(wfl, b + u - bs);
+      u32x4 A0, A1;
+      rebuild_block<SRC>(a, sl[u].w, f, r, sl[u].ev, A0, A1);
+      const bf16x8 a0 = __builtin_bit_cast(bf16x8, A0), a1 = __builtin_bit_cast(bf16x8, A1);
+      const int q0 = u * 8 + g * 2;
+#pragma unroll
+      for (int c = 0; c < CT; ++c) {
+        const u32x4 x0 = *reinterpret_cast<const u32x4*>(xbuf + ((16 * c + r) * C::kGpr + (q0 ^ sw)) * 16);
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, __builtin_bit_cast(bf16x8, x0), acc[c], 0, 0, 0);
+      }
+#pragma unroll
+      for (int c = 0; c < CT; ++c) {
+        const u32x4 x1 = *reinterpret_cast<const u32x4*>(xbuf + ((16 * c + r) * C::kGpr + ((q0 + 1) ^ sw)) * 16);
+        if constexpr (kTwo)
+          acc2[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, __builtin_bit_cast(bf16x8, x1), acc2[c], 0, 0, 0);
+        else
+          acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, __builtin_bit_cast(bf16x8, x1), acc[c], 0, 0, 0);
+      }
+    }
+  }
+  if constexpr (kTwo) {
+#pragma unroll
+    for (int c = 0; c < CT; ++c) acc[c] += acc2[c];
+  }
+  if (!tile_ok) return;
+  // D lane layout: column lane % 16 of column tile c, rows 4 * (lane / 16) + j of the tile.
+  float* dst = part ? part + (size_t)s * a.m * a.n : a.y;
+  const int n0 = t * 16 + 4 * g;
+#pragma unroll
+  for (int c = 0; c < CT; ++c) {
+    const int mm = mcol0 + 16 * c + r;
+    if (mm >= a.m) continue;
+    float* yp = dst + (size_t)mm * a.n + n0;
+    if (n0 + 3 < a.n && (a.n & 3) == 0) {
+      *reinterpret_cast<floatx4*>(yp) = acc[c];
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (n0 + j < a.n) yp[j] = acc[c][j];
+    }
+  }
+}
+
+// y[i] = sum over s of part[s][i], in slice order.
+__global__ __launch_bounds__(256) void k_reduce_parts(const float* part, float* y, int S, int64_t count) {
+  const int64_t n4 = count >> 2;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+    floatx4 v = reinterpret_cast<const floatx4*>(part)[i];
+    for (int s = 1; s < S; ++s) v += reinterpret_cast<const floatx4*>(part + (size_t)s * count)[i];
+    reinterpret_cast<floatx4*>(y)[i] = v;
+  }
+  for (int64_t i = (n4 << 2) + (int64_t)blockIdx.x * 256 + threadIdx.x; i < count; i += (int64_t)gridDim.x * 256) {
+    float v = part[i];
+    for (int s = 1; s < S; ++s) v += part[(size_t)s * count + i];
+    y[i] = v;
+  }
+}
+
+// =========================================================================================
 // Huffman decoder.
 //
 // Chunks restart at every 64-column block of every tile, so the work splits into units of
@@ -818,12 +1062,18 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* y, uint16_t* x, in
 // =========================================================================================
 // Host launchers
 // =========================================================================================
+// Kernel variants: kind 0 = per-tile kernel (waves split the tile's blocks; `unroll` blocks
+// a batch), kind 1 = multi-tile kernel (`waves` row tiles a workgroup, X batches of `unroll`
+// blocks in LDS, K split over workgroups).
 struct Variant {
+  int kind;
   int waves;
   int unroll;
 };
-static const Variant kVariants[] = {{4, 8}, {2, 8}, {8, 8}, {16, 8}, {1, 8}, {4, 4}, {2, 4}, {8, 4}, {16, 4}, {1, 4}};
+static const Variant kVariants[] = {{0, 4, 8}, {0, 2, 8}, {0, 8, 8},  {0, 16, 8}, {0, 1, 8}, {0, 4, 4}, {0, 2, 4},
+                                    {0, 8, 4}, {0, 16, 4}, {0, 1, 4}, {1, 8, 4},  {1, 4, 4}, {1, 8, 2}, {1, 4, 2}};
 static constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
+static constexpr int kMtDefault = 10;   // {1, 8, 4}
 
 static int col_tiles(int m) {
   const int ct = (m + 15) / 16;
@@ -837,8 +1087,58 @@ static int default_variant(int64_t tiles, int64_t kb, int ct) {
   int w = 1;
   while (w < cap && tiles * w < 1536 && kb / (w * 2) >= 4) w *= 2;
   for (int v = 0; v < kNumVariants; ++v)
-    if (kVariants[v].waves == w && kVariants[v].unroll == 4) return v;
+    if (kVariants[v].kind == 0 && kVariants[v].waves == w && kVariants[v].unroll == 4) return v;
   return 0;
+}
+
+// Multi-tile kernel: K slices so that about 2048 waves run, each slice at most 64 blocks
+// (one block per lane in the flag registers), at most kb slices.
+static int mt_slices(int64_t tiles, int R, int64_t kb) {
+  const int64_t groups = (tiles + R - 1) / R;
+  int64_t S = (2048 + groups * R - 1) / (groups * R);
+  S = std::max<int64_t>(S, (kb + 63) / 64);
+  S = std::min<int64_t>(std::max<int64_t>(S, 1), std::min<int64_t>(kb, 16));
+  return (int)S;
+}
+static int64_t mt_max_slices(int64_t kb) { return std::max<int64_t>(16, (kb + 63) / 64); }
+
+template <int SRC, int CT, int U, int R>
+static hipError_t launch_mt_t(const GemmArgs& a, int64_t tiles, int S, float* part, hipStream_t s) {
+  using C = MtCfg<CT, U>;
+  const dim3 grid((unsigned)((tiles + R - 1) / R), (unsigned)S, (unsigned)((a.m + 16 * CT - 1) / (16 * CT)));
+  hipLaunchKernelGGL((k_gemm_mt<SRC, CT, U, R>), grid, dim3(64 * R), 2 * C::kBufBytes, s, a, S > 1 ? part : nullptr, S);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || S == 1) return e;
+  const int64_t count = (int64_t)a.m * a.n;
+  const int64_t blocks = std::min<int64_t>((count / 4 + 255) / 256 + 1, 2048);
+  hipLaunchKernelGGL(k_reduce_parts, dim3((unsigned)blocks), dim3(256), 0, s, part, a.y, S, count);
+  return hipGetLastError();
+}
+
+template <int SRC, int CT>
+static hipError_t launch_mt_c(const GemmArgs& a, int64_t tiles, int R, int U, int S, float* part, hipStream_t s) {
+  // Every wave issues the same number of X DMAs (2*CT*U a batch, a multiple of R); 128-row
+  // batches use 2 blocks (64 KB of LDS, double-buffered).
+  if constexpr (CT == 8) {
+    return R == 8 ? launch_mt_t<SRC, 8, 2, 8>(a, tiles, S, part, s) : launch_mt_t<SRC, 8, 2, 4>(a, tiles, S, part, s);
+  } else if constexpr (CT == 1) {
+    return R == 8 ? launch_mt_t<SRC, 1, 4, 8>(a, tiles, S, part, s)
+                  : (U >= 4 ? launch_mt_t<SRC, 1, 4, 4>(a, tiles, S, part, s) : launch_mt_t<SRC, 1, 2, 4>(a, tiles, S, part, s));
+  } else {
+    if (U >= 4)
+      return R == 8 ? launch_mt_t<SRC, CT, 4, 8>(a, tiles, S, part, s) : launch_mt_t<SRC, CT, 4, 4>(a, tiles, S, part, s);
+    return R == 8 ? launch_mt_t<SRC, CT, 2, 8>(a, tiles, S, part, s) : launch_mt_t<SRC, CT, 2, 4>(a, tiles, S, part, s);
+  }
+}
+
+template <int SRC>
+static hipError_t launch_mt(const GemmArgs& a, int64_t tiles, int R, int U, int S, float* part, hipStream_t s) {
+  switch (col_tiles(std::min(a.m, 128))) {
+    case 1: return launch_mt_c<SRC, 1>(a, tiles, R, U, S, part, s);
+    case 2: return launch_mt_c<SRC, 2>(a, tiles, R, U, S, part, s);
+    case 4: return launch_mt_c<SRC, 4>(a, tiles, R, U, S, part, s);
+    default: return launch_mt_c<SRC, 8>(a, tiles, R, U, S, part, s);
+  }
 }
 
 struct Launch {
@@ -885,9 +1185,33 @@ static hipError_t launch_gemm_c(const GemmArgs& a, int ct, const Launch& L, hipS
   }
 }
 
-static uw_status run_gemm(int src, const GemmArgs& a, int64_t tiles, int variant, int max_tile_verb, hipStream_t s) {
+// part / part_bytes: workspace for the multi-tile kernel's K-slice partial sums (may be
+// null: then it runs one slice, or the per-tile kernel when one slice cannot hold k).
+static uw_status run_gemm(int src, const GemmArgs& a, int64_t tiles, int variant, int max_tile_verb, float* part,
+                          size_t part_bytes, hipStream_t s) {
   int ct = col_tiles(a.m);
-  if (variant < 0) variant = default_variant(tiles, a.kb, ct);
+  if (variant < 0) variant = a.m > 16 ? kMtDefault : default_variant(tiles, a.kb, ct);
+  if (kVariants[variant].kind == 1) {
+    const int R = kVariants[variant].waves, U = kVariants[variant].unroll;
+    int S = mt_slices(tiles, R, a.kb);
+    const size_t plane = (size_t)a.m * a.n * sizeof(float);
+    if (S > 1 && (!part || part_bytes < (size_t)S * plane))
+      S = part ? (int)std::min<size_t>(part_bytes / plane, (size_t)S) : 1;
+    const bool pal = src <= SRC_PAL_LUT;
+    if (S < 1 || (pal && (a.kb + S - 1) / S > 64)) {
+      variant = default_variant(tiles, a.kb, ct);  // not enough workspace: per-tile kernel
+    } else {
+      hipError_t e;
+      switch (src) {
+        case SRC_PAL_AFFINE: e = launch_mt<SRC_PAL_AFFINE>(a, tiles, R, U, S, part, s); break;
+        case SRC_PAL_LUT: e = launch_mt<SRC_PAL_LUT>(a, tiles, R, U, S, part, s); break;
+        case SRC_EXP: e = launch_mt<SRC_EXP>(a, tiles, R, U, S, part, s); break;
+        default: e = launch_mt<SRC_BF16>(a, tiles, R, U, S, part, s); break;
+      }
+      if (e != hipSuccess) return fail(UW_E_HIP, "gemm launch: %s", hipGetErrorString(e));
+      return UW_OK;
+    }
+  }
   Launch L;
   L.tiles = (int)tiles;
   L.unroll = kVariants[variant].unroll;
@@ -1080,11 +1404,12 @@ uw_status uw_workspace_size(const uw_dmat* d, int32_t m, int32_t op, size_t* byt
     int32_t v;
     if (!autotune_lookup(n, k, m, &pipe, &v)) pipe = UW_PIPE_DIRECT_PALETTE;
   }
+  const uint64_t parts = (uint64_t)mt_max_slices((int64_t)d->info.kb) * (uint64_t)std::max(m, 1) * n * sizeof(float);
   switch (pipe) {
-    case UW_PIPE_FULL_DECODE: *bytes = kErrBytes + align_up(2 * n * k, kAlign); break;
-    case UW_PIPE_EXP_ONLY: *bytes = kErrBytes + align_up(np * k, kAlign); break;
-    case UW_PIPE_TRANSCODE: *bytes = kErrBytes + align_up(np * k / 2, kAlign); break;
-    case UW_PIPE_DIRECT_PALETTE: *bytes = 0; break;
+    case UW_PIPE_FULL_DECODE: *bytes = kErrBytes + align_up(2 * n * k, kAlign) + parts; break;
+    case UW_PIPE_EXP_ONLY: *bytes = kErrBytes + align_up(np * k, kAlign) + parts; break;
+    case UW_PIPE_TRANSCODE: *bytes = kErrBytes + align_up(np * k / 2, kAlign) + parts; break;
+    case UW_PIPE_DIRECT_PALETTE: *bytes = kErrBytes + parts; break;
     case UW_OP_DECODE_FULL:
     case UW_OP_TRANSCODE:
     case UW_OP_DECODE_EXP: *bytes = kErrBytes; break;
@@ -1117,8 +1442,12 @@ int32_t uw_variant_count(void) { return kNumVariants; }
 const char* uw_variant_name(int32_t variant) {
   static char names[kNumVariants][48];
   if (variant < 0 || variant >= kNumVariants) return "";
-  snprintf(names[variant], sizeof(names[variant]), "waves=%d unroll=%d", kVariants[variant].waves,
-           kVariants[variant].unroll);
+  if (kVariants[variant].kind == 0)
+    snprintf(names[variant], sizeof(names[variant]), "waves=%d unroll=%d", kVariants[variant].waves,
+             kVariants[variant].unroll);
+  else
+    snprintf(names[variant], sizeof(names[variant]), "multitile tiles=%d unroll=%d", kVariants[variant].waves,
+             kVariants[variant].unroll);
   return names[variant];
 }
 
@@ -1140,38 +1469,54 @@ uw_status uw_gemm_variant(const uw_dmat* d, const uint16_t* x, float* y, int32_t
   }
   if (pipeline < UW_PIPE_FULL_DECODE || pipeline > UW_PIPE_DIRECT_PALETTE) return fail(UW_E_ARG, "bad pipeline %d", pipeline);
   if (variant < 0) variant = autotune_variant(d->info.n, d->info.k, m, pipeline);
-  size_t need = 0;
-  st = uw_workspace_size(d, m, pipeline, &need);
-  if (st) return st;
-  if (need && (!ws || ws_bytes < need)) return fail(UW_E_WORKSPACE, "pipeline %d needs %zu workspace bytes", pipeline, need);
+  // Workspace: [error word][decoded operand (pipelines 1-3)][K-slice partial sums].  The
+  // decode pipelines need the first two; the partial sums are optional (without them the
+  // multi-tile kernel runs one K slice or the per-tile kernel runs instead).
+  const uint64_t np = d->info.np, k = d->info.k, n = d->info.n;
+  uint64_t dec = 0;
+  switch (pipeline) {
+    case UW_PIPE_FULL_DECODE: dec = align_up(2 * n * k, kAlign); break;
+    case UW_PIPE_EXP_ONLY: dec = align_up(np * k, kAlign); break;
+    case UW_PIPE_TRANSCODE: dec = align_up(np * k / 2, kAlign); break;
+    default: break;
+  }
+  if (dec && (!ws || ws_bytes < kErrBytes + dec))
+    return fail(UW_E_WORKSPACE, "pipeline %d needs at least %llu workspace bytes", pipeline,
+                (unsigned long long)(kErrBytes + dec));
+  uint8_t* wsb = reinterpret_cast<uint8_t*>(ws);
+  float* part = nullptr;
+  size_t part_bytes = 0;
+  if (ws && ws_bytes > kErrBytes + dec) {
+    part = reinterpret_cast<float*>(wsb + kErrBytes + dec);
+    part_bytes = ws_bytes - kErrBytes - dec;
+  }
   GemmArgs a;
   fill_gemm_args(d, a, x, y, m);
-  uint8_t* wsb = reinterpret_cast<uint8_t*>(ws);
   const int pal_src = d->info.affine ? SRC_PAL_AFFINE : SRC_PAL_LUT;
   const int vs = d->max_tile_verb;
   switch (pipeline) {
     case UW_PIPE_DIRECT_PALETTE:
       if (!d->idx) return fail(UW_E_ARG, "direct palette needs an index stream bound at uw_dmat_bind");
       a.aux = d->idx;
-      st = run_gemm(pal_src, a, d->info.tiles, variant, vs, s);
+      st = run_gemm(pal_src, a, d->info.tiles, variant, vs, part, part_bytes, s);
       break;
     case UW_PIPE_TRANSCODE:
       st = run_decode(d, DEC_IDX, wsb + kErrBytes, ws, ws_bytes, s);
       if (st) return st;
       a.aux = wsb + kErrBytes;
-      st = run_gemm(pal_src, a, d->info.tiles, variant, vs, s);
+      st = run_gemm(pal_src, a, d->info.tiles, variant, vs, part, part_bytes, s);
       break;
     case UW_PIPE_EXP_ONLY:
       st = run_decode(d, DEC_EXP, wsb + kErrBytes, ws, ws_bytes, s);
       if (st) return st;
       a.aux = wsb + kErrBytes;
-      st = run_gemm(SRC_EXP, a, d->info.tiles, variant, 0, s);
+      st = run_gemm(SRC_EXP, a, d->info.tiles, variant, 0, part, part_bytes, s);
       break;
     default:
       st = run_decode(d, DEC_BF16, wsb + kErrBytes, ws, ws_bytes, s);
       if (st) return st;
       a.aux = wsb + kErrBytes;
-      st = run_gemm(SRC_BF16, a, d->info.tiles, variant, 0, s);
+      st = run_gemm(SRC_BF16, a, d->info.tiles, variant, 0, part, part_bytes, s);
       break;
   }
   if (!st) clear_error();
@@ -1200,7 +1545,7 @@ uw_status uw_gemm_bf16(const uint16_t* w, int64_t n, int64_t k, const uint16_t* 
   a.k = (int32_t)k;
   a.m = m;
   a.kb = (int32_t)(k / 64);
-  uw_status st = run_gemm(SRC_BF16, a, (n + 15) / 16, variant, 0, s);
+  uw_status st = run_gemm(SRC_BF16, a, (n + 15) / 16, variant, 0, nullptr, 0, s);
   if (!st) clear_error();
   return st;
 }

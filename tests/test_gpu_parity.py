@@ -129,17 +129,52 @@ def test_gemm_all_pipelines(name, m):
         check_gemm(y, x, w)
 
 
-@pytest.mark.parametrize("variant", range(10))
+N_VARIANTS = 14
+
+
+def test_variant_count():
+    assert uw.uw_variant_count() == N_VARIANTS
+
+
+@pytest.mark.parametrize("variant", range(N_VARIANTS))
 def test_gemm_every_variant(variant):
+    """Every kernel variant, with and without a workspace (the multi-tile kernel splits K
+    over workgroups only when it has room for the partial sums), at batch sizes that take
+    1, 2, 4 and 8 MFMA column tiles and a second column group."""
     t = torch()
     w = synth.small_gaussian(200, 2048, seed=11, plant_frac=0.05)["w"]
     cm = uw.CompressedMatrix(w)
-    for m in (1, 24, 70):
+    for m in (1, 24, 70, 128, 200):
         x = synth.gaussian_bf16(np.random.default_rng(m), (m, 2048), 1.0)
-        y = t.empty((m, 200), dtype=t.float32, device="cuda")
-        uw.uw_gemm_variant(cm.d, dev_u16(x), y, m, uw.UW_PIPE_DIRECT_PALETTE, variant)
+        for ws in (None, cm.workspace(m, uw.UW_PIPE_DIRECT_PALETTE)):
+            y = t.full((m, 200), float("nan"), dtype=t.float32, device="cuda")
+            uw.uw_gemm_variant(cm.d, dev_u16(x), y, m, uw.UW_PIPE_DIRECT_PALETTE, variant, ws)
+            check_gemm(y, x, w)
+        yb = t.full((m, 200), float("nan"), dtype=t.float32, device="cuda")
+        uw.uw_gemm_bf16(dev_u16(w), dev_u16(x), yb, m, variant)
+        check_gemm(yb, x, w)
+
+
+@pytest.mark.parametrize("variant", range(N_VARIANTS))
+def test_gemm_long_k_every_variant(variant):
+    """k = 9216 (144 blocks: more than one flag register of blocks, so the multi-tile kernel
+    needs several K slices), ragged rows, verbatim segments; the exponent and transcode
+    pipelines too."""
+    t = torch()
+    w = synth.small_gaussian(70, 9216, seed=13, plant_frac=0.1)["w"]
+    cm = uw.CompressedMatrix(w)
+    for m in (3, 40):
+        x = synth.gaussian_bf16(np.random.default_rng(m), (m, 9216), 1.0)
+        for pipe in (uw.UW_PIPE_DIRECT_PALETTE, uw.UW_PIPE_EXP_ONLY, uw.UW_PIPE_TRANSCODE):
+            ws = cm.workspace(m, pipe)
+            y = t.full((m, 70), float("nan"), dtype=t.float32, device="cuda")
+            uw.uw_gemm_variant(cm.d, dev_u16(x), y, m, pipe, variant, ws)
+            uw.uw_check(ws)
+            check_gemm(y, x, w)
+        y = t.full((m, 70), float("nan"), dtype=t.float32, device="cuda")
+        uw.uw_gemm_variant(cm.d, dev_u16(x), y, m, uw.UW_PIPE_DIRECT_PALETTE, variant, None)
         check_gemm(y, x, w)
-        yb = t.empty((m, 200), dtype=t.float32, device="cuda")
+        yb = t.full((m, 70), float("nan"), dtype=t.float32, device="cuda")
         uw.uw_gemm_bf16(dev_u16(w), dev_u16(x), yb, m, variant)
         check_gemm(yb, x, w)
 
