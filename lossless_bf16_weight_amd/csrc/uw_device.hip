@@ -654,39 +654,76 @@ __global__ __launch_bounds__(64 * R) void k_gemm_mt(GemmArgs a, float* part, int
   for (int c = 0; c < (kTwo ? CT : 1); ++c) acc2[c] = floatx4{0.f, 0.f, 0.f, 0.f};
   const int sw = r & C::kSwz;
 
-  issue_x(0, smem);
-  MtSlot<SRC> sl[U];
-  for (int i = 0; i < nbatch; ++i) {
-    __builtin_amdgcn_s_waitcnt(0);   // this wave's X DMAs for batch i have landed
-    __syncthreads();                 // ... and everyone's; batch i-1's buffer is free again
-    const int b = bs + i * U;
+  auto load_batch = [&](int i, MtSlot<SRC>* sl) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) load_block(b + u, sl[u]);
-    if (i + 1 < nbatch) issue_x(i + 1, smem + ((i + 1) & 1) * C::kBufBytes);
-    const uint8_t* xbuf = smem + (i & 1) * C::kBufBytes;
+    for (int u = 0; u < U; ++u) load_block(bs + i * U + u, sl[u]);
+  };
+  // X fragments of block u of the batch: column tile c, MFMA step k2 (x[c][0..1]).
+  auto load_x = [&](const uint8_t* xbuf, int u, u32x4 (&x)[CT][2]) {
+    const int q0 = u * 8 + g * 2;
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+      x[c][0] = *reinterpret_cast<const u32x4*>(xbuf + ((16 * c + r) * C::kGpr + (q0 ^ sw)) * 16);
+      x[c][1] = *reinterpret_cast<const u32x4*>(xbuf + ((16 * c + r) * C::kGpr + ((q0 + 1) ^ sw)) * 16);
+    }
+  };
+  // One block: rebuild this lane's weights, then 2*CT MFMAs against the block's X fragments.
+  auto mma_block = [&](int b, const MtSlot<SRC>& sl, const u32x4 (&x)[CT][2]) {
+    uint32_t f = 0;
+    if constexpr (kPal) f = __builtin_amdgcn_readlane(wfl, b - bs);
+    u32x4 A0, A1;
+    rebuild_block<SRC>(a, sl.w, f, r, sl.ev, A0, A1);
+    const bf16x8 a0 = __builtin_bit_cast(bf16x8, A0), a1 = __builtin_bit_cast(bf16x8, A1);
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, __builtin_bit_cast(bf16x8, x[c][0]), acc[c], 0, 0, 0);
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+      if constexpr (kTwo)
+        acc2[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, __builtin_bit_cast(bf16x8, x[c][1]), acc2[c], 0, 0, 0);
+      else
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, __builtin_bit_cast(bf16x8, x[c][1]), acc[c], 0, 0, 0);
+    }
+  };
+  // A batch: the X fragments of block u+1 are read from LDS while block u is computed.
+  auto compute_batch = [&](int i, const MtSlot<SRC>* sl, const uint8_t* xbuf) {
+    const int b = bs + i * U;
+    u32x4 xe[CT][2], xo[CT][2];
+    load_x(xbuf, 0, xe);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (b + u >= be) break;
-      uint32_t f = 0;
-      if constexpr (kPal) f = __builtin_amdgcn_readlane(wfl, b + u - bs);
-      u32x4 A0, A1;
-      rebuild_block<SRC>(a, sl[u].w, f, r, sl[u].ev, A0, A1);
-      const bf16x8 a0 = __builtin_bit_cast(bf16x8, A0), a1 = __builtin_bit_cast(bf16x8, A1);
-      const int q0 = u * 8 + g * 2;
-#pragma unroll
-      for (int c = 0; c < CT; ++c) {
-        const u32x4 x0 = *reinterpret_cast<const u32x4*>(xbuf + ((16 * c + r) * C::kGpr + (q0 ^ sw)) * 16);
-        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, __builtin_bit_cast(bf16x8, x0), acc[c], 0, 0, 0);
+      if (u + 1 < U) {
+        if (u & 1) load_x(xbuf, u + 1, xe); else load_x(xbuf, u + 1, xo);
       }
-#pragma unroll
-      for (int c = 0; c < CT; ++c) {
-        const u32x4 x1 = *reinterpret_cast<const u32x4*>(xbuf + ((16 * c + r) * C::kGpr + ((q0 + 1) ^ sw)) * 16);
-        if constexpr (kTwo)
-          acc2[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, __builtin_bit_cast(bf16x8, x1), acc2[c], 0, 0, 0);
-        else
-          acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, __builtin_bit_cast(bf16x8, x1), acc[c], 0, 0, 0);
-      }
+      if (u & 1) mma_block(b + u, sl[u], xo); else mma_block(b + u, sl[u], xe);
     }
+  };
+
+  // Software pipeline, one batch deep: the weights and X of batch i+1 are requested before
+  // batch i is computed, so they have a whole compute phase to arrive.  Two register sets
+  // (sa, sb) and two X buffers alternate; each phase starts with a barrier after which
+  // batch i's data is in place and batch i-1's X buffer is free.
+  MtSlot<SRC> sa[U], sb[U];
+  uint8_t* const xb1 = smem + C::kBufBytes;
+  load_batch(0, sa);
+  issue_x(0, smem);
+  for (int i = 0; i < nbatch; i += 2) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (i + 1 < nbatch) {
+      load_batch(i + 1, sb);
+      issue_x(i + 1, xb1);
+    }
+    compute_batch(i, sa, smem);
+    if (i + 1 >= nbatch) break;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (i + 2 < nbatch) {
+      load_batch(i + 2, sa);
+      issue_x(i + 2, smem);
+    }
+    compute_batch(i + 1, sb, xb1);
   }
   if constexpr (kTwo) {
 #pragma unroll
