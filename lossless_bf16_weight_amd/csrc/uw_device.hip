@@ -748,13 +748,21 @@ __global__ __launch_bounds__(64 * R) void k_gemm_mt(GemmArgs a, float* part, int
   }
 }
 
-// y[i] = sum over s of part[s][i], in slice order.
+// y[i] = sum over s of part[s][i], in slice order.  A thread owns 4 consecutive elements
+// and requests all S slices' values before adding them, so the loads overlap.
+constexpr int kMaxSlices = 16;
 __global__ __launch_bounds__(256) void k_reduce_parts(const float* part, float* y, int S, int64_t count) {
   const int64_t n4 = count >> 2;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
-    floatx4 v = reinterpret_cast<const floatx4*>(part)[i];
-    for (int s = 1; s < S; ++s) v += reinterpret_cast<const floatx4*>(part + (size_t)s * count)[i];
-    reinterpret_cast<floatx4*>(y)[i] = v;
+    floatx4 v[kMaxSlices];
+#pragma unroll
+    for (int s = 0; s < kMaxSlices; ++s)
+      if (s < S) v[s] = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(part + (size_t)s * count) + i);
+    floatx4 sum = v[0];
+#pragma unroll
+    for (int s = 1; s < kMaxSlices; ++s)
+      if (s < S) sum += v[s];
+    reinterpret_cast<floatx4*>(y)[i] = sum;
   }
   for (int64_t i = (n4 << 2) + (int64_t)blockIdx.x * 256 + threadIdx.x; i < count; i += (int64_t)gridDim.x * 256) {
     float v = part[i];
@@ -1137,7 +1145,7 @@ static int mt_slices(int64_t tiles, int R, int64_t kb) {
   S = std::min<int64_t>(std::max<int64_t>(S, 1), std::min<int64_t>(kb, 16));
   return (int)S;
 }
-static int64_t mt_max_slices(int64_t kb) { return std::max<int64_t>(16, (kb + 63) / 64); }
+static int64_t mt_max_slices(int64_t kb) { return std::max<int64_t>(kMaxSlices, (kb + 63) / 64); }
 
 template <int SRC, int CT, int U, int R>
 static hipError_t launch_mt_t(const GemmArgs& a, int64_t tiles, int S, float* part, hipStream_t s) {
@@ -1147,7 +1155,7 @@ static hipError_t launch_mt_t(const GemmArgs& a, int64_t tiles, int S, float* pa
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
   const int64_t count = (int64_t)a.m * a.n;
-  const int64_t blocks = std::min<int64_t>((count / 4 + 255) / 256 + 1, 2048);
+  const int64_t blocks = std::min<int64_t>((count / 4 + 255) / 256 + 1, 4096);
   hipLaunchKernelGGL(k_reduce_parts, dim3((unsigned)blocks), dim3(256), 0, s, part, a.y, S, count);
   return hipGetLastError();
 }

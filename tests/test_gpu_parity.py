@@ -179,6 +179,33 @@ def test_gemm_long_k_every_variant(variant):
         check_gemm(yb, x, w)
 
 
+def test_shared_workspace_across_calls():
+    """One zeroed workspace serves a sequence of calls on different matrices, batch sizes and
+    pipelines (each call must leave the K-split counters as it found them), and repeating the
+    sequence reproduces every output bit for bit (partial sums are added in slice order)."""
+    t = torch()
+    mats = [synth.small_gaussian(200, 2048, seed=31, plant_frac=0.05)["w"],
+            synth.small_gaussian(70, 9216, seed=32, plant_frac=0.1)["w"]]
+    cms = [uw.CompressedMatrix(w) for w in mats]
+    calls = [(i, m, p) for i in range(2) for m in (24, 70, 128, 200) for p in ALL_PIPES]
+    size = max(uw.uw_workspace_size(cms[i].d, m, p) for i, m, p in calls)
+    ws = t.zeros(size, dtype=t.uint8, device="cuda")
+    first = {}
+    for rep in range(2):
+        for i, m, p in calls:
+            w = mats[i]
+            x = synth.gaussian_bf16(np.random.default_rng(1000 + m), (m, w.shape[1]), 1.0)
+            y = t.full((m, w.shape[0]), float("nan"), dtype=t.float32, device="cuda")
+            uw.uw_gemm_variant(cms[i].d, dev_u16(x), y, m, p, 13 if m > 16 else -1, ws)
+            uw.uw_check(ws)
+            out = y.cpu().numpy()
+            if rep == 0:
+                check_gemm(y, x, w)
+                first[(i, m, p)] = out
+            else:
+                assert np.array_equal(out, first[(i, m, p)]), (i, m, p)
+
+
 def test_bf16_gemm_ragged_rows():
     t = torch()
     w = synth.small_gaussian(45, 320, seed=2)["w"]
