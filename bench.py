@@ -111,6 +111,121 @@ def time_launches(fn, copies, steps, warmup, stream):
     return total, per
 
 
+def time_torch_bf16(w, xs, steps, warmup):
+    """torch.matmul (hipBLASLt) on the uncompressed BF16 matrix, rotated copies, per batch."""
+    import torch
+    n, k = w.shape
+    copies = max(2, int(np.ceil(ROTATE_BYTES / (2 * n * k))))
+    wd = [torch.from_numpy(w.view(np.int16)).cuda().view(torch.bfloat16) for _ in range(copies)]
+    out = {}
+    for m, xd in xs.items():
+        xb = xd.view(torch.bfloat16)
+        tot, _ = time_launches(lambda i: torch.matmul(xb, wd[i].t()), copies, steps, warmup,
+                               torch.cuda.current_stream())
+        out[m] = tot * 1e3 / steps
+    del wd
+    return out
+
+
+def diagnostic(args):
+    """Diagnostic lines (not the headline): every pipeline autotuned per batch size on the
+    down_proj shape (4096 x 14336, M = 1..64) or the heavy-tail 8192^2 matrix (M = 128), timed
+    against torch BF16; or one decode step through the 32-layer MLP stack at M = 16."""
+    import torch
+    import lossless_bf16_weight_amd as uw
+    from lossless_bf16_weight_amd import autotune, synth
+    from oracle import gemm as ogemm
+    assert torch.cuda.is_available(), "no GPU"
+    steps, warmup = min(args.steps, 200), min(args.warmup, 20)
+    if args.workload == "stack":
+        return stack_step(args, steps, warmup)
+    c = synth.config3() if args.workload == "down" else synth.config5()
+    ms = (1, 8, 16, 32, 64) if args.workload == "down" else (128,)
+    w, x_all = c["w"], c["x"]
+    n, k = w.shape
+    tuner = autotune.Tuner(w, rotate_bytes=ROTATE_BYTES)
+    table = tuner.tune(ms, log=log)
+    table.apply()
+    info = uw.uw_blob_info(tuner.blob)
+    resident = int(info["resident_bytes"])
+    xs = {m: torch.from_numpy(np.ascontiguousarray(x_all[:m]).view(np.int16)).cuda() for m in ms}
+    rows = np.random.default_rng(0).choice(n, 256, replace=False)
+    res = []
+    torch_us = time_torch_bf16(w, xs, steps, warmup)
+    for m in ms:
+        best = table.best_pipeline(n, k, m)
+        ws = torch.zeros(uw.uw_workspace_size(tuner.mats[0], m, best.pipeline), dtype=torch.uint8, device="cuda")
+        y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+        step = lambda i: uw.uw_gemm(tuner.mats[i], xs[m], y, m, uw.UW_PIPE_AUTO, ws)
+        step(0)
+        torch.cuda.synchronize()
+        yr, sr = ogemm.gemm_ref_rows(np.ascontiguousarray(x_all[:m]), w, rows)
+        assert ogemm.within_bound(y.cpu().numpy().astype(np.float64)[:, rows], yr, sr).all(), "parity failure"
+        tot, _ = time_launches(step, tuner.copies, steps, warmup, torch.cuda.current_stream())
+        us = tot * 1e3 / steps
+        bf = table.best_variant.get((n, k, m, uw.UW_PIPE_BF16))
+        res.append({"m": m, "pipeline": autotune.PIPELINE_NAMES[best.pipeline],
+                    "variant": uw.uw_variant_name(best.variant), "us": round(us, 3),
+                    "compressed_tb_s": round((resident + 2 * m * k + 4 * m * n) / us / 1e6, 3),
+                    "eff_weight_gb_s": round(2.0 * n * k / us / 1e3, 1),
+                    "tflop_s": round(2.0 * m * n * k / us / 1e6, 1),
+                    "torch_bf16_us": round(torch_us[m], 3),
+                    "own_bf16_us": round(bf.us, 3) if bf else None,
+                    "speedup_vs_torch_bf16": round(torch_us[m] / us, 3)})
+        log("m=%d: %s" % (m, res[-1]))
+    return {"diagnostic": args.workload, "n": n, "k": k, "bits_per_weight": round(8 * resident / (n * k), 4),
+            "results": res}
+
+
+def stack_step(args, steps, warmup):
+    """One decode step at M = 16 through the 32-layer MLP stack (96 compressed matrices, SwiGLU
+    and RMS norm between), timed against the same step with torch BF16 matmuls."""
+    import torch
+    from concurrent.futures import ThreadPoolExecutor
+    import lossless_bf16_weight_amd as uw
+    from lossless_bf16_weight_amd import synth
+    from lossless_bf16_weight_amd.stack import MLPStack
+    meta = synth.config4_meta()
+    layers = len(meta["stds"])
+    st = MLPStack(16, 4096, 14336)
+    bf = []
+    t0 = time.time()
+    jobs = [(l, j) for l in range(layers) for j in range(3)]
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        mats = ex.map(lambda lj: synth.config4_matrix(meta, *lj), jobs)
+        pending = []
+        for (l, j), w in zip(jobs, mats):
+            pending.append(uw.CompressedMatrix(w))
+            bf.append(torch.from_numpy(w.view(np.int16)).cuda().view(torch.bfloat16))
+            if j == 2:
+                st.add_layer(*pending)
+                pending = []
+    log("stack built in %.1fs" % (time.time() - t0))
+    x = torch.from_numpy(meta["x"].view(np.int16)).cuda()
+    step = lambda i: st.step(x, pipeline=uw.UW_PIPE_DIRECT_PALETTE, check=False)
+    tot, _ = time_launches(step, 1, steps, warmup, torch.cuda.current_stream())
+    us = tot * 1e3 / steps
+    xb = x.view(torch.bfloat16)
+
+    def step_bf16(i):
+        h = xb
+        for l in range(layers):
+            g = torch.matmul(h, bf[3 * l].t()).float()
+            u = torch.matmul(h, bf[3 * l + 1].t()).float()
+            a = (torch.nn.functional.silu(g) * u).to(torch.bfloat16)
+            yy = torch.matmul(a, bf[3 * l + 2].t()).float()
+            h = (yy * torch.rsqrt((yy * yy).mean(dim=1, keepdim=True) + 1e-5)).to(torch.bfloat16)
+        return h
+
+    tot_b, _ = time_launches(step_bf16, 1, steps, warmup, torch.cuda.current_stream())
+    us_b = tot_b * 1e3 / steps
+    nparams = st.weight_count()
+    return {"diagnostic": "stack", "layers": layers, "m": 16, "us_per_step": round(us, 1),
+            "tokens_per_s": round(16 / (us * 1e-6), 1), "eff_weight_gb_s": round(2.0 * nparams / us / 1e3, 1),
+            "compressed_tb_s": round(st.resident_bytes() / us / 1e6, 3),
+            "torch_bf16_us_per_step": round(us_b, 1), "speedup_vs_torch_bf16": round(us_b / us, 3)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -120,6 +235,9 @@ def main():
     ap.add_argument("--variant", type=int, default=-1, help="fused-kernel variant id (default: autotuned)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run three device copies of 512 MiB (HBM counter calibration) and exit")
+    ap.add_argument("--workload", default="gate", choices=("gate", "down", "heavy", "stack"),
+                    help="gate (default: the headline line); down, heavy, stack: diagnostic lines for the "
+                         "down_proj batch sweep, the 8192^2 heavy-tail matrix at M=128 and the 32-layer stack")
     args = ap.parse_args()
     if args.copy_calibration:
         import torch
@@ -133,6 +251,10 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path (--gpus %d refused)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
+
+    if args.workload != "gate":
+        print(json.dumps(diagnostic(args)), flush=True)
+        return
 
     import torch
     import lossless_bf16_weight_amd as uw

@@ -52,10 +52,12 @@ class MLPStack:
             self.ws_bytes = need
         return self.ws if need else None
 
-    def step(self, x, pipeline=UW_PIPE_AUTO, trace=None):
+    def step(self, x, pipeline=UW_PIPE_AUTO, trace=None, check=True):
         """x: device int16 [m, hidden] (BF16 bits).  Returns the device tensor holding the last
         layer's output (one of two ping-pong buffers).  trace: optional list that receives,
-        per layer, host copies (x_in, g, u, h, y, x_out) -- for tests; it synchronises."""
+        per layer, host copies (x_in, g, u, h, y, x_out) -- for tests; it synchronises.
+        check: wait for the step and report a corrupt stream found by a decode pipeline
+        (UwError); pass False to keep the step asynchronous."""
         ws = self._workspace(pipeline)
         cur = x
         for i, (gate, up, down) in enumerate(self.layers):
@@ -68,7 +70,7 @@ class MLPStack:
             if trace is not None:
                 trace.append(tuple(t.cpu().numpy().copy() for t in (cur, self.g, self.u, self.h, self.y, out)))
             cur = out
-        if ws is not None:
+        if ws is not None and check:
             uw_check(ws)
         return cur
 
