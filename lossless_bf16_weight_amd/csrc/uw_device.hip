@@ -786,10 +786,13 @@ __global__ __launch_bounds__(256) void k_reduce_parts(const float* part, float* 
 //      table indexed by the next 3 bits.  The loop body is branch-free apart from that case:
 //      the refill word is read every step and used or not, and every step stores a word
 //      (to the image when 8 indices are ready, else to a per-lane dummy slot).
-//   3. Decoded 4-bit indices go to an LDS image of the unit's output (the direct-palette
-//      index layout), and the workgroup then writes the image with full-line stores; the
-//      exponent and BF16 modes convert the image while writing (palette lookup, verbatim
-//      segments from vexp, sign+mantissa merge for BF16).
+//   3. Index and exponent modes store each finished 8-index word (or its 8 exponents)
+//      straight to global memory with a bounds-checked buffer store (out of range when a lane
+//      has nothing to store, so the loop stays branch-free); without an output image the
+//      workgroup needs ~19 KB of LDS and eight fit on a CU.  The partial-line stores cost
+//      write bandwidth (about 5x / 2.5x the output bytes) that the decode arithmetic hides.
+//      The BF16 mode collects indices in an LDS image of the unit's output and merges them
+//      with the sign+mantissa bytes while writing whole lines.
 // =========================================================================================
 enum DecMode { DEC_IDX = 0, DEC_EXP = 1, DEC_BF16 = 2 };
 
@@ -828,12 +831,14 @@ struct DecLds {            // offsets (bytes) into the dynamic LDS block
   uint32_t lut, image, stage, blk, total;
 };
 
-// stage_words: a multiple of 256 (the bitstream slice is staged in 1 KB DMA steps).
-__host__ __device__ inline DecLds dec_lds(int nb, uint32_t stage_words) {
+// stage_words: a multiple of 256 (the bitstream slice is staged in 1 KB DMA steps).  direct:
+// the index mode writes straight to global memory and needs no image (the region then only
+// holds the table-build scratch).
+__host__ __device__ inline DecLds dec_lds(int nb, uint32_t stage_words, bool direct) {
   DecLds L;
   L.lut = 0;
   L.image = (kDecLut + kDecSec) * 4;
-  const uint32_t img = std::max<uint32_t>((uint32_t)nb * kImgBlk * 4u, kDecLut * 2u);  // also holds the build table
+  const uint32_t img = direct ? kDecLut * 2u : std::max<uint32_t>((uint32_t)nb * kImgBlk * 4u, kDecLut * 2u);
   L.stage = L.image + ((img + 15u) & ~15u);
   L.blk = L.stage + stage_words * 4;
   L.total = L.blk + 3u * 64u * 4u;   // block flags, verbatim ranks, per-lane dummy slots
@@ -907,7 +912,8 @@ __device__ void build_dec_lut(const DecArgs& a, uint32_t* lut, uint16_t* tmp, in
 template <int MODE>
 __global__ __launch_bounds__(64) void k_decode(DecArgs a) {
   extern __shared__ __align__(16) uint8_t dsh[];
-  const DecLds Ls = dec_lds(a.nb, a.stage_words);
+  constexpr bool kDirect = MODE != DEC_BF16;
+  const DecLds Ls = dec_lds(a.nb, a.stage_words, kDirect);
   uint32_t* lut = reinterpret_cast<uint32_t*>(dsh + Ls.lut);
   uint32_t* img = reinterpret_cast<uint32_t*>(dsh + Ls.image);
   uint32_t* stage = reinterpret_cast<uint32_t*>(dsh + Ls.stage);
@@ -963,8 +969,13 @@ __global__ __launch_bounds__(64) void k_decode(DecArgs a) {
   }
   build_dec_lut(a, lut, reinterpret_cast<uint16_t*>(img), lane);
   // Zero the image: verbatim and padding rows stay zero in the index layout.
-  for (int i = lane * 4; i < nbu * kImgBlk; i += 256) *reinterpret_cast<u32x4*>(img + i) = u32x4{0, 0, 0, 0};
+  if constexpr (!kDirect)
+    for (int i = lane * 4; i < nbu * kImgBlk; i += 256) *reinterpret_cast<u32x4*>(img + i) = u32x4{0, 0, 0, 0};
   __syncthreads();
+  // Index and exponent modes: results go straight to the unit's output range (a lane without
+  // a finished word stores out of range, which writes nothing).
+  constexpr uint32_t kOutBlk = MODE == DEC_IDX ? 512u : 1024u;   // output bytes per block
+  const __amdgpu_buffer_rsrc_t ors = make_rsrc(a.out + ((size_t)t * a.kb + bA) * kOutBlk, (uint32_t)nbu * kOutBlk);
 
   // Decode: lane -> (block in unit, chunk in block).
   const int bl = lane / a.cpb, j = lane % a.cpb;
@@ -1011,8 +1022,19 @@ __global__ __launch_bounds__(64) void k_decode(DecArgs a) {
       wi += need ? 1u : 0u;
       // 8 indices ready: store the index word (sub-tile sw / 2, half sw % 2 of row r).
       const bool flush = accn >= 8;
-      const uint32_t word_i = blk_img + (uint32_t)r * 2u + (sw >> 1) * 32u + (sw & 1u);
-      *(flush ? img + word_i : dummy) = nibbles_to_index_word((uint32_t)acc);
+      if constexpr (MODE == DEC_IDX) {
+        const uint32_t off = (uint32_t)bl * 512u + (sw >> 1) * 128u + (uint32_t)r * 8u + (sw & 1u) * 4u;
+        __builtin_amdgcn_raw_buffer_store_b32(nibbles_to_index_word((uint32_t)acc), ors, flush ? off : kOob, 0, 0);
+      } else if constexpr (MODE == DEC_EXP) {
+        // 8 exponents: half (sw % 2) of sub-tile (sw / 2) row r, 16 bytes a sub-tile row.
+        const u32x2 ex = index_word_to_exps(nibbles_to_index_word((uint32_t)acc), a.tab);
+        const uint32_t off = (uint32_t)bl * 1024u + (sw >> 1) * 256u + (uint32_t)r * 16u + (sw & 1u) * 8u;
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) int, ex), ors,
+                                              flush ? off : kOob, 0, 0);
+      } else {
+        const uint32_t word_i = blk_img + (uint32_t)r * 2u + (sw >> 1) * 32u + (sw & 1u);
+        *(flush ? img + word_i : dummy) = nibbles_to_index_word((uint32_t)acc);
+      }
       acc = flush ? acc >> 32 : acc;
       accn -= flush ? 8u : 0u;
       sw += flush ? 1u : 0u;
@@ -1027,27 +1049,29 @@ __global__ __launch_bounds__(64) void k_decode(DecArgs a) {
   if (bad) atomicOr(a.err, 1u);
   __syncthreads();
 
-  // Write the unit's output with whole-line stores.
+  // Write the rest of the unit's output.
   if constexpr (MODE == DEC_IDX) {
-    u32x4* dst = reinterpret_cast<u32x4*>(a.out + ((size_t)t * a.kb + bA) * 512);
-    for (int i = lane; i < nbu * 32; i += 64)
-      dst[i] = *reinterpret_cast<const u32x4*>(img + (i >> 5) * kImgBlk + (i & 31) * 4);
+    // Verbatim and padding rows hold index 0.
+    for (int p = lane; p < nbu * 16; p += 64) {
+      const int b = p >> 4, rr = p & 15;
+      if (rr < rows && !((blk_f[b] >> rr) & 1u)) continue;
+#pragma unroll
+      for (int g2 = 0; g2 < 4; ++g2)
+        *reinterpret_cast<u32x2*>(a.out + ((size_t)t * a.kb + bA + b) * 512 + g2 * 128 + rr * 8) = u32x2{0, 0};
+    }
   } else if constexpr (MODE == DEC_EXP) {
-    // 16-byte piece p: block p / 64, sub-tile (p / 16) % 4, row p % 16.
+    // Verbatim rows take their raw exponents, padding rows zeros; 16-byte piece p: block
+    // p / 64, sub-tile (p / 16) % 4, row p % 16.
     u32x4* dst = reinterpret_cast<u32x4*>(a.out + ((size_t)t * a.kb + bA) * 1024);
     for (int p = lane; p < nbu * 64; p += 64) {
       const int b = p >> 6, g = (p >> 4) & 3, r = p & 15;
       const uint32_t fb = blk_f[b];
-      u32x4 o = {0, 0, 0, 0};
       if ((fb >> r) & 1u) {
         const uint32_t v = blk_v[b] + __popc(fb & ((1u << r) - 1u));
-        o = *reinterpret_cast<const u32x4*>(a.vexp + (size_t)v * 64 + g * 16);
-      } else if (r < rows) {
-        const u32x2 iw = *reinterpret_cast<const u32x2*>(img + b * kImgBlk + (g * 16 + r) * 2);
-        const u32x2 lo = index_word_to_exps(iw.x, a.tab), hi = index_word_to_exps(iw.y, a.tab);
-        o = u32x4{lo.x, lo.y, hi.x, hi.y};
+        dst[(b * 4 + g) * 16 + r] = *reinterpret_cast<const u32x4*>(a.vexp + (size_t)v * 64 + g * 16);
+      } else if (r >= rows) {
+        dst[(b * 4 + g) * 16 + r] = u32x4{0, 0, 0, 0};
       }
-      dst[p] = o;
     }
   } else {
     // BF16 rows: 16-byte piece p = 8 weights; row p / (nbu*8), then block, sub-tile, half.
@@ -1331,7 +1355,7 @@ static uw_status run_decode(const uw_dmat* d, int mode, uint8_t* out, void* ws, 
     const uint32_t low = (code << (13 - L)) & 7u, cnt = 1u << (13 - L);
     for (uint32_t q = 0; q < cnt; ++q) a.sec[(blk + 1) * 8 + low + q] = 1u | ((uint32_t)L << 3) | ((uint32_t)L << 7) | ((uint32_t)sym << 16);
   }
-  const DecLds L = dec_lds(a.nb, a.stage_words);
+  const DecLds L = dec_lds(a.nb, a.stage_words, mode != DEC_BF16);
   int dev = 0, lds_max = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
