@@ -127,6 +127,7 @@ struct GemmArgs {
   const uint16_t* x;
   float* y;
   int32_t n, k, m, kb;
+  int32_t vs_segs;          // per-tile kernel: verbatim segments the LDS stage holds (multiple of 16)
   uint32_t base2;
   uint32_t tab[4];
   uint32_t m0, m1;  // 0x000F000F, 0x00F000F0 (see exps_affine)
@@ -190,24 +191,29 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, uint8_t* ld
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)lds, 16, voff, 0, 0, 0);
 }
 
-// LDS layout of k_gemm (bytes): partial sums | flags (u16) | verbatim prefix (u32) |
-// verbatim exponents | X rows (padded) + one zero row.
+// LDS layout of k_gemm (bytes): flags (u16) | verbatim prefix (u32) | verbatim exponents
+// (vs_segs segments) | X rows (padded).  The cross-wave partial sums reuse the same bytes
+// once every wave is done with the staged data, so the footprint stays small enough for
+// four 8-wave workgroups a CU.
 struct LdsLayout {
   uint32_t red, fl, vp, ve, x, total;
 };
-__host__ __device__ inline LdsLayout lds_layout(int nw, int ct, int kb, bool pal, bool vs, bool xl, int mv, int k) {
+__host__ __device__ inline LdsLayout lds_layout(int nw, int ct, int kb, bool pal, int vs_segs, bool xl, int mv,
+                                                int k) {
   LdsLayout L;
   L.red = 0;
-  L.fl = (uint32_t)nw * ct * 64 * 16;
+  L.fl = 0;
   L.vp = L.fl + (pal ? (uint32_t)((kb * 2 + 15) / 16 * 16) : 0u);
   L.ve = L.vp + (pal ? (uint32_t)(((kb + 1) * 4 + 15) / 16 * 16) : 0u);
-  L.x = L.ve + (pal && vs ? (uint32_t)kVexpStageSegs * 64 : 0u);
-  L.total = L.x + (xl ? (uint32_t)(mv + 1) * xl_stride(k) : 0u);
+  L.x = L.ve + (pal ? (uint32_t)vs_segs * 64 : 0u);
+  L.total = L.x + (xl ? (uint32_t)mv * xl_stride(k) : 0u);
+  const uint32_t red_bytes = nw > 1 ? (uint32_t)nw * ct * 64 * 16 : 0u;
+  if (L.total < red_bytes) L.total = red_bytes;
   return L;
 }
 
-// Dynamic LDS: [nw*CT*64 floatx4 partial sums][kb u32 flags][kb+1 u32 verbatim prefix]
-//              [VS: staged verbatim exponents][XL: mv padded X rows + 1 zero row]
+// Dynamic LDS: [kb u16 flags][kb+1 u32 verbatim prefix][VS: staged verbatim exponents]
+//              [XL: mv padded X rows]; the nw*CT*64 floatx4 partial sums alias it at the end
 template <int SRC, int CT, int U, int XL, int VS>
 __global__ __launch_bounds__((MaxThreads<CT, U>::v)) void k_gemm(GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -222,7 +228,7 @@ __global__ __launch_bounds__((MaxThreads<CT, U>::v)) void k_gemm(GemmArgs a) {
   const int mcol0 = blockIdx.y * 16 * CT;
   const int mv = min(16 * CT, a.m - mcol0);  // valid X rows of this column block
   constexpr bool kPal = SRC <= SRC_PAL_LUT;
-  const LdsLayout lay = lds_layout(nw, CT, kb, kPal, VS, XL, mv, a.k);
+  const LdsLayout lay = lds_layout(nw, CT, kb, kPal, VS ? a.vs_segs : 0, XL, mv, a.k);
   floatx4* red = reinterpret_cast<floatx4*>(smem + lay.red);
   uint16_t* sfl = reinterpret_cast<uint16_t*>(smem + lay.fl);
   uint32_t* svp = reinterpret_cast<uint32_t*>(smem + lay.vp);
@@ -264,8 +270,9 @@ __global__ __launch_bounds__((MaxThreads<CT, U>::v)) void k_gemm(GemmArgs a) {
   uint32_t xoff[CT];
 #pragma unroll
   for (int c = 0; c < CT; ++c) xoff[c] = 16 * c + r < mv ? (uint32_t)((16 * c + r) * a.k + g * 16) * 2 : kOob;
-  // XL: LDS byte offset of this lane's X row; rows past mv read the zero row after the X rows
-  const uint32_t xl_off = (uint32_t)((r < mv ? r : mv) * xl_stride(a.k) + g * 32);
+  // XL: LDS byte offset of this lane's X row.  Rows past mv read row 0: they only feed MFMA
+  // output columns past mv, which are never stored.
+  const uint32_t xl_off = (uint32_t)((r < mv ? r : 0) * xl_stride(a.k) + g * 32);
 
   uint32_t vbase = 0;
   __amdgpu_buffer_rsrc_t vrs = make_rsrc(a.vexp, 0);
@@ -362,7 +369,7 @@ __global__ __launch_bounds__((MaxThreads<CT, U>::v)) void k_gemm(GemmArgs a) {
 #pragma unroll
     for (int c = 0; c < CT; ++c) {
       u32x4 x0, x1;
-      if constexpr (XL) {  // X rows from LDS (rows past mv read the zero row)
+      if constexpr (XL) {  // X rows from LDS
         const u32x4* xp = reinterpret_cast<const u32x4*>(sx + xl_off + b * 128);
         x0 = xp[0];
         x1 = xp[1];
@@ -405,8 +412,6 @@ __global__ __launch_bounds__((MaxThreads<CT, U>::v)) void k_gemm(GemmArgs a) {
       const int mr = c / per_row, cc = c - mr * per_row;
       lds_dma16(xrs, sx + (size_t)mr * xl_stride(a.k) + cc * 1024, (uint32_t)mr * a.k * 2 + cc * 1024 + lane * 16);
     }
-    for (int i = threadIdx.x; i < xl_stride(a.k) / 16; i += blockDim.x)
-      reinterpret_cast<u32x4*>(sx + (size_t)mv * xl_stride(a.k))[i] = u32x4{0, 0, 0, 0};
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) load_main(b0 + u, u < nblk, buf[u]);
@@ -472,6 +477,7 @@ __global__ __launch_bounds__((MaxThreads<CT, U>::v)) void k_gemm(GemmArgs a) {
     for (int c = 0; c < CT; ++c) store(c, lane, acc[c]);
     return;
   }
+  __syncthreads();  // the partial sums overwrite the staged X rows and exponents
 #pragma unroll
   for (int c = 0; c < CT; ++c) red[(wave * CT + c) * 64 + lane] = acc[c];
   __syncthreads();
@@ -1218,8 +1224,10 @@ struct Launch {
 template <int SRC, int CT, int U, int XL, int VS>
 static hipError_t launch_gemm_t(const GemmArgs& a, const Launch& L, hipStream_t s) {
   const int gy = (a.m + 16 * CT - 1) / (16 * CT);
-  const size_t shm = lds_layout(L.waves, CT, a.kb, SRC <= SRC_PAL_LUT, VS, XL, std::min(a.m, 16 * CT), a.k).total;
-  hipLaunchKernelGGL((k_gemm<SRC, CT, U, XL, VS>), dim3(L.tiles, gy), dim3(64 * L.waves), shm, s, a);
+  GemmArgs b = a;
+  b.vs_segs = VS ? (L.max_tile_verb + 15) / 16 * 16 : 0;  // the stage is filled 16 segments at a time
+  const size_t shm = lds_layout(L.waves, CT, a.kb, SRC <= SRC_PAL_LUT, b.vs_segs, XL, std::min(a.m, 16 * CT), a.k).total;
+  hipLaunchKernelGGL((k_gemm<SRC, CT, U, XL, VS>), dim3(L.tiles, gy), dim3(64 * L.waves), shm, s, b);
   return hipGetLastError();
 }
 
@@ -1238,7 +1246,7 @@ template <int SRC, int CT>
 static hipError_t launch_gemm_v(const GemmArgs& a, const Launch& L, hipStream_t s) {
   constexpr bool pal = SRC <= SRC_PAL_LUT;
   const int mv = std::min(a.m, 16);
-  const bool xl = CT == 1 && a.k % 512 == 0 && (size_t)(mv + 1) * xl_stride(a.k) <= (size_t)kXlMaxBytes;
+  const bool xl = CT == 1 && a.k % 512 == 0 && (size_t)mv * xl_stride(a.k) <= (size_t)kXlMaxBytes;
   const bool vs_ok = L.max_tile_verb <= kVexpStageSegs;
   if (pal && vs_ok) return xl ? launch_gemm_u<SRC, CT, CT == 1, 1>(a, L, s) : launch_gemm_u<SRC, CT, 0, 1>(a, L, s);
   return xl ? launch_gemm_u<SRC, CT, CT == 1, 0>(a, L, s) : launch_gemm_u<SRC, CT, 0, 0>(a, L, s);
