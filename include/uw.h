@@ -150,8 +150,14 @@ uw_status uw_dmat_bind(uw_dmat* d, const void* blob_host, size_t bytes, const vo
 uw_status uw_dmat_get_info(const uw_dmat* d, uw_info* out);
 
 /* Workspace bytes a call needs.  op: a UW_PIPE_* value for uw_gemm, or one of the decode
- * targets below.  The first 256 bytes hold the error word; they must be zero before the first
- * use (uw_check clears the word again). */
+ * targets below.  Layout: [256 bytes: error word][decoded matrix, decode pipelines only]
+ * [fp32 K-slice partial sums of the multi-tile kernel: up to 16 slices of m x n].
+ * The first 256 bytes must be zero before the first use (uw_check clears the word again); the
+ * rest needs no initialisation.  One workspace may serve any sequence of calls (any matrix, m,
+ * pipeline) issued in order on one stream; calls that may overlap need workspaces of their own.
+ * The partial-sum room is optional: uw_gemm uses as many K slices as the room it is given holds
+ * (none with ws NULL or only the error word), which changes speed and the fp32 summation order
+ * (results stay within the GEMM tolerance; the same room gives bit-identical results). */
 enum { UW_OP_DECODE_FULL = 16, UW_OP_TRANSCODE = 17, UW_OP_DECODE_EXP = 18 };
 uw_status uw_workspace_size(const uw_dmat* d, int32_t m, int32_t op, size_t* bytes);
 
@@ -174,7 +180,9 @@ uw_status uw_decode_exponents(const uw_dmat* d, uint8_t* exp_out, void* ws, size
  * x: device [m, k] BF16; y: device [m, n] fp32; 1 <= m <= UW_MAX_M.
  * pipeline: UW_PIPE_AUTO..UW_PIPE_DIRECT_PALETTE; variant: kernel variant id (uw_variant_count),
  * -1 = the autotune table's variant for (n, k, m, pipeline), else the built-in default.
- * ws: workspace of uw_workspace_size(d, m, pipeline) bytes (may be NULL when that size is 0).
+ * ws: workspace of uw_workspace_size(d, m, pipeline) bytes.  The direct-palette pipeline also
+ * accepts NULL or less (fewer K slices, see uw_workspace_size); the decode pipelines need at
+ * least the error word and their decoded matrix, else UW_E_WORKSPACE.
  * Errors: UW_E_ARG, UW_E_SHAPE, UW_E_WORKSPACE, UW_E_HIP. */
 uw_status uw_gemm(const uw_dmat* d, const uint16_t* x, float* y, int32_t m, int32_t pipeline,
                   void* ws, size_t ws_bytes, hipStream_t s);
