@@ -43,6 +43,15 @@ def student_t_bf16(rng, shape, df, scale):
     return f32_to_bf16_bits(rng.standard_t(df, size=shape).astype(np.float32) * np.float32(scale))
 
 
+def subnormal_bf16(rng, shape):
+    """Edge case: BF16 bit patterns with exponent field 0 (zeros and subnormals, 70 %) or the two
+    smallest normal exponents 1 and 2; random sign and mantissa."""
+    e = rng.choice(np.array([0, 1, 2], np.uint16), size=shape, p=[0.7, 0.2, 0.1])
+    m = rng.integers(0, 128, size=shape).astype(np.uint16)
+    s = rng.integers(0, 2, size=shape).astype(np.uint16)
+    return (s << 15) | (e << 7) | m
+
+
 def plant_outliers(rng, w, frac):
     """Give max(1, round(frac*N)) distinct rows one value of +-2**(+-20); returns the rows."""
     n, k = w.shape

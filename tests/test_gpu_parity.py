@@ -54,6 +54,8 @@ CASES = {
     "all_verbatim_20x128": lambda: every_segment_verbatim(20, 128, 8),
     "single_exponent_16x128": lambda: np.full((16, 128), 0x3F80, np.uint16) | (np.arange(128, dtype=np.uint16)[None, :] & 0x7F),
     "bimodal_lut_96x512": lambda: bimodal(96, 512, 6),
+    "all_zero_32x128": lambda: np.zeros((32, 128), np.uint16),
+    "subnormal_48x256": lambda: synth.subnormal_bf16(np.random.default_rng(7), (48, 256)),
 }
 
 

@@ -45,6 +45,8 @@ CASES = [
     ("one_row", lambda: synth.small_gaussian(1, 64, seed=3)["w"]),
     ("student_t", lambda: synth.student_t_bf16(np.random.default_rng(5), (48, 1024), 3, 0.02)),
     ("uniform_bits", lambda: np.random.default_rng(6).integers(0, 65536, size=(33, 320)).astype(np.uint16)),
+    ("all_zero", lambda: np.zeros((32, 128), np.uint16)),
+    ("subnormal", lambda: synth.subnormal_bf16(np.random.default_rng(7), (48, 256))),
 ]
 
 
