@@ -19,6 +19,7 @@ import hashlib
 import json
 import os
 import re
+import subprocess
 import sys
 import time
 
@@ -55,6 +56,25 @@ def traffic_from_profile():
     if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
         return None
     return float(m_bytes.group(1))
+
+
+def device_info():
+    """GPU name and clocks as rocm-smi reports them (queried in a child process before this process
+    touches the GPU), and the host CPU model; fields are None where a query fails."""
+    info = {"gpu": None, "clocks": None, "cpu_model": None}
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
+        lines = [ln.strip() for ln in r.stdout.splitlines() if re.search(r"(sclk|mclk|fclk).*Mhz", ln, re.I)]
+        info["clocks"] = lines[:6] or None
+    except Exception:
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            m = re.search(r"^model name\s*:\s*(.+)$", f.read(), re.M)
+        info["cpu_model"] = m.group(1).strip() if m else None
+    except OSError:
+        pass
+    return info
 
 
 def cpu_baseline(w, x, seconds=10.0):
@@ -256,6 +276,7 @@ def main():
         print(json.dumps(diagnostic(args)), flush=True)
         return
 
+    dinfo = device_info()   # before the GPU is initialised here
     import torch
     import lossless_bf16_weight_amd as uw
     from lossless_bf16_weight_amd import autotune, synth
@@ -263,6 +284,7 @@ def main():
 
     assert torch.cuda.is_available(), "no GPU"
     dev = torch.device("cuda:0")
+    dinfo["gpu"] = "%s (%s)" % (torch.cuda.get_device_name(0), torch.cuda.get_device_properties(0).gcnArchName)
     stream = torch.cuda.current_stream()
     t0 = time.time()
     c = synth.config2()
@@ -374,6 +396,7 @@ def main():
         "speedup_vs_best_bf16": round(best_bf16_us / us, 4),
         "load_time_transcode_us": round(1e3 * float(np.median(t_tc)), 2),
         "host_encode_s": round(enc_s, 3),
+        "device": dinfo,
     }
     print(json.dumps(out), flush=True)
 
