@@ -116,15 +116,6 @@ def _check(status):
         raise UwError(status, lib().uw_last_error().decode(errors="replace"))
 
 
-def _ptr(t):
-    """Device or host address of a torch tensor or numpy array (None -> NULL)."""
-    if t is None:
-        return None
-    if isinstance(t, np.ndarray):
-        return t.ctypes.data
-    return t.data_ptr()
-
-
 def _stream(stream):
     import torch
     s = stream if stream is not None else torch.cuda.current_stream()
@@ -133,6 +124,27 @@ def _stream(stream):
 
 def _nbytes(t):
     return 0 if t is None else t.numel() * t.element_size()
+
+
+def _dev(t, name, min_bytes, dtypes=None, optional=False):
+    """Device address of a contiguous CUDA tensor holding at least min_bytes (the C ABI takes
+    raw pointers it cannot bound-check, so a wrong buffer is refused here, not faulted on)."""
+    if t is None:
+        if optional:
+            return None
+        raise ValueError("%s: a CUDA tensor is required" % name)
+    if isinstance(t, np.ndarray) or not getattr(t, "is_cuda", False):
+        raise ValueError("%s: must be a CUDA tensor (got %s)" % (name, type(t).__name__))
+    if not t.is_contiguous():
+        raise ValueError("%s: must be contiguous" % name)
+    if dtypes is not None and str(t.dtype).replace("torch.", "") not in dtypes:
+        raise ValueError("%s: dtype %s, expected one of %s" % (name, t.dtype, "/".join(dtypes)))
+    if _nbytes(t) < min_bytes:
+        raise ValueError("%s: %d bytes, the call needs at least %d" % (name, _nbytes(t), min_bytes))
+    return t.data_ptr()
+
+
+_U16 = ("int16", "uint16", "bfloat16")
 
 
 # ----------------------------------------------------------------------------------------
@@ -178,15 +190,18 @@ def uw_blob_info(blob):
 # Device view and kernels
 # ----------------------------------------------------------------------------------------
 class DMat:
-    """A bound uw_dmat plus the tensors it borrows (kept alive here)."""
+    """A bound uw_dmat plus the tensors it borrows (kept alive here).  blob_dev: a device copy
+    of the whole host blob; idx_dev: the direct-palette index stream (info idx_bytes) or None."""
 
     def __init__(self, blob_host, blob_dev, idx_dev=None):
         self.buf = ctypes.create_string_buffer(lib().uw_dmat_size())
         self.blob_host = np.ascontiguousarray(blob_host, dtype=np.uint8)
+        info = uw_blob_info(self.blob_host)
         self.blob_dev = blob_dev
         self.idx = idx_dev
-        _check(lib().uw_dmat_bind(self.buf, self.blob_host.ctypes.data, self.blob_host.size, _ptr(blob_dev),
-                                  _ptr(idx_dev)))
+        _check(lib().uw_dmat_bind(self.buf, self.blob_host.ctypes.data, self.blob_host.size,
+                                  _dev(blob_dev, "blob_dev", self.blob_host.size),
+                                  _dev(idx_dev, "idx_dev", int(info["idx_bytes"]), optional=True)))
         info = Info()
         _check(lib().uw_dmat_get_info(self.buf, ctypes.byref(info)))
         self.info = info.as_dict()
@@ -207,29 +222,43 @@ def uw_workspace_size(d, m, op):
 
 
 def uw_decode_full(d, w_out, ws, stream=None):
-    _check(lib().uw_decode_full(d.handle, _ptr(w_out), _ptr(ws), _nbytes(ws), _stream(stream)))
+    n, k = int(d.info["n"]), int(d.info["k"])
+    _check(lib().uw_decode_full(d.handle, _dev(w_out, "w_out", 2 * n * k), _dev(ws, "ws", 0, optional=True),
+                                _nbytes(ws), _stream(stream)))
 
 
 def uw_transcode_palette(d, idx_out, ws, stream=None):
-    _check(lib().uw_transcode_palette(d.handle, _ptr(idx_out), _ptr(ws), _nbytes(ws), _stream(stream)))
+    _check(lib().uw_transcode_palette(d.handle, _dev(idx_out, "idx_out", int(d.info["idx_bytes"])),
+                                      _dev(ws, "ws", 0, optional=True), _nbytes(ws), _stream(stream)))
 
 
 def uw_decode_exponents(d, exp_out, ws, stream=None):
-    _check(lib().uw_decode_exponents(d.handle, _ptr(exp_out), _ptr(ws), _nbytes(ws), _stream(stream)))
+    need = int(d.info["np"]) * int(d.info["k"])
+    _check(lib().uw_decode_exponents(d.handle, _dev(exp_out, "exp_out", need), _dev(ws, "ws", 0, optional=True),
+                                     _nbytes(ws), _stream(stream)))
+
+
+def _gemm_ptrs(n, k, x, y, m, ws):
+    mm = int(m) if 1 <= int(m) <= UW_MAX_M else 0   # other m: the library refuses them (UW_E_SHAPE)
+    return (_dev(x, "x", 2 * mm * k, _U16), _dev(y, "y", 4 * mm * n, ("float32",)),
+            _dev(ws, "ws", 0, optional=True))
 
 
 def uw_gemm(d, x, y, m, pipeline=UW_PIPE_AUTO, ws=None, stream=None):
-    _check(lib().uw_gemm(d.handle, _ptr(x), _ptr(y), m, pipeline, _ptr(ws), _nbytes(ws), _stream(stream)))
+    px, py, pw = _gemm_ptrs(int(d.info["n"]), int(d.info["k"]), x, y, m, ws)
+    _check(lib().uw_gemm(d.handle, px, py, m, pipeline, pw, _nbytes(ws), _stream(stream)))
 
 
 def uw_gemm_variant(d, x, y, m, pipeline, variant, ws=None, stream=None):
-    _check(lib().uw_gemm_variant(d.handle, _ptr(x), _ptr(y), m, pipeline, variant, _ptr(ws), _nbytes(ws),
-                                 _stream(stream)))
+    px, py, pw = _gemm_ptrs(int(d.info["n"]), int(d.info["k"]), x, y, m, ws)
+    _check(lib().uw_gemm_variant(d.handle, px, py, m, pipeline, variant, pw, _nbytes(ws), _stream(stream)))
 
 
 def uw_gemm_bf16(w, x, y, m, variant=-1, stream=None):
     n, k = w.shape
-    _check(lib().uw_gemm_bf16(_ptr(w), n, k, _ptr(x), _ptr(y), m, variant, _stream(stream)))
+    pw = _dev(w, "w", 2 * n * k, _U16)
+    px, py, _ = _gemm_ptrs(n, k, x, y, m, None)
+    _check(lib().uw_gemm_bf16(pw, n, k, px, py, m, variant, _stream(stream)))
 
 
 def uw_variant_count():
@@ -241,7 +270,7 @@ def uw_variant_name(v):
 
 
 def uw_check(ws, stream=None):
-    _check(lib().uw_check(_ptr(ws), _stream(stream)))
+    _check(lib().uw_check(_dev(ws, "ws", 0, optional=True), _stream(stream)))
 
 
 def uw_autotune_load(path):
@@ -273,12 +302,17 @@ def uw_autotune_clear():
 
 
 def uw_swiglu(g, u, h, stream=None):
-    _check(lib().uw_swiglu(_ptr(g), _ptr(u), _ptr(h), g.numel(), _stream(stream)))
+    """h = bf16(silu(g) * u); g, u fp32, h BF16 bits (int16), all of g.numel() elements."""
+    count = g.numel()
+    _check(lib().uw_swiglu(_dev(g, "g", 4 * count, ("float32",)), _dev(u, "u", 4 * count, ("float32",)),
+                           _dev(h, "h", 2 * count, _U16), count, _stream(stream)))
 
 
 def uw_rmsnorm(y, x, eps=1e-5, stream=None):
+    """x = bf16(y / sqrt(mean(y^2, rows) + eps)); y fp32 [m, n], x BF16 bits [m, n]."""
     m, n = y.shape
-    _check(lib().uw_rmsnorm(_ptr(y), _ptr(x), m, n, eps, _stream(stream)))
+    _check(lib().uw_rmsnorm(_dev(y, "y", 4 * m * n, ("float32",)), _dev(x, "x", 2 * m * n, _U16), m, n, eps,
+                            _stream(stream)))
 
 
 # ----------------------------------------------------------------------------------------
@@ -301,6 +335,7 @@ class CompressedMatrix:
         self._ws = {}
         if keep_index:
             uw_transcode_palette(self.d, self.idx, self.err)
+            uw_check(self.err)   # load time: a corrupt bitstream is reported here
 
     def workspace(self, m, pipeline):
         """A zeroed workspace of uw_workspace_size bytes (error word, decoded operand of

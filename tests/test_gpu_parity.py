@@ -288,6 +288,33 @@ def test_argument_errors_launch_nothing():
     assert ei.value.status == uw.UW_E_ARG
 
 
+def test_binding_refuses_wrong_buffers():
+    """Short, non-contiguous or wrongly typed device buffers are refused by the binding
+    (ValueError) before a kernel could read or write past them."""
+    t = torch()
+    w = synth.small_gaussian(32, 128, seed=1)["w"]
+    cm = uw.CompressedMatrix(w)
+    x = dev_u16(synth.gaussian_bf16(np.random.default_rng(1), (4, 128), 1.0))
+    y = t.empty((4, 32), dtype=t.float32, device="cuda")
+    with pytest.raises(ValueError, match="needs at least"):
+        uw.uw_gemm(cm.d, x, y[:2], 4, uw.UW_PIPE_DIRECT_PALETTE)             # y too short for m = 4
+    with pytest.raises(ValueError, match="needs at least"):
+        uw.uw_gemm(cm.d, x[:1], y, 4, uw.UW_PIPE_DIRECT_PALETTE)             # x too short
+    with pytest.raises(ValueError, match="contiguous"):
+        uw.uw_gemm(cm.d, x, t.empty((32, 4), dtype=t.float32, device="cuda").t(), 4, uw.UW_PIPE_DIRECT_PALETTE)
+    with pytest.raises(ValueError, match="dtype"):
+        uw.uw_gemm(cm.d, x.float(), y, 4, uw.UW_PIPE_DIRECT_PALETTE)
+    with pytest.raises(ValueError, match="needs at least"):
+        uw.uw_decode_full(cm.d, t.empty((16, 128), dtype=t.int16, device="cuda"), err_ws())
+    with pytest.raises(ValueError, match="needs at least"):
+        uw.DMat(cm.blob, cm.blob_dev[:100])
+    with pytest.raises(ValueError, match="needs at least"):
+        uw.uw_swiglu(t.zeros(64, device="cuda"), t.zeros(32, device="cuda"), t.zeros(64, dtype=t.int16, device="cuda"))
+    # the right buffers still work after the refusals
+    uw.uw_gemm(cm.d, x, y, 4, uw.UW_PIPE_DIRECT_PALETTE)
+    check_gemm(y, host_u16(x), w)
+
+
 def test_glue_kernels():
     t = torch()
     rng = np.random.default_rng(4)

@@ -207,3 +207,23 @@ def test_variant_names():
     assert all(uw.uw_variant_name(v).startswith(("waves=", "multitile ")) for v in range(n))
     assert any(uw.uw_variant_name(v).startswith("multitile ") for v in range(n))
     assert uw.uw_variant_name(n) == ""
+
+
+def test_binding_refuses_host_buffers():
+    """Device entry points take raw pointers the library cannot bound-check: the binding
+    refuses host arrays and CPU tensors before anything reaches the C ABI."""
+    import torch
+    w = synth.small_gaussian(32, 128, seed=1)["w"]
+    blob = uw.uw_encode(w)
+    with pytest.raises(ValueError, match="CUDA tensor"):
+        uw.DMat(blob, blob)                       # numpy "device" copy
+    with pytest.raises(ValueError, match="CUDA tensor"):
+        uw.DMat(blob, torch.from_numpy(blob))     # CPU tensor
+    g = torch.zeros(16, dtype=torch.float32)
+    with pytest.raises(ValueError, match="CUDA tensor"):
+        uw.uw_swiglu(g, g, torch.zeros(16, dtype=torch.int16))
+    with pytest.raises(ValueError, match="CUDA tensor"):
+        uw.uw_rmsnorm(torch.zeros((2, 8), dtype=torch.float32), torch.zeros((2, 8), dtype=torch.int16))
+    with pytest.raises(ValueError, match="CUDA tensor"):
+        uw.uw_gemm_bf16(torch.zeros((16, 64), dtype=torch.int16), torch.zeros((1, 64), dtype=torch.int16),
+                        torch.zeros((1, 16), dtype=torch.float32), 1)
