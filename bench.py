@@ -159,8 +159,8 @@ def diagnostic(args):
     steps, warmup = min(args.steps, 200), min(args.warmup, 20)
     if args.workload == "stack":
         return stack_step(args, steps, warmup)
-    c = synth.config3() if args.workload == "down" else synth.config5()
-    ms = (1, 8, 16, 32, 64) if args.workload == "down" else (128,)
+    c = {"down": synth.config3, "heavy": synth.config5, "small": synth.config1}[args.workload]()
+    ms = {"down": (1, 8, 16, 32, 64), "heavy": (128,), "small": (1,)}[args.workload]
     w, x_all = c["w"], c["x"]
     n, k = w.shape
     tuner = autotune.Tuner(w, rotate_bytes=ROTATE_BYTES)
@@ -193,8 +193,22 @@ def diagnostic(args):
                     "own_bf16_us": round(bf.us, 3) if bf else None,
                     "speedup_vs_torch_bf16": round(torch_us[m] / us, 3)})
         log("m=%d: %s" % (m, res[-1]))
-    return {"diagnostic": args.workload, "n": n, "k": k, "bits_per_weight": round(8 * resident / (n * k), 4),
-            "results": res}
+    out = {"diagnostic": args.workload, "n": n, "k": k, "bits_per_weight": round(8 * resident / (n * k), 4),
+           "results": res}
+    if args.workload == "small":
+        # The 1024^2 case is launch/L2 sized (1.6 MB): microseconds only, no roofline claim.
+        err = torch.zeros(64, dtype=torch.int32, device="cuda")
+        wout = torch.empty((n, k), dtype=torch.int16, device="cuda")
+        idx = [m_.idx for m_ in tuner.mats]
+        tot, _ = time_launches(lambda i: uw.uw_transcode_palette(tuner.mats[i], idx[i], err), tuner.copies,
+                               steps, warmup, torch.cuda.current_stream())
+        out["transcode_us"] = round(tot * 1e3 / steps, 3)
+        tot, _ = time_launches(lambda i: uw.uw_decode_full(tuner.mats[i], wout, err), tuner.copies, steps, warmup,
+                               torch.cuda.current_stream())
+        out["decode_full_us"] = round(tot * 1e3 / steps, 3)
+        uw.uw_check(err)
+        assert np.array_equal(wout.cpu().numpy().view(np.uint16), w), "decode not bit-exact"
+    return out
 
 
 def stack_step(args, steps, warmup):
@@ -255,9 +269,10 @@ def main():
     ap.add_argument("--variant", type=int, default=-1, help="fused-kernel variant id (default: autotuned)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run three device copies of 512 MiB (HBM counter calibration) and exit")
-    ap.add_argument("--workload", default="gate", choices=("gate", "down", "heavy", "stack"),
-                    help="gate (default: the headline line); down, heavy, stack: diagnostic lines for the "
-                         "down_proj batch sweep, the 8192^2 heavy-tail matrix at M=128 and the 32-layer stack")
+    ap.add_argument("--workload", default="gate", choices=("gate", "down", "heavy", "stack", "small"),
+                    help="gate (default: the headline line); down, heavy, stack, small: diagnostic lines for the "
+                         "down_proj batch sweep, the 8192^2 heavy-tail matrix at M=128, the 32-layer stack and "
+                         "the 1024^2 single-matrix case")
     args = ap.parse_args()
     if args.copy_calibration:
         import torch
