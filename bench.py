@@ -235,6 +235,14 @@ def stack_step(args, steps, warmup):
                 st.add_layer(*pending)
                 pending = []
     log("stack built in %.1fs" % (time.time() - t0))
+    # Kernel variant per matrix shape at M = 16 chosen by measurement (the library's autotuner,
+    # once, as an engine would at load time); gate and up share a shape.
+    from lossless_bf16_weight_amd import autotune
+    for lj in ((0, 0), (0, 2)):
+        tuner = autotune.Tuner(synth.config4_matrix(meta, *lj), bf16=False)
+        tuner.tune([16], pipelines=(uw.UW_PIPE_DIRECT_PALETTE,), bf16=False, log=log).apply()
+        del tuner
+    torch.cuda.empty_cache()
     x = torch.from_numpy(meta["x"].view(np.int16)).cuda()
     step = lambda i: st.step(x, pipeline=uw.UW_PIPE_DIRECT_PALETTE, check=False)
     tot, _ = time_launches(step, 1, steps, warmup, torch.cuda.current_stream())

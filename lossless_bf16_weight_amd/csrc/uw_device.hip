@@ -1114,10 +1114,52 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float v) {
   return (uint16_t)(b >> 16);
 }
 
+__device__ __forceinline__ uint16_t swiglu1(float gv, float uv) { return f32_to_bf16(gv / (1.0f + expf(-gv)) * uv); }
+
 __global__ void k_swiglu(const float* g, const float* u, uint16_t* h, int64_t count) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += (int64_t)gridDim.x * blockDim.x) {
-    const float gv = g[i];
-    h[i] = f32_to_bf16(gv / (1.0f + expf(-gv)) * u[i]);
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += (int64_t)gridDim.x * blockDim.x)
+    h[i] = swiglu1(g[i], u[i]);
+}
+
+// Four elements a thread (count % 4 == 0, 16-byte aligned g and u, 8-byte aligned h).
+__global__ void k_swiglu4(const floatx4* g, const floatx4* u, u32x2* h, int64_t count4) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count4; i += (int64_t)gridDim.x * blockDim.x) {
+    const floatx4 gv = g[i], uv = u[i];
+    h[i] = u32x2{(uint32_t)swiglu1(gv[0], uv[0]) | ((uint32_t)swiglu1(gv[1], uv[1]) << 16),
+                 (uint32_t)swiglu1(gv[2], uv[2]) | ((uint32_t)swiglu1(gv[3], uv[3]) << 16)};
+  }
+}
+
+// One 1024-thread workgroup a row, V float4 vectors a thread held in registers between the
+// sum of squares and the scaling (n % 4 == 0, n <= 4096 * V).  Fixed reduction order: each
+// thread's vectors in order, a butterfly inside each wave, then the 16 wave sums in order.
+template <int V>
+__global__ __launch_bounds__(1024) void k_rmsnorm_v(const float* y, uint16_t* x, int n, float eps) {
+  __shared__ float part[16];
+  const floatx4* yr = reinterpret_cast<const floatx4*>(y + (size_t)blockIdx.x * n);
+  u32x2* xr = reinterpret_cast<u32x2*>(x + (size_t)blockIdx.x * n);
+  const int n4 = n >> 2;
+  floatx4 v[V];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const int i = (int)threadIdx.x + j * 1024;
+    v[j] = i < n4 ? yr[i] : floatx4{0.f, 0.f, 0.f, 0.f};
+    ss += v[j][0] * v[j][0] + v[j][1] * v[j][1] + v[j][2] * v[j][2] + v[j][3] * v[j][3];
+  }
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) tot += part[w];
+  const float scale = 1.0f / sqrtf(tot / (float)n + eps);
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const int i = (int)threadIdx.x + j * 1024;
+    if (i < n4)
+      xr[i] = u32x2{(uint32_t)f32_to_bf16(v[j][0] * scale) | ((uint32_t)f32_to_bf16(v[j][1] * scale) << 16),
+                    (uint32_t)f32_to_bf16(v[j][2] * scale) | ((uint32_t)f32_to_bf16(v[j][3] * scale) << 16)};
   }
 }
 
@@ -1647,8 +1689,15 @@ uw_status uw_check(void* ws, hipStream_t s) {
 uw_status uw_swiglu(const float* g, const float* u, uint16_t* h, int64_t count, hipStream_t s) {
   if (!g || !u || !h || count < 0) return fail(UW_E_ARG, "bad argument");
   if (count == 0) return UW_OK;
-  const int64_t blocks = std::min<int64_t>((count + 255) / 256, 4096);
-  hipLaunchKernelGGL(k_swiglu, dim3((unsigned)blocks), dim3(256), 0, s, g, u, h, count);
+  const bool vec = count % 4 == 0 && reinterpret_cast<uintptr_t>(g) % 16 == 0 && reinterpret_cast<uintptr_t>(u) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(h) % 8 == 0;
+  const int64_t items = vec ? count / 4 : count;
+  const int64_t blocks = std::min<int64_t>((items + 255) / 256, 4096);
+  if (vec)
+    hipLaunchKernelGGL(k_swiglu4, dim3((unsigned)blocks), dim3(256), 0, s, reinterpret_cast<const floatx4*>(g),
+                       reinterpret_cast<const floatx4*>(u), reinterpret_cast<u32x2*>(h), items);
+  else
+    hipLaunchKernelGGL(k_swiglu, dim3((unsigned)blocks), dim3(256), 0, s, g, u, h, count);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(UW_E_HIP, "swiglu launch: %s", hipGetErrorString(e));
   clear_error();
@@ -1657,7 +1706,16 @@ uw_status uw_swiglu(const float* g, const float* u, uint16_t* h, int64_t count, 
 
 uw_status uw_rmsnorm(const float* y, uint16_t* x, int32_t m, int32_t n, float eps, hipStream_t s) {
   if (!y || !x || m < 1 || n < 1) return fail(UW_E_ARG, "bad argument");
-  hipLaunchKernelGGL(k_rmsnorm, dim3((unsigned)m), dim3(256), 0, s, y, x, n, eps);
+  const bool vec = n % 4 == 0 && n <= 4 * 4096 && reinterpret_cast<uintptr_t>(y) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(x) % 8 == 0;
+  if (vec && n <= 4096)
+    hipLaunchKernelGGL((k_rmsnorm_v<1>), dim3((unsigned)m), dim3(1024), 0, s, y, x, n, eps);
+  else if (vec && n <= 8192)
+    hipLaunchKernelGGL((k_rmsnorm_v<2>), dim3((unsigned)m), dim3(1024), 0, s, y, x, n, eps);
+  else if (vec)
+    hipLaunchKernelGGL((k_rmsnorm_v<4>), dim3((unsigned)m), dim3(1024), 0, s, y, x, n, eps);
+  else
+    hipLaunchKernelGGL(k_rmsnorm, dim3((unsigned)m), dim3(256), 0, s, y, x, n, eps);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(UW_E_HIP, "rmsnorm launch: %s", hipGetErrorString(e));
   clear_error();

@@ -315,17 +315,28 @@ def test_binding_refuses_wrong_buffers():
     check_gemm(y, host_u16(x), w)
 
 
-def test_glue_kernels():
+@pytest.mark.parametrize("shape", [(16, 1000), (7, 333), (1, 4)])
+def test_swiglu(shape):
+    """SwiGLU glue within one BF16 ulp of the oracle: the 4-wide path (element count a
+    multiple of 4) and the scalar path."""
     t = torch()
     rng = np.random.default_rng(4)
-    g = (rng.standard_normal((16, 1000)) * 3).astype(np.float32)
-    u = rng.standard_normal((16, 1000)).astype(np.float32)
-    h = t.empty((16, 1000), dtype=t.int16, device="cuda")
+    g = (rng.standard_normal(shape) * 3).astype(np.float32)
+    u = rng.standard_normal(shape).astype(np.float32)
+    h = t.empty(shape, dtype=t.int16, device="cuda")
     uw.uw_swiglu(t.from_numpy(g).cuda(), t.from_numpy(u).cuda(), h)
     ref = gemm.swiglu_ref(g, u).astype(np.int32)
     assert np.abs(host_u16(h).astype(np.int32) - ref).max() <= 1
-    y = (rng.standard_normal((16, 4096)) * 5).astype(np.float32)
-    xo = t.empty((16, 4096), dtype=t.int16, device="cuda")
+
+
+@pytest.mark.parametrize("shape", [(16, 4096), (2, 6000), (2, 12000), (3, 1001), (1, 20000), (5, 4)])
+def test_rmsnorm(shape):
+    """Weightless RMS norm within one BF16 ulp of the oracle: one, two and four vectors a
+    thread, and the scalar kernel (row length not a multiple of 4, or past 16384)."""
+    t = torch()
+    rng = np.random.default_rng(5)
+    y = (rng.standard_normal(shape) * 5).astype(np.float32)
+    xo = t.empty(shape, dtype=t.int16, device="cuda")
     uw.uw_rmsnorm(t.from_numpy(y).cuda(), xo)
     ref = gemm.rmsnorm_ref(y).astype(np.int32)
     assert np.abs(host_u16(xo).astype(np.int32) - ref).max() <= 1
