@@ -226,6 +226,17 @@ uw_status uw_autotune_clear(void);
 /* Glue of an MLP decode step (SwiGLU between up/gate and down):
  * h[i] = bf16(silu(g[i]) * u[i]) in fp32, round to nearest even; count elements. */
 uw_status uw_swiglu(const float* g, const float* u, uint16_t* h, int64_t count, hipStream_t s);
+
+/* The up projection with the SwiGLU glue fused into its output: h = bf16(silu(gate) * (x W^T))
+ * element by element ([m, n]; W = the bound matrix, typically up_proj; gate = the fp32 output
+ * of the gate projection, e.g. from uw_gemm earlier on the same stream).  The GEMM is exactly
+ * uw_gemm_variant's (same kernels, same summation order) and the epilogue the arithmetic of
+ * uw_swiglu, so h equals uw_gemm_variant followed by uw_swiglu bit for bit, without the fp32
+ * product going through memory.  gate: device fp32 [m, n], 16-byte aligned; h: device BF16
+ * bits [m, n], 8-byte aligned.  Other arguments, workspace and errors as uw_gemm_variant. */
+uw_status uw_gemm_swiglu(const uw_dmat* d, const uint16_t* x, const float* gate, uint16_t* h,
+                         int32_t m, int32_t pipeline, int32_t variant, void* ws, size_t ws_bytes,
+                         hipStream_t s);
 /* x[r, :] = bf16(y[r, :] / sqrt(mean(y[r, :]^2) + eps)) for rows r < m of an [m, n] fp32 y. */
 uw_status uw_rmsnorm(const float* y, uint16_t* x, int32_t m, int32_t n, float eps,
                      hipStream_t s);

@@ -35,6 +35,15 @@ namespace uw {
 // where spread(sm) = [sm_lo, sm_lo, sm_hi, sm_hi] bytes puts each sign bit at bit 15 of its
 // half and each mantissa at bits 6..0.
 // =========================================================================================
+// fp32 -> BF16, round to nearest even (finite inputs; the MLP glue's rounding).
+__device__ __forceinline__ uint16_t f32_to_bf16(float v) {
+  uint32_t b = __float_as_uint(v);
+  b += 0x7FFFu + ((b >> 16) & 1u);
+  return (uint16_t)(b >> 16);
+}
+// SwiGLU of one element: bf16(silu(g) * u), silu(g) = g / (1 + e^-g).
+__device__ __forceinline__ uint16_t swiglu1(float gv, float uv) { return f32_to_bf16(gv / (1.0f + expf(-gv)) * uv); }
+
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
@@ -125,13 +134,42 @@ struct GemmArgs {
   const uint32_t* vprefix;
   const uint8_t* vexp;
   const uint16_t* x;
-  float* y;
+  float* y;                 // fp32 output, or unused with the SwiGLU epilogue
+  const float* gate;        // SwiGLU epilogue: h = bf16(silu(gate) * y) replaces y (null: plain y)
+  uint16_t* h;
   int32_t n, k, m, kb;
   int32_t vs_segs;          // per-tile kernel: verbatim segments the LDS stage holds (multiple of 16)
   uint32_t base2;
   uint32_t tab[4];
   uint32_t m0, m1;  // 0x000F000F, 0x00F000F0 (see exps_affine)
 };
+
+// Final output of four consecutive elements of row mm, columns n0..n0+3 (those < n): fp32 Y,
+// or with the SwiGLU epilogue h = bf16(silu(gate) * y) -- the same arithmetic as the separate
+// SwiGLU kernel on the same y, so both routes give identical bits.
+__device__ __forceinline__ void store_out4(const GemmArgs& a, int mm, int n0, floatx4 v) {
+  const size_t o = (size_t)mm * a.n + n0;
+  const bool full = n0 + 3 < a.n && (a.n & 3) == 0;
+  if (a.gate) {
+    if (full) {
+      const floatx4 gv = *reinterpret_cast<const floatx4*>(a.gate + o);
+      *reinterpret_cast<u32x2*>(a.h + o) = u32x2{(uint32_t)swiglu1(gv[0], v[0]) | ((uint32_t)swiglu1(gv[1], v[1]) << 16),
+                                                 (uint32_t)swiglu1(gv[2], v[2]) | ((uint32_t)swiglu1(gv[3], v[3]) << 16)};
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (n0 + j < a.n) a.h[o + j] = swiglu1(a.gate[o + j], v[j]);
+    }
+  } else {
+    if (full) {
+      *reinterpret_cast<floatx4*>(a.y + o) = v;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (n0 + j < a.n) a.y[o + j] = v[j];
+    }
+  }
+}
 
 template <int SRC>
 struct WRegs;
@@ -461,16 +499,7 @@ __global__ __launch_bounds__((MaxThreads<CT, U>::v)) void k_gemm(GemmArgs a) {
   // Epilogue: D lane layout = column m (lane%16), rows 4*(lane/16) + j.
   auto store = [&](int c, int l, floatx4 v) {
     const int mm = mcol0 + 16 * c + (l & 15);
-    if (mm >= a.m) return;
-    const int n0 = t * 16 + 4 * (l >> 4);
-    float* yp = a.y + (size_t)mm * a.n + n0;
-    if (n0 + 3 < a.n && (a.n & 3) == 0) {
-      *reinterpret_cast<floatx4*>(yp) = v;
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (n0 + j < a.n) yp[j] = v[j];
-    }
+    if (mm < a.m) store_out4(a, mm, t * 16 + 4 * (l >> 4), v);
   };
   if (nw == 1) {
 #pragma unroll
@@ -737,13 +766,16 @@ __global__ __launch_bounds__(64 * R) void k_gemm_mt(GemmArgs a, float* part, int
   }
   if (!tile_ok) return;
   // D lane layout: column lane % 16 of column tile c, rows 4 * (lane / 16) + j of the tile.
-  float* dst = part ? part + (size_t)s * a.m * a.n : a.y;
   const int n0 = t * 16 + 4 * g;
 #pragma unroll
   for (int c = 0; c < CT; ++c) {
     const int mm = mcol0 + 16 * c + r;
     if (mm >= a.m) continue;
-    float* yp = dst + (size_t)mm * a.n + n0;
+    if (!part) {  // one K slice: the final output
+      store_out4(a, mm, n0, acc[c]);
+      continue;
+    }
+    float* yp = part + (size_t)s * a.m * a.n + (size_t)mm * a.n + n0;
     if (n0 + 3 < a.n && (a.n & 3) == 0) {
       *reinterpret_cast<floatx4*>(yp) = acc[c];
     } else {
@@ -757,7 +789,9 @@ __global__ __launch_bounds__(64 * R) void k_gemm_mt(GemmArgs a, float* part, int
 // y[i] = sum over s of part[s][i], in slice order.  A thread owns 4 consecutive elements
 // and requests all S slices' values before adding them, so the loads overlap.
 constexpr int kMaxSlices = 16;
-__global__ __launch_bounds__(256) void k_reduce_parts(const float* part, float* y, int S, int64_t count) {
+// With gate set, the sum goes through the SwiGLU epilogue into h instead of y.
+__global__ __launch_bounds__(256) void k_reduce_parts(const float* part, float* y, const float* gate, uint16_t* h,
+                                                      int S, int64_t count) {
   const int64_t n4 = count >> 2;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
     floatx4 v[kMaxSlices];
@@ -768,12 +802,21 @@ __global__ __launch_bounds__(256) void k_reduce_parts(const float* part, float* 
 #pragma unroll
     for (int s = 1; s < kMaxSlices; ++s)
       if (s < S) sum += v[s];
-    reinterpret_cast<floatx4*>(y)[i] = sum;
+    if (gate) {
+      const floatx4 gv = reinterpret_cast<const floatx4*>(gate)[i];
+      reinterpret_cast<u32x2*>(h)[i] = u32x2{(uint32_t)swiglu1(gv[0], sum[0]) | ((uint32_t)swiglu1(gv[1], sum[1]) << 16),
+                                             (uint32_t)swiglu1(gv[2], sum[2]) | ((uint32_t)swiglu1(gv[3], sum[3]) << 16)};
+    } else {
+      reinterpret_cast<floatx4*>(y)[i] = sum;
+    }
   }
   for (int64_t i = (n4 << 2) + (int64_t)blockIdx.x * 256 + threadIdx.x; i < count; i += (int64_t)gridDim.x * 256) {
     float v = part[i];
     for (int s = 1; s < S; ++s) v += part[(size_t)s * count + i];
-    y[i] = v;
+    if (gate)
+      h[i] = swiglu1(gate[i], v);
+    else
+      y[i] = v;
   }
 }
 
@@ -1108,13 +1151,6 @@ __global__ __launch_bounds__(64) void k_decode(DecArgs a) {
 // =========================================================================================
 // MLP glue (SwiGLU between up/gate and down; RMS norm feeding the next layer)
 // =========================================================================================
-__device__ __forceinline__ uint16_t f32_to_bf16(float v) {
-  uint32_t b = __float_as_uint(v);
-  b += 0x7FFFu + ((b >> 16) & 1u);
-  return (uint16_t)(b >> 16);
-}
-
-__device__ __forceinline__ uint16_t swiglu1(float gv, float uv) { return f32_to_bf16(gv / (1.0f + expf(-gv)) * uv); }
 
 __global__ void k_swiglu(const float* g, const float* u, uint16_t* h, int64_t count) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += (int64_t)gridDim.x * blockDim.x)
@@ -1228,7 +1264,7 @@ static hipError_t launch_mt_t(const GemmArgs& a, int64_t tiles, int S, float* pa
   if (e != hipSuccess || S == 1) return e;
   const int64_t count = (int64_t)a.m * a.n;
   const int64_t blocks = std::min<int64_t>((count / 4 + 255) / 256 + 1, 4096);
-  hipLaunchKernelGGL(k_reduce_parts, dim3((unsigned)blocks), dim3(256), 0, s, part, a.y, S, count);
+  hipLaunchKernelGGL(k_reduce_parts, dim3((unsigned)blocks), dim3(256), 0, s, part, a.y, a.gate, a.h, S, count);
   return hipGetLastError();
 }
 
@@ -1570,11 +1606,16 @@ const char* uw_variant_name(int32_t variant) {
   return names[variant];
 }
 
-uw_status uw_gemm_variant(const uw_dmat* d, const uint16_t* x, float* y, int32_t m, int32_t pipeline, int32_t variant,
-                          void* ws, size_t ws_bytes, hipStream_t s) {
+}  // extern "C"
+
+// Shared body of uw_gemm_variant and uw_gemm_swiglu: y (fp32), or h = bf16(silu(gate) * y).
+static uw_status gemm_entry(const uw_dmat* d, const uint16_t* x, float* y, const float* gate, uint16_t* h, int32_t m,
+                            int32_t pipeline, int32_t variant, void* ws, size_t ws_bytes, hipStream_t s) {
   uw_status st = check_dmat(d);
   if (st) return st;
-  if (!x || !y) return fail(UW_E_ARG, "null x or y");
+  if (!x || (gate ? !h : !y)) return fail(UW_E_ARG, gate ? "null x or h" : "null x or y");
+  if (gate && ((reinterpret_cast<uintptr_t>(gate) & 15) || (reinterpret_cast<uintptr_t>(h) & 7)))
+    return fail(UW_E_ARG, "gate must be 16-byte and h 8-byte aligned");
   if (m < 1 || m > UW_MAX_M) return fail(UW_E_SHAPE, "m=%d outside [1, %d]", m, UW_MAX_M);
   if (variant < -1 || variant >= kNumVariants) return fail(UW_E_ARG, "bad variant %d", variant);
   if (pipeline == UW_PIPE_AUTO) {
@@ -1610,7 +1651,10 @@ uw_status uw_gemm_variant(const uw_dmat* d, const uint16_t* x, float* y, int32_t
     part_bytes = ws_bytes - kErrBytes - dec;
   }
   GemmArgs a;
+  std::memset(&a, 0, sizeof(a));
   fill_gemm_args(d, a, x, y, m);
+  a.gate = gate;
+  a.h = h;
   const int pal_src = d->info.affine ? SRC_PAL_AFFINE : SRC_PAL_LUT;
   const int vs = d->max_tile_verb;
   switch (pipeline) {
@@ -1642,9 +1686,22 @@ uw_status uw_gemm_variant(const uw_dmat* d, const uint16_t* x, float* y, int32_t
   return st;
 }
 
+extern "C" {
+
+uw_status uw_gemm_variant(const uw_dmat* d, const uint16_t* x, float* y, int32_t m, int32_t pipeline, int32_t variant,
+                          void* ws, size_t ws_bytes, hipStream_t s) {
+  return gemm_entry(d, x, y, nullptr, nullptr, m, pipeline, variant, ws, ws_bytes, s);
+}
+
 uw_status uw_gemm(const uw_dmat* d, const uint16_t* x, float* y, int32_t m, int32_t pipeline, void* ws, size_t ws_bytes,
                   hipStream_t s) {
-  return uw_gemm_variant(d, x, y, m, pipeline, -1, ws, ws_bytes, s);
+  return gemm_entry(d, x, y, nullptr, nullptr, m, pipeline, -1, ws, ws_bytes, s);
+}
+
+uw_status uw_gemm_swiglu(const uw_dmat* d, const uint16_t* x, const float* gate, uint16_t* h, int32_t m,
+                         int32_t pipeline, int32_t variant, void* ws, size_t ws_bytes, hipStream_t s) {
+  if (!gate) return fail(UW_E_ARG, "null gate");
+  return gemm_entry(d, x, nullptr, gate, h, m, pipeline, variant, ws, ws_bytes, s);
 }
 
 uw_status uw_gemm_bf16(const uint16_t* w, int64_t n, int64_t k, const uint16_t* x, float* y, int32_t m, int32_t variant,

@@ -2,7 +2,8 @@
 
 Per layer l with input x_l [m, hidden] (BF16):
     g = x_l gate^T, u = x_l up^T        (fused reconstruct GEMMs, fp32 out)
-    h = bf16(silu(g) * u)               (SwiGLU, uw_swiglu)
+    h = bf16(silu(g) * u)               (SwiGLU: in the up GEMM's epilogue, uw_gemm_swiglu;
+                                         or uw_gemm + uw_swiglu when u itself is wanted)
     y = h down^T                        (fused reconstruct GEMM, fp32 out)
     x_{l+1} = bf16(y / sqrt(mean(y^2) + eps))   (weightless RMS norm, uw_rmsnorm)
 
@@ -15,7 +16,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import UW_PIPE_AUTO, CompressedMatrix, uw_check, uw_gemm, uw_rmsnorm, uw_swiglu, uw_workspace_size
+from . import (UW_PIPE_AUTO, CompressedMatrix, uw_check, uw_gemm, uw_gemm_swiglu, uw_rmsnorm, uw_swiglu,
+               uw_workspace_size)
 
 
 class MLPStack:
@@ -52,19 +54,26 @@ class MLPStack:
             self.ws_bytes = need
         return self.ws if need else None
 
-    def step(self, x, pipeline=UW_PIPE_AUTO, trace=None, check=True):
+    def step(self, x, pipeline=UW_PIPE_AUTO, trace=None, check=True, fused=None):
         """x: device int16 [m, hidden] (BF16 bits).  Returns the device tensor holding the last
         layer's output (one of two ping-pong buffers).  trace: optional list that receives,
         per layer, host copies (x_in, g, u, h, y, x_out) -- for tests; it synchronises.
         check: wait for the step and report a corrupt stream found by a decode pipeline
-        (UwError); pass False to keep the step asynchronous."""
+        (UwError); pass False to keep the step asynchronous.  fused: SwiGLU in the up GEMM's
+        epilogue (default unless tracing, which needs u itself); the outputs are identical."""
+        fused = trace is None if fused is None else fused
+        if fused and trace is not None:
+            raise ValueError("a traced step needs u: use fused=False")
         ws = self._workspace(pipeline)
         cur = x
         for i, (gate, up, down) in enumerate(self.layers):
             out = self.xs[i % 2]
             uw_gemm(gate.d, cur, self.g, self.m, pipeline, ws)
-            uw_gemm(up.d, cur, self.u, self.m, pipeline, ws)
-            uw_swiglu(self.g, self.u, self.h)
+            if fused:
+                uw_gemm_swiglu(up.d, cur, self.g, self.h, self.m, pipeline, -1, ws)
+            else:
+                uw_gemm(up.d, cur, self.u, self.m, pipeline, ws)
+                uw_swiglu(self.g, self.u, self.h)
             uw_gemm(down.d, self.h, self.y, self.m, pipeline, ws)
             uw_rmsnorm(self.y, out, self.eps)
             if trace is not None:

@@ -190,3 +190,6 @@ def test_c4_stack_step(stack4):
             assert np.abs(xo.astype(np.int32) - gemm.rmsnorm_ref(y).astype(np.int32)).max() <= 1
             assert np.isfinite(y).all()
         log("c4 pipeline %d: 32 layers, 96 GEMMs + glue within bound" % pipe)
+        fused = st.step(x, pipeline=pipe, fused=True)   # SwiGLU in the up GEMM's epilogue
+        assert np.array_equal(as_bf16_bits(fused), as_bf16_bits(trace[-1][5])), "fused step differs"
+        log("c4 pipeline %d: fused step bit-identical" % pipe)

@@ -340,3 +340,55 @@ def test_rmsnorm(shape):
     uw.uw_rmsnorm(t.from_numpy(y).cuda(), xo)
     ref = gemm.rmsnorm_ref(y).astype(np.int32)
     assert np.abs(host_u16(xo).astype(np.int32) - ref).max() <= 1
+
+
+@pytest.mark.parametrize("name", ["ragged_37x192", "tiles_160x1024", "bimodal_lut_96x512"])
+def test_gemm_swiglu_equals_unfused(name):
+    """uw_gemm_swiglu gives exactly uw_gemm_variant then uw_swiglu: every variant and pipeline,
+    per-tile and multi-tile kernels, with the K-slice reduction (workspace) and without."""
+    t = torch()
+    w = CASES[name]()
+    n, k = w.shape
+    cm = uw.CompressedMatrix(w)
+    rng = np.random.default_rng(11)
+    for m in (1, 5, 16, 17, 40, 128):
+        x = dev_u16(synth.gaussian_bf16(rng, (m, k), 1.0))
+        gate = t.from_numpy((rng.standard_normal((m, n)) * 2).astype(np.float32)).cuda()
+        y = t.empty((m, n), dtype=t.float32, device="cuda")
+        h_ref = t.empty((m, n), dtype=t.int16, device="cuda")
+        h = t.empty((m, n), dtype=t.int16, device="cuda")
+        for pipe in ALL_PIPES:
+            ws_full = cm.workspace(m, pipe)
+            variants = range(N_VARIANTS) if pipe == uw.UW_PIPE_DIRECT_PALETTE else (-1,)
+            for variant in variants:
+                for ws in ((ws_full, None) if pipe == uw.UW_PIPE_DIRECT_PALETTE else (ws_full,)):
+                    uw.uw_gemm_variant(cm.d, x, y, m, pipe, variant, ws)
+                    uw.uw_swiglu(gate, y, h_ref)
+                    h.fill_(0x7FFF)
+                    uw.uw_gemm_swiglu(cm.d, x, gate, h, m, pipe, variant, ws)
+                    assert t.equal(h, h_ref), "m=%d pipeline %d variant %d ws %s" % (
+                        m, pipe, variant, "yes" if ws is not None else "no")
+        if m == 1:
+            check_gemm(y, host_u16(x), w)
+    x1 = dev_u16(synth.gaussian_bf16(rng, (1, k), 1.0))
+    g1 = t.zeros(n + 4, dtype=t.float32, device="cuda")
+    with pytest.raises(uw.UwError) as ei:   # gate must be 16-byte aligned
+        uw.uw_gemm_swiglu(cm.d, x1, g1[1:], h, 1, uw.UW_PIPE_DIRECT_PALETTE)
+    assert ei.value.status == uw.UW_E_ARG
+
+
+def test_stack_fused_equals_unfused():
+    """A two-layer MLP stack: the fused step (SwiGLU in the up GEMM's epilogue) ends in the
+    same bits as the unfused one."""
+    t = torch()
+    from lossless_bf16_weight_amd.stack import MLPStack
+    rng = np.random.default_rng(12)
+    hidden, inter, m = 256, 704, 16
+    st = MLPStack(m, hidden, inter)
+    for _ in range(2):
+        st.add_layer(synth.gaussian_bf16(rng, (inter, hidden), 0.03), synth.gaussian_bf16(rng, (inter, hidden), 0.03),
+                     synth.gaussian_bf16(rng, (hidden, inter), 0.02))
+    x = dev_u16(synth.gaussian_bf16(rng, (m, hidden), 1.0))
+    a = st.step(x, pipeline=uw.UW_PIPE_DIRECT_PALETTE, fused=False).clone()
+    b = st.step(x, pipeline=uw.UW_PIPE_DIRECT_PALETTE, fused=True).clone()
+    assert t.equal(a, b)
