@@ -241,6 +241,16 @@ uw_status uw_gemm_swiglu(const uw_dmat* d, const uint16_t* x, const float* gate,
 uw_status uw_rmsnorm(const float* y, uint16_t* x, int32_t m, int32_t n, float eps,
                      hipStream_t s);
 
+/* The down projection with the RMS norm fused after it: y = x W^T (fp32 [m, n], as uw_gemm_variant)
+ * and xn[r, :] = bf16(y[r, :] / sqrt(mean(y[r, :]^2) + eps)) (BF16 bits [m, n]), equal bit for bit
+ * to uw_gemm_variant followed by uw_rmsnorm.  When the call runs the multi-tile kernel with K
+ * slices (workspace room for them), the norm is computed inside the slice reduction, one launch
+ * fewer; otherwise it runs as a separate pass over y.  Arguments, workspace and errors as
+ * uw_gemm_variant; xn: device, [m, n]. */
+uw_status uw_gemm_rmsnorm(const uw_dmat* d, const uint16_t* x, float* y, uint16_t* xn, int32_t m,
+                          float eps, int32_t pipeline, int32_t variant, void* ws, size_t ws_bytes,
+                          hipStream_t s);
+
 #ifdef __cplusplus
 }
 #endif

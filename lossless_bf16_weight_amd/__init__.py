@@ -31,7 +31,7 @@ EXPORTS = ("uw_last_error", "uw_version", "uw_build_palette", "uw_encode_bound",
            "uw_transcode_palette", "uw_decode_exponents", "uw_gemm", "uw_gemm_variant", "uw_gemm_bf16",
            "uw_variant_count", "uw_variant_name", "uw_check", "uw_autotune_load", "uw_autotune_set",
            "uw_autotune_get", "uw_autotune_set_variant", "uw_autotune_get_variant", "uw_autotune_clear", "uw_swiglu",
-           "uw_gemm_swiglu", "uw_rmsnorm")
+           "uw_gemm_swiglu", "uw_gemm_rmsnorm", "uw_rmsnorm")
 
 
 class UwError(RuntimeError):
@@ -102,6 +102,7 @@ def lib():
         "uw_autotune_clear": (_I32, []),
         "uw_swiglu": (_I32, [_P, _P, _P, _I64, _P]),
         "uw_gemm_swiglu": (_I32, [_P, _P, _P, _P, _I32, _I32, _I32, _P, _S, _P]),
+        "uw_gemm_rmsnorm": (_I32, [_P, _P, _P, _P, _I32, _F, _I32, _I32, _P, _S, _P]),
         "uw_rmsnorm": (_I32, [_P, _P, _I32, _I32, _F, _P]),
     }
     for name, (res, args) in sig.items():
@@ -264,6 +265,16 @@ def uw_gemm_swiglu(d, x, gate, h, m, pipeline=UW_PIPE_AUTO, variant=-1, ws=None,
     ph = _dev(h, "h", 2 * mm * n, _U16)
     _check(lib().uw_gemm_swiglu(d.handle, px, pg, ph, m, pipeline, variant, _dev(ws, "ws", 0, optional=True),
                                 _nbytes(ws), _stream(stream)))
+
+
+def uw_gemm_rmsnorm(d, x, y, xn, m, eps=1e-5, pipeline=UW_PIPE_AUTO, variant=-1, ws=None, stream=None):
+    """y = x W^T (fp32) and xn = bf16(RMS-normed rows of y): the down projection with the norm
+    fused into its K-slice reduction when it runs one."""
+    n, k = int(d.info["n"]), int(d.info["k"])
+    px, py, pw = _gemm_ptrs(n, k, x, y, m, ws)
+    mm = int(m) if 1 <= int(m) <= UW_MAX_M else 0
+    pn = _dev(xn, "xn", 2 * mm * n, _U16)
+    _check(lib().uw_gemm_rmsnorm(d.handle, px, py, pn, m, eps, pipeline, variant, pw, _nbytes(ws), _stream(stream)))
 
 
 def uw_gemm_bf16(w, x, y, m, variant=-1, stream=None):

@@ -137,6 +137,8 @@ struct GemmArgs {
   float* y;                 // fp32 output, or unused with the SwiGLU epilogue
   const float* gate;        // SwiGLU epilogue: h = bf16(silu(gate) * y) replaces y (null: plain y)
   uint16_t* h;
+  uint16_t* xn;             // K-slice reduction also writes xn = RMS-normed BF16 rows of y (null: no)
+  float eps;
   int32_t n, k, m, kb;
   int32_t vs_segs;          // per-tile kernel: verbatim segments the LDS stage holds (multiple of 16)
   uint32_t base2;
@@ -1166,12 +1168,67 @@ __global__ void k_swiglu4(const floatx4* g, const floatx4* u, u32x2* h, int64_t 
   }
 }
 
+// Sum of squares of one float4 and the BF16 packing of a scaled float4, shared by the RMS-norm
+// kernels so that every route computes the same bits.
+__device__ __forceinline__ float rms_acc(float ss, floatx4 v) {
+  return ss + (v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3]);
+}
+__device__ __forceinline__ u32x2 rms_pack(floatx4 v, float scale) {
+  return u32x2{(uint32_t)f32_to_bf16(v[0] * scale) | ((uint32_t)f32_to_bf16(v[1] * scale) << 16),
+               (uint32_t)f32_to_bf16(v[2] * scale) | ((uint32_t)f32_to_bf16(v[3] * scale) << 16)};
+}
+__device__ __forceinline__ float rms_scale(float* part16, float ss, int n, float eps) {
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+  if ((threadIdx.x & 63) == 0) part16[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) tot += part16[w];
+  return 1.0f / sqrtf(tot / (float)n + eps);
+}
+
+// K-slice reduction of the down projection with the RMS norm in it: one 1024-thread workgroup
+// a row; each float4 of y is the in-order sum of its S slices (as k_reduce_parts), written to
+// y, and the row is normalised as k_rmsnorm_v<V> does (same element grouping and order).
+template <int V>
+__global__ __launch_bounds__(1024) void k_reduce_rmsnorm(const float* part, float* y, uint16_t* xn, int S, int n,
+                                                         int64_t count, float eps) {
+  __shared__ float part16[16];
+  const int n4 = n >> 2;
+  const size_t row4 = (size_t)blockIdx.x * n4;
+  floatx4 v[V];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const int i = (int)threadIdx.x + j * 1024;
+    v[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    if (i < n4) {
+      floatx4 p[kMaxSlices];
+#pragma unroll
+      for (int q = 0; q < kMaxSlices; ++q)
+        if (q < S) p[q] = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(part + (size_t)q * count) + row4 + i);
+      v[j] = p[0];
+#pragma unroll
+      for (int q = 1; q < kMaxSlices; ++q)
+        if (q < S) v[j] += p[q];
+      reinterpret_cast<floatx4*>(y)[row4 + i] = v[j];
+    }
+    ss = rms_acc(ss, v[j]);
+  }
+  const float scale = rms_scale(part16, ss, n, eps);
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const int i = (int)threadIdx.x + j * 1024;
+    if (i < n4) reinterpret_cast<u32x2*>(xn)[row4 + i] = rms_pack(v[j], scale);
+  }
+}
+
 // One 1024-thread workgroup a row, V float4 vectors a thread held in registers between the
 // sum of squares and the scaling (n % 4 == 0, n <= 4096 * V).  Fixed reduction order: each
 // thread's vectors in order, a butterfly inside each wave, then the 16 wave sums in order.
 template <int V>
 __global__ __launch_bounds__(1024) void k_rmsnorm_v(const float* y, uint16_t* x, int n, float eps) {
-  __shared__ float part[16];
+  __shared__ float part[16];   // wave sums
   const floatx4* yr = reinterpret_cast<const floatx4*>(y + (size_t)blockIdx.x * n);
   u32x2* xr = reinterpret_cast<u32x2*>(x + (size_t)blockIdx.x * n);
   const int n4 = n >> 2;
@@ -1181,21 +1238,13 @@ __global__ __launch_bounds__(1024) void k_rmsnorm_v(const float* y, uint16_t* x,
   for (int j = 0; j < V; ++j) {
     const int i = (int)threadIdx.x + j * 1024;
     v[j] = i < n4 ? yr[i] : floatx4{0.f, 0.f, 0.f, 0.f};
-    ss += v[j][0] * v[j][0] + v[j][1] * v[j][1] + v[j][2] * v[j][2] + v[j][3] * v[j][3];
+    ss = rms_acc(ss, v[j]);
   }
-  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
-  __syncthreads();
-  float tot = 0.f;
-#pragma unroll
-  for (int w = 0; w < 16; ++w) tot += part[w];
-  const float scale = 1.0f / sqrtf(tot / (float)n + eps);
+  const float scale = rms_scale(part, ss, n, eps);
 #pragma unroll
   for (int j = 0; j < V; ++j) {
     const int i = (int)threadIdx.x + j * 1024;
-    if (i < n4)
-      xr[i] = u32x2{(uint32_t)f32_to_bf16(v[j][0] * scale) | ((uint32_t)f32_to_bf16(v[j][1] * scale) << 16),
-                    (uint32_t)f32_to_bf16(v[j][2] * scale) | ((uint32_t)f32_to_bf16(v[j][3] * scale) << 16)};
+    if (i < n4) xr[i] = rms_pack(v[j], scale);
   }
 }
 
@@ -1263,6 +1312,16 @@ static hipError_t launch_mt_t(const GemmArgs& a, int64_t tiles, int S, float* pa
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
   const int64_t count = (int64_t)a.m * a.n;
+  if (a.xn) {  // the caller checked rms_fusable(): n % 4 == 0, n <= 16384, aligned y and xn
+    const dim3 g((unsigned)a.m), b(1024);
+    if (a.n <= 4096)
+      hipLaunchKernelGGL((k_reduce_rmsnorm<1>), g, b, 0, s, part, a.y, a.xn, S, a.n, count, a.eps);
+    else if (a.n <= 8192)
+      hipLaunchKernelGGL((k_reduce_rmsnorm<2>), g, b, 0, s, part, a.y, a.xn, S, a.n, count, a.eps);
+    else
+      hipLaunchKernelGGL((k_reduce_rmsnorm<4>), g, b, 0, s, part, a.y, a.xn, S, a.n, count, a.eps);
+    return hipGetLastError();
+  }
   const int64_t blocks = std::min<int64_t>((count / 4 + 255) / 256 + 1, 4096);
   hipLaunchKernelGGL(k_reduce_parts, dim3((unsigned)blocks), dim3(256), 0, s, part, a.y, a.gate, a.h, S, count);
   return hipGetLastError();
@@ -1342,30 +1401,41 @@ static hipError_t launch_gemm_c(const GemmArgs& a, int ct, const Launch& L, hipS
 
 // part / part_bytes: workspace for the multi-tile kernel's K-slice partial sums (may be
 // null: then it runs one slice, or the per-tile kernel when one slice cannot hold k).
+// The kernel a GEMM call runs: resolves variant (-1: the default for the shape) and returns
+// the multi-tile kernel's K-slice count, or 0 for the per-tile kernel (also when the
+// multi-tile variant cannot run: not enough workspace for its slices).
+static int plan_gemm(int src, const GemmArgs& a, int64_t tiles, int* variant, const float* part, size_t part_bytes) {
+  const int ct = col_tiles(a.m);
+  if (*variant < 0) *variant = a.m > 16 ? kMtDefault : default_variant(tiles, a.kb, ct);
+  if (kVariants[*variant].kind != 1) return 0;
+  const int R = kVariants[*variant].waves;
+  int S = mt_slices(tiles, R, a.kb);
+  const size_t plane = (size_t)a.m * a.n * sizeof(float);
+  if (S > 1 && (!part || part_bytes < (size_t)S * plane))
+    S = part ? (int)std::min<size_t>(part_bytes / plane, (size_t)S) : 1;
+  const bool pal = src <= SRC_PAL_LUT;
+  if (S < 1 || (pal && (a.kb + S - 1) / S > 64)) {
+    *variant = default_variant(tiles, a.kb, ct);
+    return 0;
+  }
+  return S;
+}
+
 static uw_status run_gemm(int src, const GemmArgs& a, int64_t tiles, int variant, int max_tile_verb, float* part,
                           size_t part_bytes, hipStream_t s) {
   int ct = col_tiles(a.m);
-  if (variant < 0) variant = a.m > 16 ? kMtDefault : default_variant(tiles, a.kb, ct);
-  if (kVariants[variant].kind == 1) {
+  const int S = plan_gemm(src, a, tiles, &variant, part, part_bytes);
+  if (S > 0) {
     const int R = kVariants[variant].waves, U = kVariants[variant].unroll;
-    int S = mt_slices(tiles, R, a.kb);
-    const size_t plane = (size_t)a.m * a.n * sizeof(float);
-    if (S > 1 && (!part || part_bytes < (size_t)S * plane))
-      S = part ? (int)std::min<size_t>(part_bytes / plane, (size_t)S) : 1;
-    const bool pal = src <= SRC_PAL_LUT;
-    if (S < 1 || (pal && (a.kb + S - 1) / S > 64)) {
-      variant = default_variant(tiles, a.kb, ct);  // not enough workspace: per-tile kernel
-    } else {
-      hipError_t e;
-      switch (src) {
-        case SRC_PAL_AFFINE: e = launch_mt<SRC_PAL_AFFINE>(a, tiles, R, U, S, part, s); break;
-        case SRC_PAL_LUT: e = launch_mt<SRC_PAL_LUT>(a, tiles, R, U, S, part, s); break;
-        case SRC_EXP: e = launch_mt<SRC_EXP>(a, tiles, R, U, S, part, s); break;
-        default: e = launch_mt<SRC_BF16>(a, tiles, R, U, S, part, s); break;
-      }
-      if (e != hipSuccess) return fail(UW_E_HIP, "gemm launch: %s", hipGetErrorString(e));
-      return UW_OK;
+    hipError_t e;
+    switch (src) {
+      case SRC_PAL_AFFINE: e = launch_mt<SRC_PAL_AFFINE>(a, tiles, R, U, S, part, s); break;
+      case SRC_PAL_LUT: e = launch_mt<SRC_PAL_LUT>(a, tiles, R, U, S, part, s); break;
+      case SRC_EXP: e = launch_mt<SRC_EXP>(a, tiles, R, U, S, part, s); break;
+      default: e = launch_mt<SRC_BF16>(a, tiles, R, U, S, part, s); break;
     }
+    if (e != hipSuccess) return fail(UW_E_HIP, "gemm launch: %s", hipGetErrorString(e));
+    return UW_OK;
   }
   Launch L;
   L.tiles = (int)tiles;
@@ -1608,9 +1678,28 @@ const char* uw_variant_name(int32_t variant) {
 
 }  // extern "C"
 
-// Shared body of uw_gemm_variant and uw_gemm_swiglu: y (fp32), or h = bf16(silu(gate) * y).
-static uw_status gemm_entry(const uw_dmat* d, const uint16_t* x, float* y, const float* gate, uint16_t* h, int32_t m,
-                            int32_t pipeline, int32_t variant, void* ws, size_t ws_bytes, hipStream_t s) {
+// Row-wise RMS norm of an fp32 [m, n] y into BF16 x (the vector kernel when the row fits it).
+static bool rms_vec(const float* y, const uint16_t* x, int n) {
+  return n % 4 == 0 && n <= 4 * 4096 && reinterpret_cast<uintptr_t>(y) % 16 == 0 && reinterpret_cast<uintptr_t>(x) % 8 == 0;
+}
+static hipError_t launch_rmsnorm(const float* y, uint16_t* x, int32_t m, int32_t n, float eps, hipStream_t s) {
+  const bool vec = rms_vec(y, x, n);
+  if (vec && n <= 4096)
+    hipLaunchKernelGGL((k_rmsnorm_v<1>), dim3((unsigned)m), dim3(1024), 0, s, y, x, n, eps);
+  else if (vec && n <= 8192)
+    hipLaunchKernelGGL((k_rmsnorm_v<2>), dim3((unsigned)m), dim3(1024), 0, s, y, x, n, eps);
+  else if (vec)
+    hipLaunchKernelGGL((k_rmsnorm_v<4>), dim3((unsigned)m), dim3(1024), 0, s, y, x, n, eps);
+  else
+    hipLaunchKernelGGL(k_rmsnorm, dim3((unsigned)m), dim3(256), 0, s, y, x, n, eps);
+  return hipGetLastError();
+}
+
+// Shared body of uw_gemm_variant, uw_gemm_swiglu and uw_gemm_rmsnorm: y (fp32); or
+// h = bf16(silu(gate) * y) instead; or y and xn = RMS-normed rows of y.
+static uw_status gemm_entry(const uw_dmat* d, const uint16_t* x, float* y, const float* gate, uint16_t* h, uint16_t* xn,
+                            float eps, int32_t m, int32_t pipeline, int32_t variant, void* ws, size_t ws_bytes,
+                            hipStream_t s) {
   uw_status st = check_dmat(d);
   if (st) return st;
   if (!x || (gate ? !h : !y)) return fail(UW_E_ARG, gate ? "null x or h" : "null x or y");
@@ -1657,6 +1746,18 @@ static uw_status gemm_entry(const uw_dmat* d, const uint16_t* x, float* y, const
   a.h = h;
   const int pal_src = d->info.affine ? SRC_PAL_AFFINE : SRC_PAL_LUT;
   const int vs = d->max_tile_verb;
+  // RMS norm: inside the K-slice reduction when the call runs one (same kernel choice as
+  // run_gemm makes), else a separate pass over y after the GEMM.
+  bool rms_fused = false;
+  if (xn) {
+    const int src = pipeline == UW_PIPE_EXP_ONLY ? SRC_EXP : pipeline == UW_PIPE_FULL_DECODE ? SRC_BF16 : pal_src;
+    int v = variant;
+    rms_fused = plan_gemm(src, a, d->info.tiles, &v, part, part_bytes) > 1 && rms_vec(y, xn, a.n);
+    if (rms_fused) {
+      a.xn = xn;
+      a.eps = eps;
+    }
+  }
   switch (pipeline) {
     case UW_PIPE_DIRECT_PALETTE:
       if (!d->idx) return fail(UW_E_ARG, "direct palette needs an index stream bound at uw_dmat_bind");
@@ -1682,6 +1783,10 @@ static uw_status gemm_entry(const uw_dmat* d, const uint16_t* x, float* y, const
       st = run_gemm(SRC_BF16, a, d->info.tiles, variant, 0, part, part_bytes, s);
       break;
   }
+  if (!st && xn && !rms_fused) {
+    const hipError_t e = launch_rmsnorm(y, xn, m, a.n, eps, s);
+    if (e != hipSuccess) return fail(UW_E_HIP, "rmsnorm launch: %s", hipGetErrorString(e));
+  }
   if (!st) clear_error();
   return st;
 }
@@ -1690,18 +1795,24 @@ extern "C" {
 
 uw_status uw_gemm_variant(const uw_dmat* d, const uint16_t* x, float* y, int32_t m, int32_t pipeline, int32_t variant,
                           void* ws, size_t ws_bytes, hipStream_t s) {
-  return gemm_entry(d, x, y, nullptr, nullptr, m, pipeline, variant, ws, ws_bytes, s);
+  return gemm_entry(d, x, y, nullptr, nullptr, nullptr, 0.f, m, pipeline, variant, ws, ws_bytes, s);
 }
 
 uw_status uw_gemm(const uw_dmat* d, const uint16_t* x, float* y, int32_t m, int32_t pipeline, void* ws, size_t ws_bytes,
                   hipStream_t s) {
-  return gemm_entry(d, x, y, nullptr, nullptr, m, pipeline, -1, ws, ws_bytes, s);
+  return gemm_entry(d, x, y, nullptr, nullptr, nullptr, 0.f, m, pipeline, -1, ws, ws_bytes, s);
 }
 
 uw_status uw_gemm_swiglu(const uw_dmat* d, const uint16_t* x, const float* gate, uint16_t* h, int32_t m,
                          int32_t pipeline, int32_t variant, void* ws, size_t ws_bytes, hipStream_t s) {
   if (!gate) return fail(UW_E_ARG, "null gate");
-  return gemm_entry(d, x, nullptr, gate, h, m, pipeline, variant, ws, ws_bytes, s);
+  return gemm_entry(d, x, nullptr, gate, h, nullptr, 0.f, m, pipeline, variant, ws, ws_bytes, s);
+}
+
+uw_status uw_gemm_rmsnorm(const uw_dmat* d, const uint16_t* x, float* y, uint16_t* xn, int32_t m, float eps,
+                          int32_t pipeline, int32_t variant, void* ws, size_t ws_bytes, hipStream_t s) {
+  if (!xn || !y) return fail(UW_E_ARG, "null y or xn");
+  return gemm_entry(d, x, y, nullptr, nullptr, xn, eps, m, pipeline, variant, ws, ws_bytes, s);
 }
 
 uw_status uw_gemm_bf16(const uint16_t* w, int64_t n, int64_t k, const uint16_t* x, float* y, int32_t m, int32_t variant,
@@ -1763,17 +1874,7 @@ uw_status uw_swiglu(const float* g, const float* u, uint16_t* h, int64_t count, 
 
 uw_status uw_rmsnorm(const float* y, uint16_t* x, int32_t m, int32_t n, float eps, hipStream_t s) {
   if (!y || !x || m < 1 || n < 1) return fail(UW_E_ARG, "bad argument");
-  const bool vec = n % 4 == 0 && n <= 4 * 4096 && reinterpret_cast<uintptr_t>(y) % 16 == 0 &&
-                   reinterpret_cast<uintptr_t>(x) % 8 == 0;
-  if (vec && n <= 4096)
-    hipLaunchKernelGGL((k_rmsnorm_v<1>), dim3((unsigned)m), dim3(1024), 0, s, y, x, n, eps);
-  else if (vec && n <= 8192)
-    hipLaunchKernelGGL((k_rmsnorm_v<2>), dim3((unsigned)m), dim3(1024), 0, s, y, x, n, eps);
-  else if (vec)
-    hipLaunchKernelGGL((k_rmsnorm_v<4>), dim3((unsigned)m), dim3(1024), 0, s, y, x, n, eps);
-  else
-    hipLaunchKernelGGL(k_rmsnorm, dim3((unsigned)m), dim3(256), 0, s, y, x, n, eps);
-  const hipError_t e = hipGetLastError();
+  const hipError_t e = launch_rmsnorm(y, x, m, n, eps, s);
   if (e != hipSuccess) return fail(UW_E_HIP, "rmsnorm launch: %s", hipGetErrorString(e));
   clear_error();
   return UW_OK;

@@ -5,7 +5,8 @@ Per layer l with input x_l [m, hidden] (BF16):
     h = bf16(silu(g) * u)               (SwiGLU: in the up GEMM's epilogue, uw_gemm_swiglu;
                                          or uw_gemm + uw_swiglu when u itself is wanted)
     y = h down^T                        (fused reconstruct GEMM, fp32 out)
-    x_{l+1} = bf16(y / sqrt(mean(y^2) + eps))   (weightless RMS norm, uw_rmsnorm)
+    x_{l+1} = bf16(y / sqrt(mean(y^2) + eps))   (weightless RMS norm: in the down GEMM's slice
+                                                 reduction, uw_gemm_rmsnorm; or uw_rmsnorm)
 
 The Unweight post compresses the MLP projections of Llama-3.1-8B (gate, up, down) and runs
 them through its reconstructive matmul; the SwiGLU and the norm between layers are the
@@ -16,8 +17,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import (UW_PIPE_AUTO, CompressedMatrix, uw_check, uw_gemm, uw_gemm_swiglu, uw_rmsnorm, uw_swiglu,
-               uw_workspace_size)
+from . import (UW_PIPE_AUTO, CompressedMatrix, uw_check, uw_gemm, uw_gemm_rmsnorm, uw_gemm_swiglu, uw_rmsnorm,
+               uw_swiglu, uw_workspace_size)
 
 
 class MLPStack:
@@ -60,7 +61,8 @@ class MLPStack:
         per layer, host copies (x_in, g, u, h, y, x_out) -- for tests; it synchronises.
         check: wait for the step and report a corrupt stream found by a decode pipeline
         (UwError); pass False to keep the step asynchronous.  fused: SwiGLU in the up GEMM's
-        epilogue (default unless tracing, which needs u itself); the outputs are identical."""
+        epilogue and the RMS norm after the down GEMM in one call (default unless tracing,
+        which needs u itself); the outputs are identical."""
         fused = trace is None if fused is None else fused
         if fused and trace is not None:
             raise ValueError("a traced step needs u: use fused=False")
@@ -74,8 +76,11 @@ class MLPStack:
             else:
                 uw_gemm(up.d, cur, self.u, self.m, pipeline, ws)
                 uw_swiglu(self.g, self.u, self.h)
-            uw_gemm(down.d, self.h, self.y, self.m, pipeline, ws)
-            uw_rmsnorm(self.y, out, self.eps)
+            if fused:
+                uw_gemm_rmsnorm(down.d, self.h, self.y, out, self.m, self.eps, pipeline, -1, ws)
+            else:
+                uw_gemm(down.d, self.h, self.y, self.m, pipeline, ws)
+                uw_rmsnorm(self.y, out, self.eps)
             if trace is not None:
                 trace.append(tuple(t.cpu().numpy().copy() for t in (cur, self.g, self.u, self.h, self.y, out)))
             cur = out

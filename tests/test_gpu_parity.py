@@ -378,8 +378,8 @@ def test_gemm_swiglu_equals_unfused(name):
 
 
 def test_stack_fused_equals_unfused():
-    """A two-layer MLP stack: the fused step (SwiGLU in the up GEMM's epilogue) ends in the
-    same bits as the unfused one."""
+    """A two-layer MLP stack: the fused step (SwiGLU in the up GEMM's epilogue, the RMS norm
+    with the down GEMM) ends in the same bits as the unfused one."""
     t = torch()
     from lossless_bf16_weight_amd.stack import MLPStack
     rng = np.random.default_rng(12)
@@ -392,3 +392,33 @@ def test_stack_fused_equals_unfused():
     a = st.step(x, pipeline=uw.UW_PIPE_DIRECT_PALETTE, fused=False).clone()
     b = st.step(x, pipeline=uw.UW_PIPE_DIRECT_PALETTE, fused=True).clone()
     assert t.equal(a, b)
+
+
+@pytest.mark.parametrize("name", ["ragged_37x192", "tiles_160x1024", "student_t_48x1024"])
+def test_gemm_rmsnorm_equals_unfused(name):
+    """uw_gemm_rmsnorm gives exactly uw_gemm_variant then uw_rmsnorm (y and the normed rows):
+    every variant and pipeline, with the K-slice reduction (the norm fused into it) and without."""
+    t = torch()
+    w = CASES[name]()
+    n, k = w.shape
+    cm = uw.CompressedMatrix(w)
+    rng = np.random.default_rng(13)
+    for m in (1, 16, 17, 40, 128):
+        x = dev_u16(synth.gaussian_bf16(rng, (m, k), 1.0))
+        y_ref = t.empty((m, n), dtype=t.float32, device="cuda")
+        xn_ref = t.empty((m, n), dtype=t.int16, device="cuda")
+        y = t.empty((m, n), dtype=t.float32, device="cuda")
+        xn = t.empty((m, n), dtype=t.int16, device="cuda")
+        for pipe in ALL_PIPES:
+            ws_full = cm.workspace(m, pipe)
+            variants = range(N_VARIANTS) if pipe == uw.UW_PIPE_DIRECT_PALETTE else (-1,)
+            for variant in variants:
+                for ws in ((ws_full, None) if pipe == uw.UW_PIPE_DIRECT_PALETTE else (ws_full,)):
+                    uw.uw_gemm_variant(cm.d, x, y_ref, m, pipe, variant, ws)
+                    uw.uw_rmsnorm(y_ref, xn_ref, 1e-5)
+                    y.fill_(float("nan"))
+                    xn.fill_(0x7FFF)
+                    uw.uw_gemm_rmsnorm(cm.d, x, y, xn, m, 1e-5, pipe, variant, ws)
+                    what = "m=%d pipeline %d variant %d ws %s" % (m, pipe, variant, "yes" if ws is not None else "no")
+                    assert t.equal(y, y_ref), what
+                    assert t.equal(xn, xn_ref), what
