@@ -208,7 +208,10 @@ uw_status uw_check(void* ws, hipStream_t s);
  *    variant for that pipeline);
  *  - the variant a concrete pipeline, or UW_PIPE_BF16 for uw_gemm_bf16, runs with when called
  *    with variant -1 (uw_autotune_set_variant; variant -1 deletes the entry).
- * Missing entries: AUTO runs DIRECT_PALETTE; variant -1 takes the built-in default.
+ * Lookup (dispatch and the getters alike): the (n, k, m) entry; else the entry of the nearest
+ * measured batch size for the same (n, k) -- nearest by ratio m'/m, the smaller m' on a tie --
+ * so a table measured at a few M also serves the sizes between; else, with no entry for
+ * (n, k) at all, AUTO runs DIRECT_PALETTE and variant -1 takes the built-in default.
  * Text file for uw_autotune_load, one entry per line, '#' starts a comment:
  *     n k m pipeline variant             (AUTO entry)
  *     variant n k m pipeline variant     (per-pipeline variant)

@@ -9,6 +9,8 @@
 // over the BF16 matrix.
 #include <algorithm>
 #include <atomic>
+#include <climits>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -566,19 +568,39 @@ static std::mutex g_tune_mu;
 static std::map<std::tuple<int64_t, int64_t, int32_t>, std::pair<int32_t, int32_t>> g_tune;
 static std::map<std::tuple<int64_t, int64_t, int32_t, int32_t>, int32_t> g_tune_var;
 
+// Entries are looked up by (n, k, m); a batch size with no entry takes the entry of the nearest
+// measured batch size for the same (n, k) (nearest by ratio, the smaller one on a tie), so a
+// table measured at a few M covers the sizes in between.
+static double m_distance(int32_t a, int32_t b) { return std::fabs(std::log((double)a / (double)b)); }
+
 bool autotune_lookup(int64_t n, int64_t k, int32_t m, int32_t* pipeline, int32_t* variant) {
   std::lock_guard<std::mutex> lk(g_tune_mu);
-  auto it = g_tune.find(std::make_tuple(n, k, m));
-  if (it == g_tune.end()) return false;
-  *pipeline = it->second.first;
-  *variant = it->second.second;
+  auto lo = g_tune.lower_bound(std::make_tuple(n, k, INT32_MIN));
+  auto hi = g_tune.upper_bound(std::make_tuple(n, k, INT32_MAX));
+  auto best = g_tune.end();
+  for (auto it = lo; it != hi; ++it)
+    if (best == g_tune.end() || m_distance(std::get<2>(it->first), m) < m_distance(std::get<2>(best->first), m))
+      best = it;
+  if (best == g_tune.end()) return false;
+  *pipeline = best->second.first;
+  *variant = best->second.second;
   return true;
 }
 
 int32_t autotune_variant(int64_t n, int64_t k, int32_t m, int32_t pipeline) {
   std::lock_guard<std::mutex> lk(g_tune_mu);
-  auto it = g_tune_var.find(std::make_tuple(n, k, m, pipeline));
-  return it == g_tune_var.end() ? -1 : it->second;
+  auto lo = g_tune_var.lower_bound(std::make_tuple(n, k, INT32_MIN, INT32_MIN));
+  auto hi = g_tune_var.upper_bound(std::make_tuple(n, k, INT32_MAX, INT32_MAX));
+  int32_t v = -1, bm = 0;
+  for (auto it = lo; it != hi; ++it) {
+    if (std::get<3>(it->first) != pipeline) continue;
+    const int32_t em = std::get<2>(it->first);
+    if (v < 0 || m_distance(em, m) < m_distance(bm, m)) {
+      v = it->second;
+      bm = em;
+    }
+  }
+  return v;
 }
 
 }  // namespace uw
@@ -675,6 +697,8 @@ uw_status uw_autotune_set_variant(int64_t n, int64_t k, int32_t m, int32_t pipel
 
 uw_status uw_autotune_get(int64_t n, int64_t k, int32_t m, int32_t* pipeline, int32_t* variant) {
   if (!pipeline || !variant) return fail(UW_E_ARG, "null argument");
+  uw_status st = check_tune_key(n, k, m, -1);
+  if (st) return st;
   if (!autotune_lookup(n, k, m, pipeline, variant)) {
     *pipeline = UW_PIPE_DIRECT_PALETTE;
     *variant = -1;
@@ -687,6 +711,8 @@ uw_status uw_autotune_get_variant(int64_t n, int64_t k, int32_t m, int32_t pipel
   if (!variant) return fail(UW_E_ARG, "null argument");
   if (pipeline < UW_PIPE_FULL_DECODE || pipeline > UW_PIPE_BF16)
     return fail(UW_E_ARG, "pipeline %d has no variant of its own", pipeline);
+  uw_status st = check_tune_key(n, k, m, -1);
+  if (st) return st;
   *variant = autotune_variant(n, k, m, pipeline);
   clear_error();
   return UW_OK;

@@ -227,3 +227,29 @@ def test_binding_refuses_host_buffers():
     with pytest.raises(ValueError, match="CUDA tensor"):
         uw.uw_gemm_bf16(torch.zeros((16, 64), dtype=torch.int16), torch.zeros((1, 64), dtype=torch.int16),
                         torch.zeros((1, 16), dtype=torch.float32), 1)
+
+
+def test_autotune_nearest_batch_size():
+    """A batch size without an entry takes the entry of the nearest measured one for the same
+    shape (by ratio, the smaller on a tie); another shape or pipeline is never borrowed."""
+    uw.uw_autotune_clear()
+    try:
+        n, k = 4096, 14336
+        uw.uw_autotune_set(n, k, 1, uw.UW_PIPE_DIRECT_PALETTE, 6)
+        uw.uw_autotune_set(n, k, 16, uw.UW_PIPE_DIRECT_PALETTE, 13)
+        uw.uw_autotune_set(n, k, 64, uw.UW_PIPE_TRANSCODE, 10)
+        assert uw.uw_autotune_get(n, k, 1) == (uw.UW_PIPE_DIRECT_PALETTE, 6)
+        assert uw.uw_autotune_get(n, k, 3) == (uw.UW_PIPE_DIRECT_PALETTE, 6)     # 3/1 = 3 < 16/3
+        assert uw.uw_autotune_get(n, k, 4) == (uw.UW_PIPE_DIRECT_PALETTE, 6)     # 4/1 = 16/4: tie -> 1
+        assert uw.uw_autotune_get(n, k, 5) == (uw.UW_PIPE_DIRECT_PALETTE, 13)
+        assert uw.uw_autotune_get(n, k, 32) == (uw.UW_PIPE_DIRECT_PALETTE, 13)   # 32/16 = 64/32: tie -> 16
+        assert uw.uw_autotune_get(n, k, 48) == (uw.UW_PIPE_TRANSCODE, 10)
+        assert uw.uw_autotune_get(n, k, 256) == (uw.UW_PIPE_TRANSCODE, 10)
+        assert uw.uw_autotune_get_variant(n, k, 40, uw.UW_PIPE_DIRECT_PALETTE) == 13  # only 1 and 16 measured
+        assert uw.uw_autotune_get_variant(n, k, 2, uw.UW_PIPE_TRANSCODE) == 10       # only 64 measured
+        assert uw.uw_autotune_get_variant(n, k, 2, uw.UW_PIPE_EXP_ONLY) == -1        # none for this pipeline
+        assert uw.uw_autotune_get(k, n, 16) == (uw.UW_PIPE_DIRECT_PALETTE, -1)   # other shape: default
+        with pytest.raises(uw.UwError):
+            uw.uw_autotune_get(n, k, 0)
+    finally:
+        uw.uw_autotune_clear()
