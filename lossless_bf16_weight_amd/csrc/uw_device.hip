@@ -104,6 +104,22 @@ __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
   return v;
 }
 
+// Exclusive prefix sum over the wave's lanes of a small per-lane value (< 2^BITS), and its
+// total, by bit slices: each bit is balloted and the set lanes below this one counted (no LDS
+// round trips, unlike shuffles).
+template <int BITS>
+__device__ __forceinline__ uint32_t wave_excl_prefix_small(uint32_t v, uint32_t* total) {
+  uint32_t pre = 0, tot = 0;
+#pragma unroll
+  for (int p = 0; p < BITS; ++p) {
+    const uint64_t m = __builtin_amdgcn_ballot_w64(((v >> p) & 1u) != 0u);
+    pre += __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u)) << p;
+    tot += (uint32_t)__popcll(m) << p;
+  }
+  *total = tot;
+  return pre;
+}
+
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
   for (int o = 1; o < 64; o <<= 1) {
     const uint32_t u = __shfl_up(v, o, 64);
@@ -140,7 +156,6 @@ struct GemmArgs {
   uint16_t* xn;             // K-slice reduction also writes xn = RMS-normed BF16 rows of y (null: no)
   float eps;
   int32_t n, k, m, kb;
-  int32_t vs_segs;          // per-tile kernel: verbatim segments the LDS stage holds (multiple of 16)
   uint32_t base2;
   uint32_t tab[4];
   uint32_t m0, m1;  // 0x000F000F, 0x00F000F0 (see exps_affine)
@@ -206,13 +221,14 @@ __device__ __forceinline__ u32x2 bload8_nt(__amdgpu_buffer_rsrc_t rs, uint32_t o
 
 // One prefetch slot: everything block b's compute needs from global memory, so compute
 // issues no global load (global loads retire in order: a load issued inside compute would
-// also wait for every prefetched block behind it).  X rows (XL) and verbatim exponents (VS)
-// can instead come from LDS, which keeps the slot at 6 VGPRs for the palette source.
-template <int SRC, int CT, int XL, int VS>
+// also wait for every prefetched block behind it).  X rows (XL) can instead come from LDS.
+// ev holds this lane's 16 raw exponents when its row's segment of the block is verbatim; the
+// load is one unconditional instruction whose other lanes are out of range (no traffic).
+template <int SRC, int CT, int XL>
 struct Slot {
   WRegs<SRC> w;
   u32x4 xb0[XL ? 1 : CT], xb1[XL ? 1 : CT];  // B operand from global (zeros past the valid rows)
-  u32x4 ev;                                   // VS == 0: this lane's verbatim exponents
+  u32x4 ev;                                   // palette sources: verbatim exponents
 };
 
 template <int CT, int U>
@@ -220,8 +236,11 @@ struct MaxThreads { static constexpr int v = CT == 1 ? (U >= 8 ? 512 : 1024) : (
 static inline int max_waves(int ct, int unroll) { return ct == 1 ? (unroll >= 8 ? 8 : 16) : ct == 2 ? 8 : 4; }
 
 __host__ __device__ constexpr int xl_stride(int k) { return 2 * k + 16; }  // padded X row in LDS
-constexpr int kVexpStageSegs = 256;  // VS: up to this many verbatim segments per tile in LDS (16 KB)
 constexpr int kXlMaxBytes = 48 * 1024;
+
+// s_waitcnt operand that waits until at most n vector-memory loads are outstanding (lgkm and
+// exp counters left alone): vmcnt bits 3:0 and 15:14.
+__host__ __device__ constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
 // Global -> LDS staging with LDS-DMA buffer loads (no VGPRs: the data goes straight to LDS;
 // lane i of one instruction writes `size` bytes at lds + i*size).  Out-of-range lanes write
@@ -231,30 +250,24 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, uint8_t* ld
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)lds, 16, voff, 0, 0, 0);
 }
 
-// LDS layout of k_gemm (bytes): flags (u16) | verbatim prefix (u32) | verbatim exponents
-// (vs_segs segments) | X rows (padded).  The cross-wave partial sums reuse the same bytes
-// once every wave is done with the staged data, so the footprint stays small enough for
-// four 8-wave workgroups a CU.
+// LDS layout of k_gemm (bytes): X rows (XL, padded) | cross-wave partial sums (nw > 1).  The
+// two do not overlap, so the epilogue needs a single barrier.
 struct LdsLayout {
-  uint32_t red, fl, vp, ve, x, total;
+  uint32_t x, red, total;
 };
-__host__ __device__ inline LdsLayout lds_layout(int nw, int ct, int kb, bool pal, int vs_segs, bool xl, int mv,
-                                                int k) {
+__host__ __device__ inline LdsLayout lds_layout(int nw, int ct, bool xl, int mv, int k) {
   LdsLayout L;
-  L.red = 0;
-  L.fl = 0;
-  L.vp = L.fl + (pal ? (uint32_t)((kb * 2 + 15) / 16 * 16) : 0u);
-  L.ve = L.vp + (pal ? (uint32_t)(((kb + 1) * 4 + 15) / 16 * 16) : 0u);
-  L.x = L.ve + (pal ? (uint32_t)vs_segs * 64 : 0u);
-  L.total = L.x + (xl ? (uint32_t)mv * xl_stride(k) : 0u);
-  const uint32_t red_bytes = nw > 1 ? (uint32_t)nw * ct * 64 * 16 : 0u;
-  if (L.total < red_bytes) L.total = red_bytes;
+  L.x = 0;
+  L.red = xl ? (uint32_t)mv * xl_stride(k) : 0u;
+  L.total = L.red + (nw > 1 ? (uint32_t)nw * ct * 64 * 16 : 0u);
   return L;
 }
 
-// Dynamic LDS: [kb u16 flags][kb+1 u32 verbatim prefix][VS: staged verbatim exponents]
-//              [XL: mv padded X rows]; the nw*CT*64 floatx4 partial sums alias it at the end
-template <int SRC, int CT, int U, int XL, int VS>
+// NB > 0: every wave owns exactly NB blocks (the launcher checks kb == NB * waves) and the
+// block loop is fully unrolled into a continuous prefetch ring: block i + U is requested just
+// before block i is computed, so U blocks stay in flight and, with no registers carried
+// around a loop, every wait covers exactly one block's loads.  NB == 0: batches of U blocks.
+template <int SRC, int CT, int U, int XL, int NB>
 __global__ __launch_bounds__((MaxThreads<CT, U>::v)) void k_gemm(GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = threadIdx.x & 63;
@@ -264,15 +277,12 @@ __global__ __launch_bounds__((MaxThreads<CT, U>::v)) void k_gemm(GemmArgs a) {
   const int r = lane & 15, g = lane >> 4;
   const int kb = a.kb;
   const int b0 = (int)((int64_t)wave * kb / nw), b1 = (int)((int64_t)(wave + 1) * kb / nw);
-  const int nblk = b1 - b0;  // >= 1: the launcher keeps nw <= kb
+  const int nblk = b1 - b0;  // 1..64: the launcher keeps nw <= kb and every range within 64 blocks
   const int mcol0 = blockIdx.y * 16 * CT;
   const int mv = min(16 * CT, a.m - mcol0);  // valid X rows of this column block
   constexpr bool kPal = SRC <= SRC_PAL_LUT;
-  const LdsLayout lay = lds_layout(nw, CT, kb, kPal, VS ? a.vs_segs : 0, XL, mv, a.k);
+  const LdsLayout lay = lds_layout(nw, CT, XL, mv, a.k);
   floatx4* red = reinterpret_cast<floatx4*>(smem + lay.red);
-  uint16_t* sfl = reinterpret_cast<uint16_t*>(smem + lay.fl);
-  uint32_t* svp = reinterpret_cast<uint32_t*>(smem + lay.vp);
-  uint8_t* sve = smem + lay.ve;
   uint8_t* sx = smem + lay.x;
 
   floatx4 acc[CT], acc2[CT];
@@ -314,12 +324,15 @@ __global__ __launch_bounds__((MaxThreads<CT, U>::v)) void k_gemm(GemmArgs a) {
   // output columns past mv, which are never stored.
   const uint32_t xl_off = (uint32_t)((r < mv ? r : 0) * xl_stride(a.k) + g * 32);
 
-  uint32_t vbase = 0;
+  // Verbatim bookkeeping (palette sources), all in registers: this wave's flags one block per
+  // lane (wfl: bit r = row r's segment of the block is verbatim) and each block's rank among
+  // the tile's verbatim segments (wvp: segments in earlier blocks of the tile).
+  uint32_t wfl = 0, wvp = 0;
   __amdgpu_buffer_rsrc_t vrs = make_rsrc(a.vexp, 0);
 
   // Loads of block b; `ok` false turns every lane offset out of range (zeros, no traffic), so
   // a batch's loads are unconditional instructions even past the wave's last block.
-  auto load_main = [&](int b, bool ok, Slot<SRC, CT, XL, VS>& sl) {
+  auto load_main = [&](int b, bool ok, Slot<SRC, CT, XL>& sl) {
     const uint32_t o0 = ok ? woff0 : kOob;
     if constexpr (SRC == SRC_BF16) {
       sl.w.w0 = bload16_nt(wrs0, o0, b * 128);
@@ -340,22 +353,17 @@ __global__ __launch_bounds__((MaxThreads<CT, U>::v)) void k_gemm(GemmArgs a) {
       }
     }
   };
-  // VS == 0: verbatim exponents through the ring (bounds-checked load, zeros unless flagged).
-  auto load_ev = [&](int b, Slot<SRC, CT, XL, VS>& sl) {
-    if constexpr (kPal && !VS) {
-      const uint32_t f = __builtin_amdgcn_readfirstlane(sfl[b]);
-      const uint32_t rank = __builtin_amdgcn_readfirstlane(svp[b]) + __popc(f & ((1u << r) - 1u));
-      sl.ev = bload16(vrs, ((f >> r) & 1u) ? rank * 64 + g * 16 : kOob);
+  // This lane's verbatim exponents of block b (zeros unless its row's segment is verbatim).
+  auto load_ev = [&](int b, bool ok, Slot<SRC, CT, XL>& sl) {
+    if constexpr (kPal) {
+      const int j = (b - b0) & 63;
+      const uint32_t f = __builtin_amdgcn_readlane(wfl, j);
+      const uint32_t rank = __builtin_amdgcn_readlane(wvp, j) + __popc(f & ((1u << r) - 1u));
+      sl.ev = bload16(vrs, (ok && ((f >> r) & 1u)) ? rank * 64 + g * 16 : kOob);
     }
   };
 
-  // Per-wave copies of the tile's flags / verbatim prefixes, block b0 + j in lane j (the
-  // launcher keeps every wave's range within 64 blocks), filled after the LDS staging.
-  uint32_t wfl = 0, wvp = 0;
-  auto wave_flag = [&](int b) -> uint32_t { return __builtin_amdgcn_readlane(wfl, b - b0); };
-  auto wave_vpre = [&](int b) -> uint32_t { return __builtin_amdgcn_readlane(wvp, b - b0); };
-
-  auto compute = [&](int b, const Slot<SRC, CT, XL, VS>& sl) {
+  auto compute = [&](int b, const Slot<SRC, CT, XL>& sl) {
     u32x4 A0, A1;
     if constexpr (SRC == SRC_BF16) {
       A0 = sl.w.w0;  // rows past n arrive as zeros (bounds-checked load)
@@ -373,20 +381,12 @@ __global__ __launch_bounds__((MaxThreads<CT, U>::v)) void k_gemm(GemmArgs a) {
         exps_raw(sl.w.e.z, sl.w.e.w, T1);
       }
       if constexpr (kPal) {
-        // This wave's flags and verbatim prefixes sit one block per lane in wfl / wvp.
-        const uint32_t f = wave_flag(b);
+        const uint32_t f = __builtin_amdgcn_readlane(wfl, b - b0);
         if (f) {  // uniform: some row of this tile has a verbatim segment in block b
           const bool mine = (f >> r) & 1u;
-          u32x4 ev;
-          if constexpr (VS) {
-            const uint32_t rank = wave_vpre(b) + __popc(f & ((1u << r) - 1u));
-            ev = *reinterpret_cast<const u32x4*>(sve + (mine ? rank * 64 + g * 16 : 0u));
-          } else {
-            ev = sl.ev;
-          }
           uint32_t R0[4], R1[4];
-          exps_raw(ev.x, ev.y, R0);
-          exps_raw(ev.z, ev.w, R1);
+          exps_raw(sl.ev.x, sl.ev.y, R0);
+          exps_raw(sl.ev.z, sl.ev.w, R1);
           const uint32_t keep = mine ? 0u : ~0u;  // element-wise select, no array select
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -426,25 +426,22 @@ __global__ __launch_bounds__((MaxThreads<CT, U>::v)) void k_gemm(GemmArgs a) {
   // computes its blocks; nothing is carried in registers from one batch to the next, so the
   // waits are exact and no copy ever waits on a load.  Memory latency is covered by the U
   // loads of a batch and by the other waves on the SIMD.
-  // Prologue: the LDS staging loads (flags, verbatim exponents, X rows) go out first, then the
-  // first batch; staging data returns first (loads retire in order), so the barriers below
-  // do not wait for the batch.
-  Slot<SRC, CT, XL, VS> buf[U];
-  uint16_t stf[4];
+  // Prologue, in issue order (loads retire in order, so each wait below covers only what it
+  // needs): this wave's verbatim flags, the X rows (LDS-DMA), the first batch of weights --
+  // nothing here waits on an earlier global load, so every wave's weight stream starts at
+  // once -- then one barrier for the X rows, the verbatim prefix (bit-sliced ballots once the
+  // flags are in) and the first batch's verbatim exponents.
+  Slot<SRC, CT, XL> buf[NB > 0 ? NB : U];
+  uint32_t fpre[4];
+  __amdgpu_buffer_rsrc_t frs;
   if constexpr (kPal) {
-    vbase = a.vprefix[t];
-    const uint32_t nvt = a.vprefix[t + 1] - vbase;
-    vrs = make_rsrc(a.vexp + (size_t)vbase * 64, nvt * 64);
-    const __amdgpu_buffer_rsrc_t frs = make_rsrc(a.flags + (size_t)t * kb, (uint32_t)kb * 2);
-    // Flags: up to 4 bounds-checked 16-bit loads a thread (sub-dword LDS-DMA would not pack
-    // them), stored to LDS once they arrive; a longer tile row takes the loop below.
+    frs = make_rsrc(a.flags + (size_t)t * kb, (uint32_t)kb * 2);
+    wfl = __builtin_amdgcn_raw_buffer_load_b16(frs, lane < nblk ? (uint32_t)(b0 + lane) * 2 : kOob, 0, 0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int i = threadIdx.x + j * (int)blockDim.x;
-      stf[j] = __builtin_amdgcn_raw_buffer_load_b16(frs, i < kb ? (uint32_t)i * 2 : kOob, 0, 0);
+    for (int j = 0; j < 4; ++j) {  // flags of the tile's blocks before b0 (first 256)
+      const int i = j * 64 + lane;
+      fpre[j] = __builtin_amdgcn_raw_buffer_load_b16(frs, i < b0 ? (uint32_t)i * 2 : kOob, 0, 0);
     }
-    if constexpr (VS)
-      for (int c = wave; c * 16 < (int)nvt; c += nw) lds_dma16(vrs, sve + c * 1024, (uint32_t)c * 1024 + lane * 16);
   }
   if constexpr (XL) {  // X rows, 1 KB a DMA (the launcher requires k % 512 == 0)
     const int per_row = a.k / 512;
@@ -455,45 +452,66 @@ __global__ __launch_bounds__((MaxThreads<CT, U>::v)) void k_gemm(GemmArgs a) {
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) load_main(b0 + u, u < nblk, buf[u]);
-  if constexpr (kPal) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int i = threadIdx.x + j * (int)blockDim.x;
-      if (i < kb) sfl[i] = stf[j];
-    }
-    for (int i = threadIdx.x + 4 * blockDim.x; i < kb; i += blockDim.x) sfl[i] = a.flags[(size_t)t * kb + i];
+  uint32_t vbase = 0, nvt = 0;
+  if constexpr (kPal) {  // scalar loads (before the barrier, which would turn them into vector loads)
+    vbase = a.vprefix[t];
+    nvt = a.vprefix[t + 1] - vbase;
   }
-  if constexpr (kPal || XL) __syncthreads();
-  if constexpr (kPal) {
-    if (wave == 0) {  // exclusive prefix of verbatim counts per block (wave-level scan)
-      uint32_t carry = 0;
-      for (int j = 0; j < kb; j += 64) {
-        const int b = j + lane;
-        const uint32_t v = b < kb ? (uint32_t)__popc((uint32_t)sfl[b]) : 0u;
-        const uint32_t incl = wave_incl_scan(v, lane);
-        if (b < kb) svp[b] = carry + incl - v;
-        carry += __shfl(incl, 63, 64);
-      }
-    }
+  if constexpr (XL) {
+    // This wave's X DMAs precede exactly the 2U weight loads above and loads retire in
+    // order, so at most 2U outstanding means they have landed; then every wave's have.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * U));
     __syncthreads();
-    wfl = b0 + lane < kb ? sfl[b0 + lane] : 0u;
-    wvp = b0 + lane < kb ? svp[b0 + lane] : 0u;
   }
-  auto run_batch = [&](int b) {
-    if constexpr (kPal && !VS) {
+  if constexpr (kPal) {
+    vrs = make_rsrc(a.vexp + (size_t)vbase * 64, nvt * 64);
+    uint32_t before = (uint32_t)__popc(fpre[0]) + __popc(fpre[1]) + __popc(fpre[2]) + __popc(fpre[3]);
+    for (int j = 256; j < b0; j += 64) {  // tile rows of more than 256 + 64 blocks
+      const int i = j + lane;
+      before += __popc((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(frs, i < b0 ? (uint32_t)i * 2 : kOob, 0, 0));
+    }
+    uint32_t tot;
+    wave_excl_prefix_small<9>(before, &tot);  // per lane at most 16 flags words of 16 bits
+    wvp = tot + wave_excl_prefix_small<5>((uint32_t)__popc(wfl), &tot);
+#pragma unroll
+    for (int u = 0; u < U; ++u) load_ev(b0 + u, u < nblk, buf[u]);
+  }
+
+  if constexpr (NB > 0) {
+    // A block's verbatim-exponent registers are read only when the block is flagged; the
+    // allocator would reuse them as soon as an unflagged block is done, and overwriting the
+    // destination of a load still in flight costs a wait for that load.  Each is kept alive
+    // until block i + U is computed, by which point the in-order waits have retired it.
+    auto keep = [](const u32x4& v) { asm volatile("" ::"v"(v.x), "v"(v.y), "v"(v.z), "v"(v.w)); };
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      if (i + U < NB) {
+        load_main(b0 + i + U, true, buf[i + U]);
+        load_ev(b0 + i + U, true, buf[i + U]);
+      }
+      if constexpr (kPal)
+        if (i >= U) keep(buf[i - U].ev);
+      compute(b0 + i, buf[i]);
+    }
+    if constexpr (kPal) {
+#pragma unroll
+      for (int i = NB - U; i < NB; ++i) keep(buf[i].ev);
+    }
+  } else {
+    auto run_batch = [&](int b) {
 #pragma unroll
       for (int u = 0; u < U; ++u)
-        if (b + u < b1) load_ev(b + u, buf[u]);
+        if (b + u < b1) compute(b + u, buf[u]);
+    };
+    run_batch(b0);
+    for (int b = b0 + U; b < b1; b += U) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        load_main(b + u, b + u < b1, buf[u]);
+        load_ev(b + u, b + u < b1, buf[u]);
+      }
+      run_batch(b);
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (b + u < b1) compute(b + u, buf[u]);
-  };
-  run_batch(b0);
-  for (int b = b0 + U; b < b1; b += U) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) load_main(b + u, b + u < b1, buf[u]);
-    run_batch(b);
   }
 
 #pragma unroll
@@ -508,7 +526,6 @@ __global__ __launch_bounds__((MaxThreads<CT, U>::v)) void k_gemm(GemmArgs a) {
     for (int c = 0; c < CT; ++c) store(c, lane, acc[c]);
     return;
   }
-  __syncthreads();  // the partial sums overwrite the staged X rows and exponents
 #pragma unroll
   for (int c = 0; c < CT; ++c) red[(wave * CT + c) * 64 + lane] = acc[c];
   __syncthreads();
@@ -1355,38 +1372,52 @@ static hipError_t launch_mt(const GemmArgs& a, int64_t tiles, int R, int U, int 
 
 struct Launch {
   int tiles, waves, unroll;
-  int max_tile_verb;  // most verbatim segments in one tile (LDS staging when they all fit)
 };
 
-template <int SRC, int CT, int U, int XL, int VS>
+template <int SRC, int CT, int U, int XL, int NB>
 static hipError_t launch_gemm_t(const GemmArgs& a, const Launch& L, hipStream_t s) {
   const int gy = (a.m + 16 * CT - 1) / (16 * CT);
-  GemmArgs b = a;
-  b.vs_segs = VS ? (L.max_tile_verb + 15) / 16 * 16 : 0;  // the stage is filled 16 segments at a time
-  const size_t shm = lds_layout(L.waves, CT, a.kb, SRC <= SRC_PAL_LUT, b.vs_segs, XL, std::min(a.m, 16 * CT), a.k).total;
-  hipLaunchKernelGGL((k_gemm<SRC, CT, U, XL, VS>), dim3(L.tiles, gy), dim3(64 * L.waves), shm, s, b);
+  const size_t shm = lds_layout(L.waves, CT, XL, std::min(a.m, 16 * CT), a.k).total;
+  hipLaunchKernelGGL((k_gemm<SRC, CT, U, XL, NB>), dim3(L.tiles, gy), dim3(64 * L.waves), shm, s, a);
   return hipGetLastError();
 }
 
-template <int SRC, int CT, int XL, int VS>
+// Fully unrolled ring (palette sources, X rows in LDS) for the per-wave block counts of the
+// MLP shapes: k = 4096 over 2 or 4 waves, k = 14336 over 4 or 8 waves, k = 8192 over 2 waves.
+template <int SRC, int U>
+static hipError_t launch_gemm_ring(const GemmArgs& a, const Launch& L, hipStream_t s) {
+  if (a.kb % L.waves == 0) {
+    switch (a.kb / L.waves) {
+      case 16: return launch_gemm_t<SRC, 1, U, 1, 16>(a, L, s);
+      case 28: return launch_gemm_t<SRC, 1, U, 1, 28>(a, L, s);
+      case 32: return launch_gemm_t<SRC, 1, U, 1, 32>(a, L, s);
+      case 56: return launch_gemm_t<SRC, 1, U, 1, 56>(a, L, s);
+      case 64: return launch_gemm_t<SRC, 1, U, 1, 64>(a, L, s);
+      default: break;
+    }
+  }
+  return launch_gemm_t<SRC, 1, U, 1, 0>(a, L, s);
+}
+
+template <int SRC, int CT, int XL>
 static hipError_t launch_gemm_u(const GemmArgs& a, const Launch& L, hipStream_t s) {
   // Deeper prefetch only where the slot stays small enough to avoid spills (X from LDS).
-  if constexpr (CT == 1) {
-    if (L.unroll >= 8) return launch_gemm_t<SRC, 1, 8, XL, VS>(a, L, s);
-    return launch_gemm_t<SRC, 1, 4, XL, VS>(a, L, s);
+  if constexpr (CT == 1 && XL && SRC <= SRC_PAL_LUT) {
+    if (L.unroll >= 8) return launch_gemm_ring<SRC, 8>(a, L, s);
+    return launch_gemm_ring<SRC, 4>(a, L, s);
+  } else if constexpr (CT == 1) {
+    if (L.unroll >= 8) return launch_gemm_t<SRC, 1, 8, XL, 0>(a, L, s);
+    return launch_gemm_t<SRC, 1, 4, XL, 0>(a, L, s);
   } else {
-    return launch_gemm_t<SRC, CT, 4, 0, VS>(a, L, s);
+    return launch_gemm_t<SRC, CT, 4, 0, 0>(a, L, s);
   }
 }
 
 template <int SRC, int CT>
 static hipError_t launch_gemm_v(const GemmArgs& a, const Launch& L, hipStream_t s) {
-  constexpr bool pal = SRC <= SRC_PAL_LUT;
   const int mv = std::min(a.m, 16);
   const bool xl = CT == 1 && a.k % 512 == 0 && (size_t)mv * xl_stride(a.k) <= (size_t)kXlMaxBytes;
-  const bool vs_ok = L.max_tile_verb <= kVexpStageSegs;
-  if (pal && vs_ok) return xl ? launch_gemm_u<SRC, CT, CT == 1, 1>(a, L, s) : launch_gemm_u<SRC, CT, 0, 1>(a, L, s);
-  return xl ? launch_gemm_u<SRC, CT, CT == 1, 0>(a, L, s) : launch_gemm_u<SRC, CT, 0, 0>(a, L, s);
+  return xl ? launch_gemm_u<SRC, CT, CT == 1>(a, L, s) : launch_gemm_u<SRC, CT, 0>(a, L, s);
 }
 
 template <int SRC>
@@ -1421,7 +1452,7 @@ static int plan_gemm(int src, const GemmArgs& a, int64_t tiles, int* variant, co
   return S;
 }
 
-static uw_status run_gemm(int src, const GemmArgs& a, int64_t tiles, int variant, int max_tile_verb, float* part,
+static uw_status run_gemm(int src, const GemmArgs& a, int64_t tiles, int variant, float* part,
                           size_t part_bytes, hipStream_t s) {
   int ct = col_tiles(a.m);
   const int S = plan_gemm(src, a, tiles, &variant, part, part_bytes);
@@ -1440,7 +1471,6 @@ static uw_status run_gemm(int src, const GemmArgs& a, int64_t tiles, int variant
   Launch L;
   L.tiles = (int)tiles;
   L.unroll = kVariants[variant].unroll;
-  L.max_tile_verb = max_tile_verb;
   // Every wave's block range must fit one lane per block (<= 64 blocks).  Wider column tiles
   // and deeper batches allow fewer waves per workgroup; past that, use shallower batches and
   // 16-column tiles.
@@ -1577,12 +1607,8 @@ uw_status uw_dmat_bind(uw_dmat* d, const void* blob_host, size_t bytes, const vo
   d->idx = reinterpret_cast<uint8_t*>(idx_dev);
   const uint8_t* hb = reinterpret_cast<const uint8_t*>(blob_host);
   const uint32_t* cb = reinterpret_cast<const uint32_t*>(hb + info.sec_off[SEC_CBASE]);
-  const uint32_t* vp = reinterpret_cast<const uint32_t*>(hb + info.sec_off[SEC_VPREFIX]);
   const uint32_t* of = reinterpret_cast<const uint32_t*>(hb + info.sec_off[SEC_OFF]);
   const uint16_t* fl = reinterpret_cast<const uint16_t*>(hb + info.sec_off[SEC_FLAGS]);
-  int32_t mv = 0;
-  for (int64_t t = 0; t < info.tiles; ++t) mv = std::max<int32_t>(mv, (int32_t)(vp[t + 1] - vp[t]));
-  d->max_tile_verb = mv;
   // Decoder units: whole blocks whose chunks fill at most one wave, and the largest
   // bitstream slice any unit stages.
   d->dec_spc = info.chunk / kSeg;
@@ -1745,7 +1771,6 @@ static uw_status gemm_entry(const uw_dmat* d, const uint16_t* x, float* y, const
   a.gate = gate;
   a.h = h;
   const int pal_src = d->info.affine ? SRC_PAL_AFFINE : SRC_PAL_LUT;
-  const int vs = d->max_tile_verb;
   // RMS norm: inside the K-slice reduction when the call runs one (same kernel choice as
   // run_gemm makes), else a separate pass over y after the GEMM.
   bool rms_fused = false;
@@ -1762,25 +1787,25 @@ static uw_status gemm_entry(const uw_dmat* d, const uint16_t* x, float* y, const
     case UW_PIPE_DIRECT_PALETTE:
       if (!d->idx) return fail(UW_E_ARG, "direct palette needs an index stream bound at uw_dmat_bind");
       a.aux = d->idx;
-      st = run_gemm(pal_src, a, d->info.tiles, variant, vs, part, part_bytes, s);
+      st = run_gemm(pal_src, a, d->info.tiles, variant, part, part_bytes, s);
       break;
     case UW_PIPE_TRANSCODE:
       st = run_decode(d, DEC_IDX, wsb + kErrBytes, ws, ws_bytes, s);
       if (st) return st;
       a.aux = wsb + kErrBytes;
-      st = run_gemm(pal_src, a, d->info.tiles, variant, vs, part, part_bytes, s);
+      st = run_gemm(pal_src, a, d->info.tiles, variant, part, part_bytes, s);
       break;
     case UW_PIPE_EXP_ONLY:
       st = run_decode(d, DEC_EXP, wsb + kErrBytes, ws, ws_bytes, s);
       if (st) return st;
       a.aux = wsb + kErrBytes;
-      st = run_gemm(SRC_EXP, a, d->info.tiles, variant, 0, part, part_bytes, s);
+      st = run_gemm(SRC_EXP, a, d->info.tiles, variant, part, part_bytes, s);
       break;
     default:
       st = run_decode(d, DEC_BF16, wsb + kErrBytes, ws, ws_bytes, s);
       if (st) return st;
       a.aux = wsb + kErrBytes;
-      st = run_gemm(SRC_BF16, a, d->info.tiles, variant, 0, part, part_bytes, s);
+      st = run_gemm(SRC_BF16, a, d->info.tiles, variant, part, part_bytes, s);
       break;
   }
   if (!st && xn && !rms_fused) {
@@ -1832,7 +1857,7 @@ uw_status uw_gemm_bf16(const uint16_t* w, int64_t n, int64_t k, const uint16_t* 
   a.k = (int32_t)k;
   a.m = m;
   a.kb = (int32_t)(k / 64);
-  uw_status st = run_gemm(SRC_BF16, a, (n + 15) / 16, variant, 0, nullptr, 0, s);
+  uw_status st = run_gemm(SRC_BF16, a, (n + 15) / 16, variant, nullptr, 0, s);
   if (!st) clear_error();
   return st;
 }

@@ -66,7 +66,6 @@ struct uw_dmat {
   const uint32_t* words;
   uint32_t words_cap;             // words readable in the device blob (aligned section)
   uint8_t* idx;                   // direct-palette index stream (caller's), may be null
-  int32_t max_tile_verb;          // max verbatim segments in one tile
   int32_t dec_spc, dec_cpb, dec_nb;  // decoder units: segments per chunk, chunks per block, blocks per unit
   uint32_t dec_stage_words;       // most bitstream words one decoder unit stages (16-byte aligned)
 };
