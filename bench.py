@@ -15,11 +15,11 @@ Prints one JSON line (stdout).  Diagnostics go to stderr.
 from __future__ import annotations
 
 import argparse
+import glob
 import hashlib
 import json
 import os
 import re
-import subprocess
 import sys
 import time
 
@@ -59,15 +59,22 @@ def traffic_from_profile():
 
 
 def device_info():
-    """GPU name and clocks as rocm-smi reports them (queried in a child process before this process
-    touches the GPU), and the host CPU model; fields are None where a query fails."""
+    """Current GPU clock levels from sysfs (the amdgpu driver's pp_dpm_* files, the starred
+    line) and the host CPU model; read from files, so no program is started (a process that
+    has touched the GPU, e.g. under a profiler's preload, must not exec another).  Fields are
+    None where a read fails."""
     info = {"gpu": None, "clocks": None, "cpu_model": None}
-    try:
-        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
-        lines = [ln.strip() for ln in r.stdout.splitlines() if re.search(r"(sclk|mclk|fclk).*Mhz", ln, re.I)]
-        info["clocks"] = lines[:6] or None
-    except Exception:
-        pass
+    clocks = []
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device"))[:4]:
+        for f in ("pp_dpm_sclk", "pp_dpm_mclk", "pp_dpm_fclk"):
+            try:
+                with open(os.path.join(dev, f)) as fh:
+                    cur = [ln.strip() for ln in fh if ln.strip().endswith("*")]
+            except OSError:
+                continue
+            if cur:
+                clocks.append("%s %s %s" % (dev.split("/")[-2], f[7:], cur[0]))
+    info["clocks"] = clocks or None
     try:
         with open("/proc/cpuinfo") as f:
             m = re.search(r"^model name\s*:\s*(.+)$", f.read(), re.M)
@@ -105,9 +112,31 @@ def cpu_baseline(w, x, seconds=10.0):
                        "1 thread, uncompressed-equivalent bytes" % (rows, rows // 16, reps, el))
 
 
-def time_launches(fn, copies, steps, warmup, stream):
-    """fn(i) launches on `stream`.  Returns (total_ms, per-launch ms list)."""
+SETTLE_MS = 50.0
+
+
+def settle(fn, copies, stream, ms=SETTLE_MS):
+    """Untimed launches of fn until `ms` of GPU time has passed.  The GPU's clocks drop while
+    the host works between measurements and take a few milliseconds of load to come back; a
+    few dozen warm-up launches of a 16 us kernel are not enough for that."""
     import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    done, i = 0.0, 0
+    while done < ms:
+        for _ in range(64):
+            fn(i % copies)
+            i += 1
+        e1.record(stream)
+        e1.synchronize()
+        done = e0.elapsed_time(e1)
+
+
+def time_launches(fn, copies, steps, warmup, stream):
+    """fn(i) launches on `stream`.  Returns (total_ms, per-launch ms list).  The clocks are
+    settled first, then `warmup` untimed launches, then exactly `steps` timed ones."""
+    import torch
+    settle(fn, copies, stream)
     for i in range(warmup):
         fn(i % copies)
     torch.cuda.synchronize()
@@ -274,7 +303,10 @@ def main():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--variant", type=int, default=-1, help="fused-kernel variant id (default: autotuned)")
+    ap.add_argument("--variant", type=int, default=-1,
+                    help="fused-kernel variant id (default: autotuned); given, nothing is autotuned")
+    ap.add_argument("--bf16-variant", type=int, default=-1,
+                    help="BF16 GEMV variant with --variant (default: the library's choice for the shape)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run three device copies of 512 MiB (HBM counter calibration) and exit")
     ap.add_argument("--workload", default="gate", choices=("gate", "down", "heavy", "stack", "small"),
@@ -325,10 +357,13 @@ def main():
     copies, mats = tuner.copies, tuner.mats
     log("encoded in %.2fs: bundle %.3f b/w, resident %.3f b/w, %d copies" % (
         enc_s, 8 * blob.size / (n * k), 8 * resident / (n * k), copies))
-    table = tuner.tune([1], pipelines=(uw.UW_PIPE_DIRECT_PALETTE,), bf16=True)
-    table.apply()
-    pal_variant = uw.uw_autotune_get_variant(n, k, 1, uw.UW_PIPE_DIRECT_PALETTE) if args.variant < 0 else args.variant
-    bf16_variant = uw.uw_autotune_get_variant(n, k, 1, uw.UW_PIPE_BF16)
+    if args.variant < 0:
+        table = tuner.tune([1], pipelines=(uw.UW_PIPE_DIRECT_PALETTE,), bf16=True)
+        table.apply()
+        pal_variant = uw.uw_autotune_get_variant(n, k, 1, uw.UW_PIPE_DIRECT_PALETTE)
+        bf16_variant = uw.uw_autotune_get_variant(n, k, 1, uw.UW_PIPE_BF16)
+    else:                      # fixed variants, no tuning launches (profiling runs)
+        pal_variant, bf16_variant = args.variant, args.bf16_variant
     log("autotuned: direct palette variant %d (%s), bf16 variant %d (%s)" % (
         pal_variant, uw.uw_variant_name(pal_variant), bf16_variant, uw.uw_variant_name(bf16_variant)))
     # load-time transcode (Huffman -> 4-bit indices), timed on the copies

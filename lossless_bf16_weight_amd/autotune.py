@@ -31,6 +31,7 @@ PIPELINES = (UW_PIPE_FULL_DECODE, UW_PIPE_EXP_ONLY, UW_PIPE_TRANSCODE, UW_PIPE_D
 PIPELINE_NAMES = {UW_PIPE_FULL_DECODE: "full_decode", UW_PIPE_EXP_ONLY: "exp_only", UW_PIPE_TRANSCODE: "transcode",
                   UW_PIPE_DIRECT_PALETTE: "direct_palette", UW_PIPE_BF16: "bf16"}
 ROTATE_BYTES = 512e6
+SETTLE_MS = 50.0      # untimed load before timing, for the clocks to come up
 
 
 @dataclasses.dataclass
@@ -97,11 +98,24 @@ def _time_interleaved(cands, launches, rounds, stream):
     Returns {key: median us per launch}."""
     import torch
     per = {key: [] for key in cands}
-    for fn, copies in cands.values():               # warm-up: code objects, clocks
+    for fn, copies in cands.values():               # warm-up: code objects
         for i in range(copies):
             fn(i)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # Clocks: the GPU needs a few milliseconds of load after an idle host phase before it runs
+    # at speed; without this the first round's candidates would be timed at a lower clock.
+    fn, copies = next(iter(cands.values()))
+    e0.record(stream)
+    i = 0
+    while True:
+        for _ in range(32):
+            fn(i % copies)
+            i += 1
+        e1.record(stream)
+        e1.synchronize()
+        if e0.elapsed_time(e1) >= SETTLE_MS:
+            break
     for r in range(rounds):
         for key, (fn, copies) in cands.items():
             e0.record(stream)

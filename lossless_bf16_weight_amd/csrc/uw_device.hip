@@ -1299,12 +1299,14 @@ static int col_tiles(int m) {
   return ct <= 1 ? 1 : ct <= 2 ? 2 : ct <= 4 ? 4 : 8;
 }
 
-static int default_variant(int64_t tiles, int64_t kb, int ct) {
-  // Measured on MI355X: about 2048 waves over the chip (8 per CU, all resident at once) with
-  // 4-block batches is best for M <= 16; wider M keeps 4-block batches and fewer waves.
+static int default_variant(int64_t tiles, int64_t kb, int ct, int m) {
+  // Measured on MI355X: at M <= 4 one wave per tile with a 4-block ring is best on every MLP
+  // shape (gate 14336 x 4096: 896 waves; down 4096 x 14336: 256 waves); otherwise about 2048
+  // waves over the chip with 4-block batches; wider M keeps 4-block batches and fewer waves.
   const int cap = ct == 1 ? 16 : ct == 2 ? 8 : 4;
+  const int64_t target = m <= 4 ? 128 : 1536;
   int w = 1;
-  while (w < cap && tiles * w < 1536 && kb / (w * 2) >= 4) w *= 2;
+  while (w < cap && tiles * w < target && kb / (w * 2) >= 4) w *= 2;
   for (int v = 0; v < kNumVariants; ++v)
     if (kVariants[v].kind == 0 && kVariants[v].waves == w && kVariants[v].unroll == 4) return v;
   return 0;
@@ -1437,7 +1439,7 @@ static hipError_t launch_gemm_c(const GemmArgs& a, int ct, const Launch& L, hipS
 // multi-tile variant cannot run: not enough workspace for its slices).
 static int plan_gemm(int src, const GemmArgs& a, int64_t tiles, int* variant, const float* part, size_t part_bytes) {
   const int ct = col_tiles(a.m);
-  if (*variant < 0) *variant = a.m > 16 ? kMtDefault : default_variant(tiles, a.kb, ct);
+  if (*variant < 0) *variant = a.m > 16 ? kMtDefault : default_variant(tiles, a.kb, ct, a.m);
   if (kVariants[*variant].kind != 1) return 0;
   const int R = kVariants[*variant].waves;
   int S = mt_slices(tiles, R, a.kb);
@@ -1446,7 +1448,7 @@ static int plan_gemm(int src, const GemmArgs& a, int64_t tiles, int* variant, co
     S = part ? (int)std::min<size_t>(part_bytes / plane, (size_t)S) : 1;
   const bool pal = src <= SRC_PAL_LUT;
   if (S < 1 || (pal && (a.kb + S - 1) / S > 64)) {
-    *variant = default_variant(tiles, a.kb, ct);
+    *variant = default_variant(tiles, a.kb, ct, a.m);
     return 0;
   }
   return S;
