@@ -497,6 +497,21 @@ __global__ __launch_bounds__((MaxThreads<CT, U>::v)) void k_gemm(GemmArgs a) {
 #pragma unroll
       for (int i = NB - U; i < NB; ++i) keep(buf[i].ev);
     }
+  } else if constexpr (CT == 1 && XL && kPal) {
+    // The same ring as a loop over U statically indexed slots: slot u holds block b + u and is
+    // refilled with block b + u + U as soon as that block is computed.  Before the refill the
+    // slot's exponent registers are held until their load has retired (it was issued right
+    // after the block's weights, which compute just waited for).
+    auto keep = [](const u32x4& v) { asm volatile("" ::"v"(v.x), "v"(v.y), "v"(v.z), "v"(v.w)); };
+    for (int b = b0; b < b1; b += U) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (b + u < b1) compute(b + u, buf[u]);
+        keep(buf[u].ev);
+        load_main(b + u + U, b + u + U < b1, buf[u]);
+        load_ev(b + u + U, b + u + U < b1, buf[u]);
+      }
+    }
   } else {
     auto run_batch = [&](int b) {
 #pragma unroll
