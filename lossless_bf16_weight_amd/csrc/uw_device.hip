@@ -267,21 +267,25 @@ __host__ __device__ inline LdsLayout lds_layout(int nw, int ct, bool xl, int mv,
 // block loop is fully unrolled into a continuous prefetch ring: block i + U is requested just
 // before block i is computed, so U blocks stay in flight and, with no registers carried
 // around a loop, every wait covers exactly one block's loads.  NB == 0: batches of U blocks.
-template <int SRC, int CT, int U, int XL, int NB>
+// SHX (shared X): each wave owns a whole tile of its own (tile blockIdx.x * waves + wave, all
+// kb <= 64 blocks) instead of a K range of one tile; the workgroup's waves share one copy of
+// the X rows in LDS and need no cross-wave sum.
+template <int SRC, int CT, int U, int XL, int NB, int SHX>
 __global__ __launch_bounds__((MaxThreads<CT, U>::v)) void k_gemm(GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nw = blockDim.x >> 6;
-  const int t = blockIdx.x;
+  const int t = SHX ? (int)blockIdx.x * nw + wave : (int)blockIdx.x;
+  const bool tile_ok = t * 16 < a.n;  // SHX: the last workgroup may hold tiles past n
   const int r = lane & 15, g = lane >> 4;
   const int kb = a.kb;
-  const int b0 = (int)((int64_t)wave * kb / nw), b1 = (int)((int64_t)(wave + 1) * kb / nw);
+  const int b0 = SHX ? 0 : (int)((int64_t)wave * kb / nw), b1 = SHX ? kb : (int)((int64_t)(wave + 1) * kb / nw);
   const int nblk = b1 - b0;  // 1..64: the launcher keeps nw <= kb and every range within 64 blocks
   const int mcol0 = blockIdx.y * 16 * CT;
   const int mv = min(16 * CT, a.m - mcol0);  // valid X rows of this column block
   constexpr bool kPal = SRC <= SRC_PAL_LUT;
-  const LdsLayout lay = lds_layout(nw, CT, XL, mv, a.k);
+  const LdsLayout lay = lds_layout(SHX ? 1 : nw, CT, XL, mv, a.k);
   floatx4* red = reinterpret_cast<floatx4*>(smem + lay.red);
   uint8_t* sx = smem + lay.x;
 
@@ -306,13 +310,15 @@ __global__ __launch_bounds__((MaxThreads<CT, U>::v)) void k_gemm(GemmArgs a) {
     woff0 = row_ok ? (uint32_t)(r * a.k + g * 16) * 2 : kOob;
     woff1 = 0;
   } else {
-    wrs0 = make_rsrc(a.sm + tile_bytes, (uint32_t)a.k * 16);
+    const uint32_t tb = tile_ok ? (uint32_t)a.k * 16 : 0u;  // a tile past n reads zeros
+    const size_t base = tile_ok ? tile_bytes : 0;
+    wrs0 = make_rsrc(a.sm + base, tb);
     woff0 = lane * 16;
     if constexpr (SRC == SRC_EXP) {
-      wrs1 = make_rsrc(a.aux + tile_bytes, (uint32_t)a.k * 16);
+      wrs1 = make_rsrc(a.aux + base, tb);
       woff1 = lane * 16;
     } else {
-      wrs1 = make_rsrc(a.aux + tile_bytes / 2, (uint32_t)a.k * 8);
+      wrs1 = make_rsrc(a.aux + base / 2, tb / 2);
       woff1 = lane * 8;
     }
   }
@@ -435,27 +441,36 @@ __global__ __launch_bounds__((MaxThreads<CT, U>::v)) void k_gemm(GemmArgs a) {
   uint32_t fpre[4];
   __amdgpu_buffer_rsrc_t frs;
   if constexpr (kPal) {
-    frs = make_rsrc(a.flags + (size_t)t * kb, (uint32_t)kb * 2);
+    frs = make_rsrc(a.flags + (tile_ok ? (size_t)t * kb : 0), tile_ok ? (uint32_t)kb * 2 : 0u);
     wfl = __builtin_amdgcn_raw_buffer_load_b16(frs, lane < nblk ? (uint32_t)(b0 + lane) * 2 : kOob, 0, 0);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {  // flags of the tile's blocks before b0 (first 256)
       const int i = j * 64 + lane;
-      fpre[j] = __builtin_amdgcn_raw_buffer_load_b16(frs, i < b0 ? (uint32_t)i * 2 : kOob, 0, 0);
+      fpre[j] = SHX ? 0u : __builtin_amdgcn_raw_buffer_load_b16(frs, i < b0 ? (uint32_t)i * 2 : kOob, 0, 0);
     }
   }
-  if constexpr (XL) {  // X rows, 1 KB a DMA (the launcher requires k % 512 == 0)
-    const int per_row = a.k / 512;
-    for (int c = wave; c < mv * per_row; c += nw) {
-      const int mr = c / per_row, cc = c - mr * per_row;
+  // X rows, 1 KB (8 blocks of one row) a DMA; the launcher requires k % 512 == 0.  With shared
+  // X and an unrolled ring the rows are staged in parts of kXPart blocks: the first part here,
+  // the rest once the first weights are out, each part checked by a barrier before its first
+  // block (see the ring), so the start waits for 1/4 of X at k = 4096 instead of all of it.
+  constexpr bool kXParts = SHX && NB > 0 && XL;
+  constexpr int kXPart = 16;
+  const int per_row = a.k / 512;
+  auto stage_x = [&](int cc0, int cc1) {  // chunks [cc0, cc1) of every valid row
+    const int cpr = cc1 - cc0;
+    for (int c = wave; c < mv * cpr; c += nw) {
+      const int mr = c / cpr, cc = cc0 + (c - mr * cpr);
       lds_dma16(xrs, sx + (size_t)mr * xl_stride(a.k) + cc * 1024, (uint32_t)mr * a.k * 2 + cc * 1024 + lane * 16);
     }
-  }
+  };
+  if constexpr (XL) stage_x(0, kXParts ? min(kXPart / 8, per_row) : per_row);
 #pragma unroll
   for (int u = 0; u < U; ++u) load_main(b0 + u, u < nblk, buf[u]);
   uint32_t vbase = 0, nvt = 0;
   if constexpr (kPal) {  // scalar loads (before the barrier, which would turn them into vector loads)
-    vbase = a.vprefix[t];
-    nvt = a.vprefix[t + 1] - vbase;
+    const int tv = tile_ok ? t : 0;
+    vbase = a.vprefix[tv];
+    nvt = tile_ok ? a.vprefix[tv + 1] - vbase : 0u;
   }
   if constexpr (XL) {
     // This wave's X DMAs precede exactly the 2U weight loads above and loads retire in
@@ -476,6 +491,7 @@ __global__ __launch_bounds__((MaxThreads<CT, U>::v)) void k_gemm(GemmArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) load_ev(b0 + u, u < nblk, buf[u]);
   }
+  if constexpr (kXParts) stage_x(min(kXPart / 8, per_row), per_row);
 
   if constexpr (NB > 0) {
     // A block's verbatim-exponent registers are read only when the block is flagged; the
@@ -491,6 +507,15 @@ __global__ __launch_bounds__((MaxThreads<CT, U>::v)) void k_gemm(GemmArgs a) {
       }
       if constexpr (kPal)
         if (i >= U) keep(buf[i - U].ev);
+      if constexpr (kXParts) {
+        if (i > 0 && i % kXPart == 0) {
+          // X part i / kXPart was requested before block i's weights, so once this wave has
+          // waited for those (the empty asm use forces the wait here) its DMAs have landed;
+          // the barrier then covers every wave's.
+          if constexpr (SRC == SRC_BF16) keep(buf[i].w.w0); else keep(buf[i].w.s);
+          __builtin_amdgcn_s_barrier();
+        }
+      }
       compute(b0 + i, buf[i]);
     }
     if constexpr (kPal) {
@@ -536,9 +561,11 @@ __global__ __launch_bounds__((MaxThreads<CT, U>::v)) void k_gemm(GemmArgs a) {
     const int mm = mcol0 + 16 * c + (l & 15);
     if (mm < a.m) store_out4(a, mm, t * 16 + 4 * (l >> 4), v);
   };
-  if (nw == 1) {
+  if (nw == 1 || SHX) {
+    if (tile_ok) {
 #pragma unroll
-    for (int c = 0; c < CT; ++c) store(c, lane, acc[c]);
+      for (int c = 0; c < CT; ++c) store(c, lane, acc[c]);
+    }
     return;
   }
 #pragma unroll
@@ -1298,14 +1325,16 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* y, uint16_t* x, in
 // =========================================================================================
 // Kernel variants: kind 0 = per-tile kernel (waves split the tile's blocks; `unroll` blocks
 // a batch), kind 1 = multi-tile kernel (`waves` row tiles a workgroup, X batches of `unroll`
-// blocks in LDS, K split over workgroups).
+// blocks in LDS, K split over workgroups), kind 2 = per-tile kernel with shared X (`waves`
+// whole tiles a workgroup, all X rows in LDS once; M <= 16, k <= 4096, palette sources).
 struct Variant {
   int kind;
   int waves;
   int unroll;
 };
 static const Variant kVariants[] = {{0, 4, 8}, {0, 2, 8}, {0, 8, 8},  {0, 16, 8}, {0, 1, 8}, {0, 4, 4}, {0, 2, 4},
-                                    {0, 8, 4}, {0, 16, 4}, {0, 1, 4}, {1, 8, 4},  {1, 4, 4}, {1, 8, 2}, {1, 4, 2}};
+                                    {0, 8, 4}, {0, 16, 4}, {0, 1, 4}, {1, 8, 4},  {1, 4, 4}, {1, 8, 2}, {1, 4, 2},
+                                    {2, 2, 4}, {2, 4, 4}};
 static constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 static constexpr int kMtDefault = 10;   // {1, 8, 4}
 
@@ -1391,12 +1420,24 @@ struct Launch {
   int tiles, waves, unroll;
 };
 
-template <int SRC, int CT, int U, int XL, int NB>
+template <int SRC, int CT, int U, int XL, int NB, int SHX = 0>
 static hipError_t launch_gemm_t(const GemmArgs& a, const Launch& L, hipStream_t s) {
   const int gy = (a.m + 16 * CT - 1) / (16 * CT);
-  const size_t shm = lds_layout(L.waves, CT, XL, std::min(a.m, 16 * CT), a.k).total;
-  hipLaunchKernelGGL((k_gemm<SRC, CT, U, XL, NB>), dim3(L.tiles, gy), dim3(64 * L.waves), shm, s, a);
+  const size_t shm = lds_layout(SHX ? 1 : L.waves, CT, XL, std::min(a.m, 16 * CT), a.k).total;
+  const unsigned gx = SHX ? (unsigned)((L.tiles + L.waves - 1) / L.waves) : (unsigned)L.tiles;
+  hipLaunchKernelGGL((k_gemm<SRC, CT, U, XL, NB, SHX>), dim3(gx, gy), dim3(64 * L.waves), shm, s, a);
   return hipGetLastError();
+}
+
+// Shared-X launch: L.waves tiles a workgroup, each wave a whole tile row of kb blocks.
+template <int SRC>
+static hipError_t launch_gemm_shx(const GemmArgs& a, const Launch& L, hipStream_t s) {
+  switch (a.kb) {
+    case 16: return launch_gemm_t<SRC, 1, 4, 1, 16, 1>(a, L, s);
+    case 32: return launch_gemm_t<SRC, 1, 4, 1, 32, 1>(a, L, s);
+    case 64: return launch_gemm_t<SRC, 1, 4, 1, 64, 1>(a, L, s);
+    default: return launch_gemm_t<SRC, 1, 4, 1, 0, 1>(a, L, s);
+  }
 }
 
 // Fully unrolled ring (palette sources, X rows in LDS) for the per-wave block counts of the
@@ -1469,6 +1510,20 @@ static int plan_gemm(int src, const GemmArgs& a, int64_t tiles, int* variant, co
   return S;
 }
 
+// Largest dynamic LDS a workgroup may use on the current device (queried once per device).
+static int lds_limit() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kXlMaxBytes;
+  if (cache[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || v <= 0)
+      v = kXlMaxBytes;
+    cache[dev] = v;
+  }
+  return cache[dev];
+}
+
 static uw_status run_gemm(int src, const GemmArgs& a, int64_t tiles, int variant, float* part,
                           size_t part_bytes, hipStream_t s) {
   int ct = col_tiles(a.m);
@@ -1488,6 +1543,21 @@ static uw_status run_gemm(int src, const GemmArgs& a, int64_t tiles, int variant
   Launch L;
   L.tiles = (int)tiles;
   L.unroll = kVariants[variant].unroll;
+  if (kVariants[variant].kind == 2) {
+    // Shared X needs the palette ring's conditions and every X row of the call in one
+    // workgroup's LDS (up to the device's limit, so one such workgroup a CU at M = 16).
+    const int mv = std::min(a.m, 16);
+    const bool pal = src <= SRC_PAL_LUT;
+    if (ct == 1 && pal && a.kb <= 64 && a.k % 512 == 0 && (size_t)mv * xl_stride(a.k) <= (size_t)lds_limit()) {
+      L.waves = kVariants[variant].waves;
+      const hipError_t e = src == SRC_PAL_AFFINE ? launch_gemm_shx<SRC_PAL_AFFINE>(a, L, s)
+                                                 : launch_gemm_shx<SRC_PAL_LUT>(a, L, s);
+      if (e != hipSuccess) return fail(UW_E_HIP, "gemm launch: %s", hipGetErrorString(e));
+      return UW_OK;
+    }
+    variant = default_variant(tiles, a.kb, ct, a.m);
+    L.unroll = kVariants[variant].unroll;
+  }
   // Every wave's block range must fit one lane per block (<= 64 blocks).  Wider column tiles
   // and deeper batches allow fewer waves per workgroup; past that, use shallower batches and
   // 16-column tiles.
@@ -1712,6 +1782,9 @@ const char* uw_variant_name(int32_t variant) {
   if (variant < 0 || variant >= kNumVariants) return "";
   if (kVariants[variant].kind == 0)
     snprintf(names[variant], sizeof(names[variant]), "waves=%d unroll=%d", kVariants[variant].waves,
+             kVariants[variant].unroll);
+  else if (kVariants[variant].kind == 2)
+    snprintf(names[variant], sizeof(names[variant]), "shared-x tiles=%d unroll=%d", kVariants[variant].waves,
              kVariants[variant].unroll);
   else
     snprintf(names[variant], sizeof(names[variant]), "multitile tiles=%d unroll=%d", kVariants[variant].waves,

@@ -131,7 +131,8 @@ def test_gemm_all_pipelines(name, m):
         check_gemm(y, x, w)
 
 
-N_VARIANTS = 14
+N_VARIANTS = 16
+SHARED_X_VARIANTS = (14, 15)   # kind 2: whole tiles per wave, X rows shared in LDS
 
 
 def test_variant_count():
@@ -179,6 +180,27 @@ def test_gemm_long_k_every_variant(variant):
         yb = t.full((m, 70), float("nan"), dtype=t.float32, device="cuda")
         uw.uw_gemm_bf16(dev_u16(w), dev_u16(x), yb, m, variant)
         check_gemm(yb, x, w)
+
+
+@pytest.mark.parametrize("variant", SHARED_X_VARIANTS)
+@pytest.mark.parametrize("shape", [(200, 4096), (1000, 1024), (37, 2048)], ids=["200x4096", "1000x1024", "37x2048"])
+def test_gemm_shared_x(variant, shape):
+    """The shared-X per-tile kernel (each wave a whole tile, the workgroup's X rows staged once
+    in LDS) at every batch size it takes, 1..16: ragged tile counts (the last workgroup holds
+    tiles past n), verbatim segments, up to 131 KB of X in LDS at k = 4096, M = 16."""
+    t = torch()
+    n, k = shape
+    w = synth.small_gaussian(n, k, seed=17, plant_frac=0.05)["w"]
+    cm = uw.CompressedMatrix(w)
+    assert uw.uw_variant_name(variant).startswith("shared-x ")
+    for m in (1, 2, 5, 8, 16):
+        x = synth.gaussian_bf16(np.random.default_rng(500 + m), (m, k), 1.0)
+        y = t.full((m, n), float("nan"), dtype=t.float32, device="cuda")
+        uw.uw_gemm_variant(cm.d, dev_u16(x), y, m, uw.UW_PIPE_DIRECT_PALETTE, variant, None)
+        check_gemm(y, x, w)
+        y2 = t.full((m, n), float("nan"), dtype=t.float32, device="cuda")
+        uw.uw_gemm_variant(cm.d, dev_u16(x), y2, m, uw.UW_PIPE_TRANSCODE, variant, cm.workspace(m, uw.UW_PIPE_TRANSCODE))
+        check_gemm(y2, x, w)
 
 
 def test_shared_workspace_across_calls():
