@@ -705,25 +705,22 @@ __global__ __launch_bounds__(64 * R) void k_gemm_mt(GemmArgs a, float* part, int
     }
   }
 
-  // Verbatim bookkeeping of this slice: flags of block bs + j in lane j, and the tile-relative
-  // rank of its first verbatim segment.
-  uint32_t wfl = 0, wvp = 0;
-  __amdgpu_buffer_rsrc_t vrs = make_rsrc(a.vexp, 0);
+  // Verbatim bookkeeping of this slice: flags of block bs + j in lane j (wfl), and each block's
+  // rank among the tile's verbatim segments (wvp).  The flags are requested first; the ranks
+  // are computed once they are in, after the first batch's weights have gone out.
+  uint32_t wfl = 0, wvp = 0, fpre[4] = {0u, 0u, 0u, 0u};
+  __amdgpu_buffer_rsrc_t vrs = make_rsrc(a.vexp, 0), frs = make_rsrc(a.flags, 0);
   if constexpr (kPal) {
-    if (tile_ok) {
-      const uint16_t* fl = a.flags + (size_t)t * a.kb;
-      uint32_t before = 0;
-      for (int j = lane; j < bs; j += 64) before += (uint32_t)__popc((uint32_t)fl[j]);
-      before = wave_sum(before);
-      wfl = lane < be - bs ? (uint32_t)fl[bs + lane] : 0u;
-      const uint32_t v = (uint32_t)__popc(wfl);
-      wvp = before + wave_incl_scan(v, lane) - v;
-      const uint32_t v0 = a.vprefix[t];
-      vrs = make_rsrc(a.vexp + (size_t)v0 * 64, (a.vprefix[t + 1] - v0) * 64);
+    frs = make_rsrc(a.flags + (tile_ok ? (size_t)t * a.kb : 0), tile_ok ? (uint32_t)a.kb * 2 : 0u);
+    wfl = __builtin_amdgcn_raw_buffer_load_b16(frs, lane < be - bs ? (uint32_t)(bs + lane) * 2 : kOob, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {  // flags of the tile's blocks before the slice (first 256)
+      const int i = j * 64 + lane;
+      fpre[j] = __builtin_amdgcn_raw_buffer_load_b16(frs, i < bs ? (uint32_t)i * 2 : kOob, 0, 0);
     }
   }
 
-  auto load_block = [&](int b, MtSlot<SRC>& sl) {
+  auto load_w = [&](int b, MtSlot<SRC>& sl) {
     const bool ok = b < be;
     const uint32_t o0 = ok ? woff0 : kOob;
     if constexpr (SRC == SRC_BF16) {
@@ -735,11 +732,20 @@ __global__ __launch_bounds__(64 * R) void k_gemm_mt(GemmArgs a, float* part, int
     } else {
       sl.w.s = bload16_nt(wrs0, o0, b * 1024);
       sl.w.i = bload8_nt(wrs1, ok ? woff1 : kOob, b * 512);
+    }
+  };
+  auto load_ev = [&](int b, MtSlot<SRC>& sl) {
+    if constexpr (kPal) {
+      const bool ok = b < be;
       const int jb = ok ? b - bs : 0;
       const uint32_t f = __builtin_amdgcn_readlane(wfl, jb);
       const uint32_t rank = __builtin_amdgcn_readlane(wvp, jb) + (uint32_t)__popc(f & ((1u << r) - 1u));
       sl.ev = bload16(vrs, (ok && ((f >> r) & 1u)) ? rank * 64 + g * 16 : kOob);
     }
+  };
+  auto load_block = [&](int b, MtSlot<SRC>& sl) {
+    load_w(b, sl);
+    load_ev(b, sl);
   };
 
   constexpr bool kTwo = CT <= 2;   // a second accumulator set keeps back-to-back MFMAs independent
@@ -802,11 +808,39 @@ __global__ __launch_bounds__(64 * R) void k_gemm_mt(GemmArgs a, float* part, int
   // batch i's data is in place and batch i-1's X buffer is free.
   MtSlot<SRC> sa[U], sb[U];
   uint8_t* const xb1 = smem + C::kBufBytes;
-  load_batch(0, sa);
+  // Prologue in issue order: flags (above), X batch 0, the weights of batch 0, then the
+  // tile's verbatim base (scalar), the ranks (bit-sliced ballots) and batch 0's verbatim
+  // exponents -- no weight load waits on an earlier global load.
   issue_x(0, smem);
-  for (int i = 0; i < nbatch; i += 2) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) load_w(bs + u, sa[u]);
+  if constexpr (kPal) {
+    const int tv = tile_ok ? t : 0;
+    const uint32_t v0 = a.vprefix[tv];
+    const uint32_t nv = tile_ok ? a.vprefix[tv + 1] - v0 : 0u;
+    vrs = make_rsrc(a.vexp + (size_t)v0 * 64, nv * 64);
+    uint32_t before = (uint32_t)__popc(fpre[0]) + __popc(fpre[1]) + __popc(fpre[2]) + __popc(fpre[3]);
+    for (int j = 256; j < bs; j += 64) {  // tile rows of more than 256 + 64 blocks
+      const int i = j + lane;
+      before += __popc((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(frs, i < bs ? (uint32_t)i * 2 : kOob, 0, 0));
+    }
+    uint32_t tot;
+    wave_excl_prefix_small<9>(before, &tot);
+    wvp = tot + wave_excl_prefix_small<5>((uint32_t)__popc(wfl), &tot);
+#pragma unroll
+    for (int u = 0; u < U; ++u) load_ev(bs + u, sa[u]);
+    // Batch 0 ready except, at most, its verbatim exponents (the last U loads; a flagged block
+    // waits for its own when it reads them).
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(U));
+  } else {
     __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+  }
+  __syncthreads();
+  for (int i = 0; i < nbatch; i += 2) {
+    if (i > 0) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
     if (i + 1 < nbatch) {
       load_batch(i + 1, sb);
       issue_x(i + 1, xb1);
