@@ -188,6 +188,8 @@ def diagnostic(args):
     steps, warmup = min(args.steps, 200), min(args.warmup, 20)
     if args.workload == "stack":
         return stack_step(args, steps, warmup)
+    if args.workload == "stack-hard":
+        return stack_hard_step(args, steps, warmup)
     c = {"down": synth.config3, "heavy": synth.config5, "small": synth.config1}[args.workload]()
     ms = {"down": (1, 8, 16, 32, 64), "heavy": (128,), "small": (1,)}[args.workload]
     w, x_all = c["w"], c["x"]
@@ -297,6 +299,68 @@ def stack_step(args, steps, warmup):
             "torch_bf16_us_per_step": round(us_b, 1), "speedup_vs_torch_bf16": round(us_b / us, 3)}
 
 
+def stack_hard_step(args, steps, warmup):
+    """The 32-layer stack at M = 16 with hard layers (bundle only resident, index streams decoded
+    ahead on a side stream by libuw's scheduler) and easy layers (direct-palette form): step time
+    and weight footprint for 0, 1/4, 1/2 and all layers hard, each step checked bit-identical to
+    the plain fused step; and the same with the decodes on the main stream (no overlap)."""
+    import torch
+    from concurrent.futures import ThreadPoolExecutor
+    import lossless_bf16_weight_amd as uw
+    from lossless_bf16_weight_amd import autotune, synth
+    from lossless_bf16_weight_amd.stack import HardEasyStack, MLPStack
+    meta = synth.config4_meta()
+    layers = len(meta["stds"])
+    t0 = time.time()
+    jobs = [(l, j) for l in range(layers) for j in range(3)]
+    easy, bundles = [], []
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        for w in ex.map(lambda lj: synth.config4_matrix(meta, *lj), jobs):
+            cm = uw.CompressedMatrix(w)
+            easy.append(cm)
+            bundles.append(cm.blob)
+    log("stack built in %.1fs" % (time.time() - t0))
+    for lj in ((0, 0), (0, 2)):
+        tuner = autotune.Tuner(synth.config4_matrix(meta, *lj), bf16=False)
+        tuner.tune([16], pipelines=(uw.UW_PIPE_DIRECT_PALETTE,), bf16=False, log=log).apply()
+        del tuner
+    torch.cuda.empty_cache()
+    x = torch.from_numpy(meta["x"].view(np.int16)).cuda()
+    plain = MLPStack(16, 4096, 14336)
+    for l in range(layers):
+        plain.add_layer(*easy[3 * l:3 * l + 3])
+    ref = plain.step(x, pipeline=uw.UW_PIPE_DIRECT_PALETTE, check=True).clone()
+    tot, _ = time_launches(lambda i: plain.step(x, pipeline=uw.UW_PIPE_DIRECT_PALETTE, check=False), 1, steps, warmup,
+                           torch.cuda.current_stream())
+    res = {"plain_us": round(tot * 1e3 / steps, 1), "plain_bits_per_weight": round(8 * plain.resident_bytes() /
+                                                                                  plain.weight_count(), 4)}
+    del plain
+    hard_cms = {}
+    for name, hard in (("none", []), ("quarter", [l for l in range(layers) if l % 4 == 3]),
+                       ("half", [l for l in range(layers) if l % 2 == 1]), ("all", list(range(layers)))):
+        for l in hard:
+            for j in range(3):
+                if (l, j) not in hard_cms:
+                    hard_cms[(l, j)] = uw.CompressedMatrix(None, blob=bundles[3 * l + j], keep_index=False)
+        mats = [tuple(hard_cms[(l, j)] if l in hard else easy[3 * l + j] for j in range(3)) for l in range(layers)]
+        row = {"hard_layers": len(hard)}
+        for overlap in (True, False) if hard else (True,):
+            st = HardEasyStack(16, 4096, 14336, mats, hard_layers=hard, overlap=overlap)
+            out = st.step(x, check=True)
+            assert torch.equal(out, ref), "scheduled step (%s, overlap=%s) differs from the plain step" % (name, overlap)
+            tot, _ = time_launches(lambda i: st.step(x, check=False), 1, steps, warmup, torch.cuda.current_stream())
+            torch.cuda.synchronize()
+            uw.uw_check(st.dws)
+            row["us_overlap" if overlap else "us_main_stream"] = round(tot * 1e3 / steps, 1)
+            row["bits_per_weight"] = round(8 * st.resident_bytes() / st.weight_count(), 4)
+            row["weight_gb"] = round(st.resident_bytes() / 1e9, 3)
+            st.close()
+            del st
+        res[name] = row
+        log("stack-hard %s: %s" % (name, row))
+    return {"diagnostic": "stack-hard", "layers": layers, "m": 16, "results": res}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -309,9 +373,10 @@ def main():
                     help="BF16 GEMV variant with --variant (default: the library's choice for the shape)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run three device copies of 512 MiB (HBM counter calibration) and exit")
-    ap.add_argument("--workload", default="gate", choices=("gate", "down", "heavy", "stack", "small"),
-                    help="gate (default: the headline line); down, heavy, stack, small: diagnostic lines for the "
-                         "down_proj batch sweep, the 8192^2 heavy-tail matrix at M=128, the 32-layer stack and "
+    ap.add_argument("--workload", default="gate", choices=("gate", "down", "heavy", "stack", "stack-hard", "small"),
+                    help="gate (default: the headline line); down, heavy, stack, stack-hard, small: diagnostic "
+                         "lines for the down_proj batch sweep, the 8192^2 heavy-tail matrix at M=128, the 32-layer "
+                         "stack, the same stack with hard (bundle-only) layers decoded ahead on a side stream, and "
                          "the 1024^2 single-matrix case")
     args = ap.parse_args()
     if args.copy_calibration:

@@ -254,6 +254,48 @@ uw_status uw_gemm_rmsnorm(const uw_dmat* d, const uint16_t* x, float* y, uint16_
                           float eps, int32_t pipeline, int32_t variant, void* ws, size_t ws_bytes,
                           hipStream_t s);
 
+/* Hard/easy MLP decode step (hard/easy-layer paragraphs of the post: a "hard" layer keeps only
+ * its Huffman bundle resident and is decoded ahead of use, off the critical path, while the GPU
+ * computes the layers before it; an "easy" layer is held in the direct-palette form).
+ *
+ * A step runs `layers` layers of the MLP stack (gate, up: [inter, hidden]; down: [hidden, inter]):
+ *   g = x gate^T; h = bf16(silu(g) * (x up^T)) (uw_gemm_swiglu); y = h down^T and
+ *   x' = bf16(y / sqrt(mean(y^2) + eps)) (uw_gemm_rmsnorm) -- the same calls, kernels and bits as
+ * issuing those entry points one by one with UW_PIPE_DIRECT_PALETTE and the autotuned variant.
+ * Matrix j of layer l is mats[3l + j] (j = 0 gate, 1 up, 2 down).  hard[3l + j] != 0: the view's
+ * own index stream is not used (it may be unbound); its 4-bit index stream is decoded on `side`
+ * into one of two slot sets (hard layers alternate between them) while `main` runs the layers
+ * before it, with events ordering decode -> use -> reuse.  Easy matrices need an index stream
+ * bound at uw_dmat_bind.  At most two hard layers are decoded ahead.
+ *
+ * Caller-owned device buffers (borrowed until uw_sched_release):
+ *   slots     2 * 3 * slot_bytes; slot_bytes >= idx_bytes of every hard matrix (uw_info)
+ *   g         m * inter fp32 (16-byte aligned);  h  m * inter BF16 (8-byte aligned)
+ *   y         m * hidden fp32;  xo  2 * m * hidden BF16: the two ping-pong layer outputs
+ *   ws        main-stream workspace: at least uw_workspace_size(m, UW_PIPE_DIRECT_PALETTE) of
+ *             every matrix (K-slice partial sums; may be NULL: no K split)
+ *   dws       side-stream error word, >= 256 bytes, zeroed; uw_check(dws) reports a corrupt
+ *             bitstream found by a decode
+ * The scheduler holds host state and four HIP events (no device memory): the caller allocates
+ * uw_sched_size() bytes for it and ends its use with uw_sched_release.  Errors: UW_E_ARG (null
+ * pointer, bad shape or stream), UW_E_SHAPE (a matrix not of its layer shape, m outside
+ * [1, 256]), UW_E_WORKSPACE (slot_bytes or a buffer too small), UW_E_NOMEM, UW_E_HIP; on an
+ * error nothing was launched. */
+typedef struct uw_sched uw_sched;
+size_t uw_sched_size(void);
+uw_status uw_sched_init(uw_sched* s, int32_t layers, int32_t m, int32_t hidden, int32_t inter,
+                        const uw_dmat* const* mats, const uint8_t* hard, void* slots,
+                        size_t slot_bytes, float* g, uint16_t* h, float* y, uint16_t* xo,
+                        void* ws, size_t ws_bytes, void* dws, size_t dws_bytes, float eps,
+                        hipStream_t main_stream, hipStream_t side_stream);
+/* One step from x (device BF16 [m, hidden]); *out receives the device address of the last
+ * layer's output (one of the two halves of xo).  Asynchronous on the main stream; the side
+ * stream's decodes are ordered by events, and the next step's first decodes wait for this
+ * step's last use of their slots. */
+uw_status uw_sched_step(uw_sched* s, const uint16_t* x, uint16_t** out);
+/* Releases the events and host state (waits for nothing: the caller synchronises first). */
+uw_status uw_sched_release(uw_sched* s);
+
 #ifdef __cplusplus
 }
 #endif

@@ -31,7 +31,8 @@ EXPORTS = ("uw_last_error", "uw_version", "uw_build_palette", "uw_encode_bound",
            "uw_transcode_palette", "uw_decode_exponents", "uw_gemm", "uw_gemm_variant", "uw_gemm_bf16",
            "uw_variant_count", "uw_variant_name", "uw_check", "uw_autotune_load", "uw_autotune_set",
            "uw_autotune_get", "uw_autotune_set_variant", "uw_autotune_get_variant", "uw_autotune_clear", "uw_swiglu",
-           "uw_gemm_swiglu", "uw_gemm_rmsnorm", "uw_rmsnorm")
+           "uw_gemm_swiglu", "uw_gemm_rmsnorm", "uw_rmsnorm", "uw_sched_size", "uw_sched_init", "uw_sched_step",
+           "uw_sched_release")
 
 
 class UwError(RuntimeError):
@@ -104,6 +105,11 @@ def lib():
         "uw_gemm_swiglu": (_I32, [_P, _P, _P, _P, _I32, _I32, _I32, _P, _S, _P]),
         "uw_gemm_rmsnorm": (_I32, [_P, _P, _P, _P, _I32, _F, _I32, _I32, _P, _S, _P]),
         "uw_rmsnorm": (_I32, [_P, _P, _I32, _I32, _F, _P]),
+        "uw_sched_size": (_S, []),
+        "uw_sched_init": (_I32, [_P, _I32, _I32, _I32, _I32, _P, _P, _P, _S, _P, _P, _P, _P, _P, _S, _P, _S, _F,
+                                 _P, _P]),
+        "uw_sched_step": (_I32, [_P, _P, ctypes.POINTER(ctypes.c_void_p)]),
+        "uw_sched_release": (_I32, [_P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -336,6 +342,48 @@ def uw_rmsnorm(y, x, eps=1e-5, stream=None):
     m, n = y.shape
     _check(lib().uw_rmsnorm(_dev(y, "y", 4 * m * n, ("float32",)), _dev(x, "x", 2 * m * n, _U16), m, n, eps,
                             _stream(stream)))
+
+
+class Sched:
+    """A bound uw_sched (hard/easy MLP step) plus the tensors it borrows.  mats: 3*layers DMat
+    (gate, up, down per layer); hard: 3*layers flags; buffers as uw_sched_init documents."""
+
+    def __init__(self, mats, hard, m, hidden, inter, slots, slot_bytes, g, h, y, xo, ws, dws, eps=1e-5,
+                 main_stream=None, side_stream=None):
+        layers = len(mats) // 3
+        if len(mats) != 3 * layers or len(hard) != len(mats) or layers < 1:
+            raise ValueError("mats and hard must hold 3 entries a layer")
+        self.keep = (mats, slots, g, h, y, xo, ws, dws)
+        self.buf = ctypes.create_string_buffer(lib().uw_sched_size())
+        self.views = (ctypes.c_void_p * len(mats))(*[ctypes.addressof(d.handle) for d in mats])
+        self.hard = (ctypes.c_uint8 * len(hard))(*[1 if f else 0 for f in hard])
+        nslot = 6 * slot_bytes if any(hard) else 0
+        _check(lib().uw_sched_init(
+            self.buf, layers, m, hidden, inter, self.views, self.hard,
+            _dev(slots, "slots", nslot, optional=not any(hard)), slot_bytes,
+            _dev(g, "g", 4 * m * inter, ("float32",)), _dev(h, "h", 2 * m * inter, _U16),
+            _dev(y, "y", 4 * m * hidden, ("float32",)), _dev(xo, "xo", 4 * m * hidden, _U16),
+            _dev(ws, "ws", 0, optional=True), _nbytes(ws), _dev(dws, "dws", 256), _nbytes(dws), eps,
+            _stream(main_stream), _stream(side_stream)))
+        self.live = True
+
+    def step(self, x):
+        """Returns the device address of the last layer's output (inside xo)."""
+        out = ctypes.c_void_p()
+        m_hidden = self.keep[5].numel() // 2
+        _check(lib().uw_sched_step(self.buf, _dev(x, "x", 2 * m_hidden, _U16), ctypes.byref(out)))
+        return out.value
+
+    def release(self):
+        if self.live:
+            _check(lib().uw_sched_release(self.buf))
+            self.live = False
+
+    def __del__(self):
+        try:
+            self.release()
+        except Exception:
+            pass
 
 
 # ----------------------------------------------------------------------------------------

@@ -18,6 +18,8 @@
 #include <algorithm>
 #include <cstdio>
 #include <cstring>
+#include <new>
+#include <vector>
 
 #include "uw_internal.h"
 
@@ -2025,6 +2027,203 @@ uw_status uw_rmsnorm(const float* y, uint16_t* x, int32_t m, int32_t n, float ep
   if (!y || !x || m < 1 || n < 1) return fail(UW_E_ARG, "bad argument");
   const hipError_t e = launch_rmsnorm(y, x, m, n, eps, s);
   if (e != hipSuccess) return fail(UW_E_HIP, "rmsnorm launch: %s", hipGetErrorString(e));
+  clear_error();
+  return UW_OK;
+}
+
+}  // extern "C"
+
+// =========================================================================================
+// Hard/easy scheduler (hard/easy-layer paragraphs of the post): hard layers keep only their
+// bundle resident; their index streams are decoded on a side stream into one of two slot
+// sets while the main stream computes the layers before them.
+//   side:  [wait use_done[i%2]] decode hard layer i -> slot set i%2, record dec_done[i%2]
+//   main:  ... [wait dec_done[i%2]] gate, up+SwiGLU, down+RMS norm of hard layer i,
+//          record use_done[i%2], then enqueue the side work of hard layer i+2
+// Two hard layers are decoded ahead at most; use_done is recorded once at set-up so that the
+// first waits of every step (which cover the previous step's last uses) are always valid.
+// =========================================================================================
+namespace uw {
+struct SchedImpl {
+  int layers = 0, m = 0, hidden = 0, inter = 0;
+  std::vector<uw_dmat> views;  // copies of the caller's views; hard ones index into a slot
+  std::vector<uint8_t> hard;
+  std::vector<int> hard_layers;  // layers with a hard matrix, in order
+  size_t slot_bytes = 0;
+  float* g = nullptr;
+  uint16_t* h = nullptr;
+  float* y = nullptr;
+  uint16_t* xo = nullptr;
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  void* dws = nullptr;
+  size_t dws_bytes = 0;
+  float eps = 1e-5f;
+  hipStream_t main = nullptr, side = nullptr;
+  hipEvent_t dec_done[2] = {nullptr, nullptr}, use_done[2] = {nullptr, nullptr};
+};
+constexpr uint64_t kSchedMagic = 0x3130484353575555ull;  // "UUWSCH01"
+}  // namespace uw
+
+struct uw_sched {
+  uint64_t magic;
+  uw::SchedImpl* impl;
+};
+
+namespace uw {
+static void sched_free_events(SchedImpl* S) {
+  for (int i = 0; i < 2; ++i) {
+    if (S->dec_done[i]) hipEventDestroy(S->dec_done[i]);
+    if (S->use_done[i]) hipEventDestroy(S->use_done[i]);
+    S->dec_done[i] = S->use_done[i] = nullptr;
+  }
+}
+
+// Side-stream work of hard layer i: wait until the slot set's previous user is done, decode
+// the layer's hard matrices into it, signal.
+static uw_status sched_issue_decode(SchedImpl* S, int i) {
+  const int set = i & 1, l = S->hard_layers[i];
+  if (hipStreamWaitEvent(S->side, S->use_done[set], 0) != hipSuccess) return fail(UW_E_HIP, "stream wait failed");
+  for (int j = 0; j < 3; ++j) {
+    if (!S->hard[3 * l + j]) continue;
+    const uw_dmat* d = &S->views[3 * l + j];
+    const uw_status st = run_decode(d, DEC_IDX, d->idx, S->dws, S->dws_bytes, S->side);
+    if (st) return st;
+  }
+  if (hipEventRecord(S->dec_done[set], S->side) != hipSuccess) return fail(UW_E_HIP, "event record failed");
+  return UW_OK;
+}
+}  // namespace uw
+
+extern "C" {
+
+size_t uw_sched_size(void) { return sizeof(uw_sched); }
+
+uw_status uw_sched_init(uw_sched* s, int32_t layers, int32_t m, int32_t hidden, int32_t inter,
+                        const uw_dmat* const* mats, const uint8_t* hard, void* slots, size_t slot_bytes, float* g,
+                        uint16_t* h, float* y, uint16_t* xo, void* ws, size_t ws_bytes, void* dws, size_t dws_bytes,
+                        float eps, hipStream_t main_stream, hipStream_t side_stream) {
+  if (!s || !mats || !hard || !g || !h || !y || !xo || !dws) return fail(UW_E_ARG, "null argument");
+  s->magic = 0;
+  s->impl = nullptr;
+  if (layers < 1 || hidden < 1 || inter < 1) return fail(UW_E_ARG, "bad stack shape");
+  if (m < 1 || m > UW_MAX_M) return fail(UW_E_SHAPE, "m=%d outside [1, %d]", m, UW_MAX_M);
+  if ((reinterpret_cast<uintptr_t>(g) & 15) || (reinterpret_cast<uintptr_t>(h) & 7))
+    return fail(UW_E_ARG, "g must be 16-byte and h 8-byte aligned");
+  if (dws_bytes < (size_t)kErrBytes) return fail(UW_E_WORKSPACE, "the side error word needs %d bytes", kErrBytes);
+  int n_hard = 0;
+  for (int l = 0; l < layers; ++l) {
+    for (int j = 0; j < 3; ++j) {
+      const uw_dmat* d = mats[3 * l + j];
+      uw_status st = check_dmat(d);
+      if (st) return st;
+      const int64_t en = j < 2 ? inter : hidden, ek = j < 2 ? hidden : inter;
+      if (d->info.n != en || d->info.k != ek)
+        return fail(UW_E_SHAPE, "layer %d matrix %d is %lldx%lld, expected %lldx%lld", l, j, (long long)d->info.n,
+                    (long long)d->info.k, (long long)en, (long long)ek);
+      if (hard[3 * l + j]) {
+        ++n_hard;
+        if (d->info.idx_bytes > slot_bytes)
+          return fail(UW_E_WORKSPACE, "slot_bytes %zu < %llu index bytes of layer %d matrix %d", slot_bytes,
+                      (unsigned long long)d->info.idx_bytes, l, j);
+      } else if (!d->idx) {
+        return fail(UW_E_ARG, "layer %d matrix %d is easy but has no index stream bound", l, j);
+      }
+    }
+  }
+  if (n_hard && !slots) return fail(UW_E_ARG, "hard matrices need slots");
+  uw::SchedImpl* S = new (std::nothrow) uw::SchedImpl();
+  if (!S) return fail(UW_E_NOMEM, "host allocation failed");
+  S->layers = layers;
+  S->m = m;
+  S->hidden = hidden;
+  S->inter = inter;
+  S->views.resize(3 * (size_t)layers);
+  S->hard.assign(hard, hard + 3 * (size_t)layers);
+  for (int l = 0; l < layers; ++l) {
+    bool any = false;
+    for (int j = 0; j < 3; ++j) {
+      S->views[3 * l + j] = *mats[3 * l + j];
+      any = any || hard[3 * l + j];
+    }
+    if (any) {  // slot set by this hard layer's position among the hard layers
+      const int set = (int)(S->hard_layers.size() & 1);
+      for (int j = 0; j < 3; ++j)
+        if (hard[3 * l + j])
+          S->views[3 * l + j].idx = reinterpret_cast<uint8_t*>(slots) + ((size_t)set * 3 + j) * slot_bytes;
+      S->hard_layers.push_back(l);
+    }
+  }
+  S->slot_bytes = slot_bytes;
+  S->g = g;
+  S->h = h;
+  S->y = y;
+  S->xo = xo;
+  S->ws = ws;
+  S->ws_bytes = ws ? ws_bytes : 0;
+  S->dws = dws;
+  S->dws_bytes = dws_bytes;
+  S->eps = eps;
+  S->main = main_stream;
+  S->side = side_stream;
+  for (int i = 0; i < 2; ++i) {
+    if (hipEventCreateWithFlags(&S->dec_done[i], hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&S->use_done[i], hipEventDisableTiming) != hipSuccess ||
+        hipEventRecord(S->use_done[i], S->main) != hipSuccess) {
+      uw::sched_free_events(S);
+      delete S;
+      return fail(UW_E_HIP, "event set-up failed");
+    }
+  }
+  s->impl = S;
+  s->magic = uw::kSchedMagic;
+  clear_error();
+  return UW_OK;
+}
+
+uw_status uw_sched_step(uw_sched* s, const uint16_t* x, uint16_t** out) {
+  if (!s || s->magic != uw::kSchedMagic || !s->impl) return fail(UW_E_ARG, "scheduler is not initialised");
+  if (!x || !out) return fail(UW_E_ARG, "null argument");
+  uw::SchedImpl* S = s->impl;
+  const int H = (int)S->hard_layers.size();
+  uw_status st = UW_OK;
+  for (int i = 0; i < std::min(H, 2) && !st; ++i) st = uw::sched_issue_decode(S, i);
+  if (st) return st;
+  const uint16_t* cur = x;
+  int hi = 0;
+  for (int l = 0; l < S->layers; ++l) {
+    uint16_t* o = S->xo + (size_t)(l & 1) * S->m * S->hidden;
+    const bool is_hard = hi < H && S->hard_layers[hi] == l;
+    if (is_hard && hipStreamWaitEvent(S->main, S->dec_done[hi & 1], 0) != hipSuccess)
+      return fail(UW_E_HIP, "stream wait failed");
+    const uw_dmat* v = &S->views[3 * (size_t)l];
+    st = gemm_entry(&v[0], cur, S->g, nullptr, nullptr, nullptr, 0.f, S->m, UW_PIPE_DIRECT_PALETTE, -1, S->ws,
+                        S->ws_bytes, S->main);
+    if (!st)
+      st = gemm_entry(&v[1], cur, nullptr, S->g, S->h, nullptr, 0.f, S->m, UW_PIPE_DIRECT_PALETTE, -1, S->ws,
+                          S->ws_bytes, S->main);
+    if (!st)
+      st = gemm_entry(&v[2], S->h, S->y, nullptr, nullptr, o, S->eps, S->m, UW_PIPE_DIRECT_PALETTE, -1, S->ws,
+                          S->ws_bytes, S->main);
+    if (st) return st;
+    if (is_hard) {
+      if (hipEventRecord(S->use_done[hi & 1], S->main) != hipSuccess) return fail(UW_E_HIP, "event record failed");
+      if (hi + 2 < H && (st = uw::sched_issue_decode(S, hi + 2))) return st;
+      ++hi;
+    }
+    cur = o;
+  }
+  *out = const_cast<uint16_t*>(cur);
+  clear_error();
+  return UW_OK;
+}
+
+uw_status uw_sched_release(uw_sched* s) {
+  if (!s || s->magic != uw::kSchedMagic || !s->impl) return fail(UW_E_ARG, "scheduler is not initialised");
+  uw::sched_free_events(s->impl);
+  delete s->impl;
+  s->impl = nullptr;
+  s->magic = 0;
   clear_error();
   return UW_OK;
 }

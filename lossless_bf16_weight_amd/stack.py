@@ -17,8 +17,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import (UW_PIPE_AUTO, CompressedMatrix, uw_check, uw_gemm, uw_gemm_rmsnorm, uw_gemm_swiglu, uw_rmsnorm,
-               uw_swiglu, uw_workspace_size)
+from . import (UW_PIPE_AUTO, UW_PIPE_DIRECT_PALETTE, CompressedMatrix, Sched, uw_check, uw_gemm, uw_gemm_rmsnorm,
+               uw_gemm_swiglu, uw_rmsnorm, uw_swiglu, uw_workspace_size)
 
 
 class MLPStack:
@@ -99,3 +99,77 @@ def as_bf16_bits(t):
     """Host uint16 view of a device or host int16 tensor/array."""
     a = t if isinstance(t, np.ndarray) else t.cpu().numpy()
     return a.view(np.uint16)
+
+
+class HardEasyStack:
+    """The same MLP stack with hard and easy layers (hard/easy-layer paragraphs of the Unweight
+    post): an easy matrix holds its direct-palette index stream (resident 12.06 bits a weight on
+    the MLP shapes); a hard one holds only its Huffman bundle (10.70 bits a weight) and its index
+    stream is decoded into one of two slot sets on a side stream while the main stream computes
+    the layers before it (libuw's uw_sched_*: the ordering lives in the library, events between
+    the streams).  Outputs are bit-identical to MLPStack.step (same kernels on the same index
+    bits).  hard_layers: the layer indices whose three matrices are hard."""
+
+    def __init__(self, m, hidden, inter, matrices, hard_layers=(), device="cuda:0", eps=1e-5, chunk=0,
+                 overlap=True):
+        import torch
+        self.m, self.hidden, self.inter, self.eps = m, hidden, inter, eps
+        self.dev = torch.device(device)
+        self.hard_layers = sorted(set(int(l) for l in hard_layers))
+        self.layers = []
+        hard = []
+        for l, (gw, uw_, dw) in enumerate(matrices):
+            is_hard = l in self.hard_layers
+            mats = []
+            for w in (gw, uw_, dw):
+                if isinstance(w, CompressedMatrix):
+                    if is_hard and w.idx is not None:
+                        raise ValueError("layer %d is hard: give its matrices without an index stream" % l)
+                    mats.append(w)
+                else:
+                    mats.append(CompressedMatrix(w, chunk=chunk, device=self.dev, keep_index=not is_hard))
+            self.layers.append(tuple(mats))
+            hard += [is_hard] * 3
+        for l in self.hard_layers:
+            if l >= len(self.layers):
+                raise ValueError("hard layer %d past the %d layers" % (l, len(self.layers)))
+        flat = [cm for lay in self.layers for cm in lay]
+        self.slot_bytes = max([int(cm.info["idx_bytes"]) for cm, f in zip(flat, hard) if f] or [0])
+        self.slot_bytes = (self.slot_bytes + 255) // 256 * 256
+        self.slots = torch.empty(6 * self.slot_bytes, dtype=torch.uint8, device=self.dev) if self.slot_bytes else None
+        self.g = torch.empty((m, inter), dtype=torch.float32, device=self.dev)
+        self.h = torch.empty((m, inter), dtype=torch.int16, device=self.dev)
+        self.y = torch.empty((m, hidden), dtype=torch.float32, device=self.dev)
+        self.xo = torch.empty((2, m, hidden), dtype=torch.int16, device=self.dev)
+        need = max(uw_workspace_size(cm.d, m, UW_PIPE_DIRECT_PALETTE) for cm in flat)
+        self.ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=self.dev) if need else None
+        self.dws = torch.zeros(64, dtype=torch.int32, device=self.dev)
+        # overlap=False decodes on the main stream (the same ordering, no concurrency): the
+        # baseline the side stream is measured against.  Streams keep the default priority.
+        self.side = torch.cuda.Stream(device=self.dev) if overlap else torch.cuda.current_stream(self.dev)
+        self.sched = Sched([cm.d for cm in flat], hard, m, hidden, inter, self.slots, self.slot_bytes, self.g, self.h,
+                           self.y, self.xo, self.ws, self.dws, eps, torch.cuda.current_stream(self.dev), self.side)
+
+    def step(self, x, check=True):
+        """One decode step from x (device int16 [m, hidden], BF16 bits) on the current stream
+        (the one bound at construction).  Returns the output half of xo."""
+        addr = self.sched.step(x)
+        out = self.xo[0] if addr == self.xo[0].data_ptr() else self.xo[1]
+        if check:
+            import torch
+            torch.cuda.synchronize(self.dev)
+            uw_check(self.dws)
+        return out
+
+    def resident_bytes(self):
+        """Device bytes the weights need: the resident direct-palette form of easy matrices, the
+        bundle of hard ones, and the two slot sets."""
+        easy = sum(cm.resident_bytes() for l, lay in enumerate(self.layers) if l not in self.hard_layers for cm in lay)
+        hard = sum(cm.bundle_bytes() for l, lay in enumerate(self.layers) if l in self.hard_layers for cm in lay)
+        return easy + hard + (0 if self.slots is None else self.slots.numel())
+
+    def weight_count(self):
+        return sum(cm.n * cm.k for lay in self.layers for cm in lay)
+
+    def close(self):
+        self.sched.release()

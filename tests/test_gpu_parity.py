@@ -444,3 +444,33 @@ def test_gemm_rmsnorm_equals_unfused(name):
                     what = "m=%d pipeline %d variant %d ws %s" % (m, pipe, variant, "yes" if ws is not None else "no")
                     assert t.equal(y, y_ref), what
                     assert t.equal(xn, xn_ref), what
+
+
+@pytest.mark.parametrize("m", [1, 16])
+@pytest.mark.parametrize("hard", [(), (0,), (1, 2), (3,), (0, 1, 2, 3)], ids=["none", "first", "middle", "last", "all"])
+def test_hard_easy_stack_equals_plain(m, hard):
+    """The hard/easy scheduler (uw_sched_*: hard layers keep only their bundle, their index
+    streams decoded on a side stream into two alternating slot sets ahead of use) gives the
+    same bits as the plain fused step on the same matrices, for three steps in a row (each
+    step's first decodes reuse slots the previous step's last hard layers used)."""
+    t = torch()
+    from lossless_bf16_weight_amd.stack import HardEasyStack, MLPStack
+    rng = np.random.default_rng(21)
+    hidden, inter, layers = 256, 704, 4
+    mats = [(synth.gaussian_bf16(rng, (inter, hidden), 0.03), synth.gaussian_bf16(rng, (inter, hidden), 0.03),
+             synth.gaussian_bf16(rng, (hidden, inter), 0.02)) for _ in range(layers)]
+    plain = MLPStack(m, hidden, inter)
+    for lay in mats:
+        plain.add_layer(*lay)
+    sched = HardEasyStack(m, hidden, inter, mats, hard_layers=hard)
+    for l, lay in enumerate(sched.layers):
+        assert all((cm.idx is None) == (l in hard) for cm in lay)
+    x = dev_u16(synth.gaussian_bf16(rng, (m, hidden), 1.0))
+    xa, xb = x.clone(), x.clone()
+    for step in range(3):
+        a = plain.step(xa, pipeline=uw.UW_PIPE_DIRECT_PALETTE, fused=True).clone()
+        b = sched.step(xb).clone()
+        assert t.equal(a, b), "m=%d hard=%s step %d" % (m, hard, step)
+        xa, xb = a, b
+    assert sched.resident_bytes() < plain.resident_bytes() + 6 * sched.slot_bytes + 1
+    sched.close()

@@ -253,3 +253,28 @@ def test_autotune_nearest_batch_size():
             uw.uw_autotune_get(n, k, 0)
     finally:
         uw.uw_autotune_clear()
+
+
+def test_sched_rejects_bad_arguments_before_any_launch():
+    """uw_sched_init validates on the host (null buffers, shapes, the side error word) and
+    uw_sched_step refuses a scheduler that was never initialised; neither touches a GPU."""
+    import ctypes
+    L = uw.lib()
+    buf = ctypes.create_string_buffer(L.uw_sched_size())
+    one = (ctypes.c_void_p * 3)()
+    hard = (ctypes.c_uint8 * 3)()
+    p = ctypes.c_void_p(256)   # never dereferenced: validation fails first
+    args = [buf, 1, 1, 64, 64, one, hard, None, 0, p, p, p, p, None, 0, p, 256, 1e-5, None, None]
+    assert L.uw_sched_init(*args) == uw.UW_E_ARG          # views are null: check_dmat refuses
+    bad = list(args)
+    bad[9] = None                                             # g
+    assert L.uw_sched_init(*bad) == uw.UW_E_ARG
+    bad = list(args)
+    bad[2] = 0                                                # m
+    assert L.uw_sched_init(*bad) == uw.UW_E_SHAPE
+    bad = list(args)
+    bad[16] = 16                                              # side error word too small
+    assert L.uw_sched_init(*bad) == uw.UW_E_WORKSPACE
+    out = ctypes.c_void_p()
+    assert L.uw_sched_step(buf, p, ctypes.byref(out)) == uw.UW_E_ARG
+    assert L.uw_sched_release(buf) == uw.UW_E_ARG
