@@ -19,6 +19,7 @@
 #include <cstdio>
 #include <cstring>
 #include <new>
+#include <type_traits>
 #include <vector>
 
 #include "uw_internal.h"
@@ -239,6 +240,16 @@ static inline int max_waves(int ct, int unroll) { return ct == 1 ? (unroll >= 8 
 
 __host__ __device__ constexpr int xl_stride(int k) { return 2 * k + 16; }  // padded X row in LDS
 constexpr int kXlMaxBytes = 48 * 1024;
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I = B .. E-1 (each index usable as
+// a constant, e.g. in an s_waitcnt operand).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 // s_waitcnt operand that waits until at most n vector-memory loads are outstanding (lgkm and
 // exp counters left alone): vmcnt bits 3:0 and 15:14.
@@ -652,7 +663,10 @@ struct MtSlot {
 };
 
 // part: S partial [m, n] fp32 planes (S > 1), or null to write y directly.
-template <int SRC, int CT, int U, int R>
+// NB > 0: every K slice holds exactly NB blocks (a multiple of U; the launcher checks), the
+// batch loop is fully unrolled and runs two batches deep over three X buffers and three
+// register sets (see the main loop); NB == 0: the loop below, one batch deep.
+template <int SRC, int CT, int U, int R, int NB>
 __global__ __launch_bounds__(64 * R) void k_gemm_mt(GemmArgs a, float* part, int S) {
   using C = MtCfg<CT, U>;
   static_assert(C::kDmas % R == 0, "every wave issues the same number of X DMAs");
@@ -808,7 +822,9 @@ __global__ __launch_bounds__(64 * R) void k_gemm_mt(GemmArgs a, float* part, int
   // batch i is computed, so they have a whole compute phase to arrive.  Two register sets
   // (sa, sb) and two X buffers alternate; each phase starts with a barrier after which
   // batch i's data is in place and batch i-1's X buffer is free.
-  MtSlot<SRC> sa[U], sb[U];
+  MtSlot<SRC> sl[NB > 0 ? 3 : 2][U];
+  MtSlot<SRC>* const sa = sl[0];
+  MtSlot<SRC>* const sb = sl[1];
   uint8_t* const xb1 = smem + C::kBufBytes;
   // Prologue in issue order: flags (above), X batch 0, the weights of batch 0, then the
   // tile's verbatim base (scalar), the ranks (bit-sliced ballots) and batch 0's verbatim
@@ -831,6 +847,40 @@ __global__ __launch_bounds__(64 * R) void k_gemm_mt(GemmArgs a, float* part, int
     wvp = tot + wave_excl_prefix_small<5>((uint32_t)__popc(wfl), &tot);
 #pragma unroll
     for (int u = 0; u < U; ++u) load_ev(bs + u, sa[u]);
+  }
+  if constexpr (NB > 0) {
+    // Two batches deep.  Per batch a wave issues, in this order, its D X DMAs, 2U weight
+    // loads and (palette sources) U verbatim-exponent loads, LW loads after its DMAs.  Batch
+    // i + 2 goes into the X buffer and register set of batch i - 1, which every wave finished
+    // computing before the barrier of phase i.  Before that barrier a wave waits for its X DMAs
+    // of batch i only: loads retire in order and at that point batch i's weights (and batch
+    // i + 1's DMAs and loads, once issued) follow them, so the count below is exact; the
+    // weights themselves are waited for by the compiler where compute reads them.
+    constexpr int NBT = NB / U;
+    constexpr int D = C::kDmas / R;
+    constexpr int LW = 2 * U + (kPal ? U : 0);
+    if constexpr (NBT > 1) {
+      issue_x(1, xb1);
+      load_batch(1, sl[1]);
+    }
+    static_for<0, NBT>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      // Not __syncthreads(): its release fence would wait for every LDS-DMA in flight,
+      // batch i + 1's included.  The explicit wait (this wave's batch-i DMAs; LDS reads of
+      // batch i - 1 done) and a bare barrier suffice; the empty asm statements keep the
+      // compiler from moving memory accesses across it.
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(LW + (i + 1 < NBT ? D + LW : 0)) & ~0x0F00);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if constexpr (i + 2 < NBT) {
+        issue_x(i + 2, smem + ((i + 2) % 3) * C::kBufBytes);
+        load_batch(i + 2, sl[(i + 2) % 3]);
+      }
+      compute_batch(i, sl[i % 3], smem + (i % 3) * C::kBufBytes);
+    });
+  } else {
+  if constexpr (kPal) {
     // Batch 0 ready except, at most, its verbatim exponents (the last U loads; a flagged block
     // waits for its own when it reads them).
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(U));
@@ -856,6 +906,7 @@ __global__ __launch_bounds__(64 * R) void k_gemm_mt(GemmArgs a, float* part, int
       issue_x(i + 2, smem);
     }
     compute_batch(i + 1, sb, xb1);
+  }
   }
   if constexpr (kTwo) {
 #pragma unroll
@@ -1407,7 +1458,22 @@ template <int SRC, int CT, int U, int R>
 static hipError_t launch_mt_t(const GemmArgs& a, int64_t tiles, int S, float* part, hipStream_t s) {
   using C = MtCfg<CT, U>;
   const dim3 grid((unsigned)((tiles + R - 1) / R), (unsigned)S, (unsigned)((a.m + 16 * CT - 1) / (16 * CT)));
-  hipLaunchKernelGGL((k_gemm_mt<SRC, CT, U, R>), grid, dim3(64 * R), 2 * C::kBufBytes, s, a, S > 1 ? part : nullptr, S);
+  float* const pp = S > 1 ? part : nullptr;
+  // Two batches deep (three X buffers) for the affine palette when every slice holds the same
+  // block count of the MLP shapes (down_proj: 28 blocks at 8 slices; 8192^2: 32 at 4) and the
+  // buffers stay within 64 KB, so several workgroups still share a CU.
+  const int nbs = a.kb % S == 0 ? a.kb / S : 0;
+  bool deep = false;
+  if constexpr (SRC == SRC_PAL_AFFINE && 3 * C::kBufBytes <= 64 * 1024) {
+    if (nbs % U == 0 && (nbs == 28 || nbs == 32)) {
+      deep = true;
+      if (nbs == 28)
+        hipLaunchKernelGGL((k_gemm_mt<SRC, CT, U, R, 28>), grid, dim3(64 * R), 3 * C::kBufBytes, s, a, pp, S);
+      else
+        hipLaunchKernelGGL((k_gemm_mt<SRC, CT, U, R, 32>), grid, dim3(64 * R), 3 * C::kBufBytes, s, a, pp, S);
+    }
+  }
+  if (!deep) hipLaunchKernelGGL((k_gemm_mt<SRC, CT, U, R, 0>), grid, dim3(64 * R), 2 * C::kBufBytes, s, a, pp, S);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
   const int64_t count = (int64_t)a.m * a.n;
@@ -2073,8 +2139,8 @@ struct uw_sched {
 namespace uw {
 static void sched_free_events(SchedImpl* S) {
   for (int i = 0; i < 2; ++i) {
-    if (S->dec_done[i]) hipEventDestroy(S->dec_done[i]);
-    if (S->use_done[i]) hipEventDestroy(S->use_done[i]);
+    if (S->dec_done[i]) (void)hipEventDestroy(S->dec_done[i]);
+    if (S->use_done[i]) (void)hipEventDestroy(S->use_done[i]);
     S->dec_done[i] = S->use_done[i] = nullptr;
   }
 }

@@ -474,3 +474,20 @@ def test_hard_easy_stack_equals_plain(m, hard):
         xa, xb = a, b
     assert sched.resident_bytes() < plain.resident_bytes() + 6 * sched.slot_bytes + 1
     sched.close()
+
+
+@pytest.mark.parametrize("k", [28672, 32768], ids=["28_blocks_a_slice", "32_blocks_a_slice"])
+def test_gemm_multitile_two_batches_deep(k):
+    """The multi-tile kernel's two-batch-deep pipeline (three X buffers, taken when every K
+    slice holds 28 or 32 blocks): 16 K slices of a long row, ragged row count, verbatim
+    segments, 1, 2 and 4 MFMA column tiles, every multi-tile variant, against the oracle."""
+    t = torch()
+    w = synth.small_gaussian(300, k, seed=23, plant_frac=0.05)["w"]
+    cm = uw.CompressedMatrix(w)
+    for m in (8, 17, 40, 64):
+        x = synth.gaussian_bf16(np.random.default_rng(900 + m), (m, k), 1.0)
+        ws = cm.workspace(m, uw.UW_PIPE_DIRECT_PALETTE)
+        for variant in (10, 11, 12, 13):
+            y = t.full((m, 300), float("nan"), dtype=t.float32, device="cuda")
+            uw.uw_gemm_variant(cm.d, dev_u16(x), y, m, uw.UW_PIPE_DIRECT_PALETTE, variant, ws)
+            check_gemm(y, x, w)
