@@ -50,6 +50,12 @@ __device__ __forceinline__ uint16_t swiglu1(float gv, float uv) { return f32_to_
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
+// (a & m) | (b & ~m) in one instruction (the compiler splits it into two for a literal mask).
+__device__ __forceinline__ uint32_t bfi(uint32_t m, uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "s"(m), "v"(a), "v"(b));
+  return r;
+}
 
 // Sign+mantissa dwords (4 weights each) -> 4 spread pair words.
 __device__ __forceinline__ void spread_sm(uint32_t s_lo, uint32_t s_hi, uint32_t p[4]) {
@@ -977,12 +983,15 @@ __global__ __launch_bounds__(256) void k_reduce_parts(const float* part, float* 
 // of the blocks' chunk counts places each chunk in the offset table.
 //   1. The unit's slice of the bitstream (contiguous: its chunks are consecutive) is staged
 //      in LDS with coalesced 16-byte loads, so the serial decode never waits on HBM.
-//   2. A 2^10-entry table (LDS) decodes up to four symbols per lookup: entry = symbol count,
-//      first length, total length, four 4-bit symbols.  A window whose first code is longer
-//      than 10 bits (rare: symbols below 2^-10 frequency) points to a block of a secondary
-//      table indexed by the next 3 bits.  The loop body is branch-free apart from that case:
-//      the refill word is read every step and used or not, and every step stores a word
-//      (to the image when 8 indices are ready, else to a per-lane dummy slot).
+//   2. A 2^10-entry table (LDS) decodes up to four symbols per lookup: entry = four 4-bit
+//      symbols (bits 0-15), total length (16-19), first length (20-23), symbol count (29-31).
+//      A window whose first code is longer than 10 bits (rare: symbols below 2^-10
+//      frequency) has count 0 and points to a block of a secondary table indexed by the next
+//      3 bits.  The bit window is two stream words and a funnel-shift amount; the loop body
+//      is branch-free apart from the long-code case: the refill word is read every step and
+//      used or not, and every step stores a word (to its place when 8 indices are ready,
+//      else out of range or to a per-lane dummy slot).  While four or more symbols remain,
+//      a lookup takes all the symbols of its entry; the last one to three take one a step.
 //   3. Index and exponent modes store each finished 8-index word (or its 8 exponents)
 //      straight to global memory with a bounds-checked buffer store (out of range when a lane
 //      has nothing to store, so the loop stays branch-free); without an output image the
@@ -1019,38 +1028,39 @@ struct DecArgs {
   uint32_t sec[kDecSec];   // secondary entries (same format as the primary ones)
 };
 
-// Image of a unit's index output: one block is 128 words (4 sub-tiles x 16 rows x 2 words),
-// stored kImgBlk words apart so that lanes writing the same (sub-tile, row) of different
+// Image of a unit's index words in decode order: a block's coded rows take 8 words each (128
+// at most); blocks sit kImgBlk words apart so that lanes at the same point of different
 // blocks hit different LDS banks.
 constexpr int kImgBlk = 132;
 
-struct DecLds {            // offsets (bytes) into the dynamic LDS block
-  uint32_t lut, image, stage, blk, total;
+struct DecLds {            // offsets (bytes) into the dynamic LDS block (the table is static)
+  uint32_t image, stage, blk, total;
 };
+constexpr uint32_t kDecTableBytes = (kDecLut + kDecSec) * 4u;
 
 // stage_words: a multiple of 256 (the bitstream slice is staged in 1 KB DMA steps).  direct:
 // the index mode writes straight to global memory and needs no image (the region then only
 // holds the table-build scratch).
 __host__ __device__ inline DecLds dec_lds(int nb, uint32_t stage_words, bool direct) {
   DecLds L;
-  L.lut = 0;
-  L.image = (kDecLut + kDecSec) * 4;
+  L.image = 0;
   const uint32_t img = direct ? kDecLut * 2u : std::max<uint32_t>((uint32_t)nb * kImgBlk * 4u, kDecLut * 2u);
   L.stage = L.image + ((img + 15u) & ~15u);
   L.blk = L.stage + stage_words * 4;
+  // The direct modes reload the unit's index words (512 bytes a block, in 1 KB steps) over
+  // the table scratch and the stage once decoding is done.
+  if (direct) L.blk = std::max<uint32_t>(L.blk, ((uint32_t)nb * 512u + 1023u) & ~1023u);
   L.total = L.blk + 3u * 64u * 4u;   // block flags, verbatim ranks, per-lane dummy slots
   return L;
 }
 
 __device__ __forceinline__ uint32_t nibbles_to_index_word(uint32_t v) {
   // Sequential nibbles n0..n7 (n_i at bits 4i) -> index-stream word (even columns in the low
-  // half, odd columns in the high half: n_i at bit 4*(i/2) + 16*(i%2)).
-  uint32_t x = v & 0x0F0F0F0Fu, y = (v >> 4) & 0x0F0F0F0Fu;
-  x = (x | (x >> 4)) & 0x00FF00FFu;
-  y = (y | (y >> 4)) & 0x00FF00FFu;
-  x = (x | (x >> 8)) & 0x0000FFFFu;
-  y = (y | (y >> 8)) & 0x0000FFFFu;
-  return x | (y << 16);
+  // half, odd columns in the high half: n_i at bit 4*(i/2) + 16*(i%2)).  Bytes 0 and 2 of px
+  // hold (n0 n2) and (n4 n6), those of py (n1 n3) and (n5 n7).
+  const uint32_t v4 = v >> 4;
+  const uint32_t px = bfi(0x0F0F0F0Fu, v, v4), py = bfi(0x0F0F0F0Fu, v4, v >> 8);
+  return perm(py, px, 0x06040200u);
 }
 
 __device__ __forceinline__ u32x2 index_word_to_exps(uint32_t iw, const uint32_t tab[4]) {
@@ -1095,10 +1105,10 @@ __device__ void build_dec_lut(const DecArgs& a, uint32_t* lut, uint16_t* tmp, in
         used += ok ? lj : 0u;
         n += ok ? 1u : 0u;
       }
-      entry = n | (l0 << 3) | (used << 7) | (syms << 16);
+      entry = (n << 29) | (l0 << 20) | (used << 16) | syms;
     } else {
       const uint32_t i = (uint32_t)w - a.pbase;                // long code: secondary block i + 1
-      entry = (i < 15u && ((a.pmask >> i) & 1u)) ? (i + 1u) << 16 : 0u;
+      entry = (i < 15u && ((a.pmask >> i) & 1u)) ? i + 1u : 0u;
     }
     lut[w] = entry;
   }
@@ -1110,8 +1120,8 @@ template <int MODE>
 __global__ __launch_bounds__(64) void k_decode(DecArgs a) {
   extern __shared__ __align__(16) uint8_t dsh[];
   constexpr bool kDirect = MODE != DEC_BF16;
+  __shared__ uint32_t lut[kDecLut + kDecSec];
   const DecLds Ls = dec_lds(a.nb, a.stage_words, kDirect);
-  uint32_t* lut = reinterpret_cast<uint32_t*>(dsh + Ls.lut);
   uint32_t* img = reinterpret_cast<uint32_t*>(dsh + Ls.image);
   uint32_t* stage = reinterpret_cast<uint32_t*>(dsh + Ls.stage);
   uint32_t* blk_f = reinterpret_cast<uint32_t*>(dsh + Ls.blk);       // flags per block of the unit
@@ -1165,9 +1175,6 @@ __global__ __launch_bounds__(64) void k_decode(DecArgs a) {
       lds_dma16(rs, reinterpret_cast<uint8_t*>(stage + i), (wb + i) * 4u + (uint32_t)lane * 16u);
   }
   build_dec_lut(a, lut, reinterpret_cast<uint16_t*>(img), lane);
-  // Zero the image: verbatim and padding rows stay zero in the index layout.
-  if constexpr (!kDirect)
-    for (int i = lane * 4; i < nbu * kImgBlk; i += 256) *reinterpret_cast<u32x4*>(img + i) = u32x4{0, 0, 0, 0};
   __syncthreads();
   // Index and exponent modes: results go straight to the unit's output range (a lane without
   // a finished word stores out of range, which writes nothing).
@@ -1180,117 +1187,151 @@ __global__ __launch_bounds__(64) void k_decode(DecArgs a) {
   const uint32_t bpre = __shfl(ch_pre, bl < 64 ? bl : 0, 64);
   uint32_t cm = realmask & ~bf;                                 // coded rows of the block
   const int ncoded = __popc(cm);
-  bool bad = false;
+  uint32_t bad = 0;
   if (bl < nbu && j * a.spc < ncoded) {
-    for (int s = 0; s < j * a.spc; ++s) cm &= cm - 1u;          // skip earlier chunks' rows
-    int r = __ffs(cm) - 1;
-    uint32_t rem = (uint32_t)min(a.spc, ncoded - j * a.spc) * 64u;
+    const int nrows = min(a.spc, ncoded - j * a.spc);
+    int32_t rem4 = nrows * 256;                                 // 4 x symbols left
     const uint32_t c = c_first + bpre + (uint32_t)j;
     const uint32_t p0 = a.off[c] - wb * 32u, p1 = a.off[c + 1] - wb * 32u;
-    uint32_t wi = p0 >> 5;
     auto word = [&](uint32_t i) -> uint32_t { return i < nst ? stage[i] : 0u; };
-    uint64_t buf = (((uint64_t)word(wi) << 32) | word(wi + 1)) << (p0 & 31u);
-    int avail = 64 - (int)(p0 & 31u);
-    wi += 2;
+    // Bit window: the 32 bits starting (32 - s) bits into w0 (s = 0: w1 itself).
+    const uint32_t b0 = p0 & 31u, wi0 = p0 >> 5;
+    uint32_t w0 = b0 ? word(wi0) : 0u, w1 = word(b0 ? wi0 + 1 : wi0);
+    const uint32_t* nxp = stage + (b0 ? wi0 + 2 : wi0 + 1);     // next stream word
+    const uint32_t* const lastp = stage + (nst ? nst - 1 : 0);
+    uint32_t s = b0 ? 32u - b0 : 0u;
+    // Output, in decode order: the q-th coded row of block bl holds its 8 index words at
+    // bl * stride + q * 32 (the chunk's rows are consecutive coded rows), so a lane fills
+    // its own run of bytes; the final layout is written from these runs afterwards.
+    constexpr uint32_t kBlkStride = MODE == DEC_BF16 ? kImgBlk * 4u : 512u;
+    uint32_t woff = (uint32_t)bl * kBlkStride + (uint32_t)(j * a.spc) * 32u;
     uint64_t acc = 0;
-    uint32_t accn = 0, sw = 0;
-    const uint32_t blk_img = (uint32_t)(bl * kImgBlk);
-    uint32_t* dummy = blk_f + 128 + lane;
-    const uint32_t wlast = nst ? nst - 1 : 0;
-    while (rem) {
-      const uint32_t hi = (uint32_t)(buf >> 32);
-      uint32_t e = lut[hi >> (32 - kDecWin)];
-      const uint32_t v = stage[min(wi, wlast)];                 // refill candidate
-      if ((e & 7u) == 0u) e = lut[kDecLut + ((e >> 16) << 3) + ((hi >> (32 - 13)) & 7u)];
-      const uint32_t nf = e & 7u;
-      const bool all = nf != 0 && nf <= rem;
-      bad |= nf == 0;
-      const uint32_t n = all ? nf : 1u;
-      const uint32_t L = all ? (e >> 7) & 15u : (e >> 3) & 15u;
-      const uint32_t syms = all ? e >> 16 : (e >> 16) & 15u;
-      acc |= (uint64_t)syms << (4 * accn);
-      accn += n;
-      rem -= n;
-      buf <<= L;
-      avail -= (int)L;
-      const bool need = avail < 32;
-      buf |= need ? (uint64_t)v << (32 - avail) : 0ull;
-      avail += need ? 32 : 0;
-      wi += need ? 1u : 0u;
-      // 8 indices ready: store the index word (sub-tile sw / 2, half sw % 2 of row r).
-      const bool flush = accn >= 8;
-      if constexpr (MODE == DEC_IDX) {
-        const uint32_t off = (uint32_t)bl * 512u + (sw >> 1) * 128u + (uint32_t)r * 8u + (sw & 1u) * 4u;
-        __builtin_amdgcn_raw_buffer_store_b32(nibbles_to_index_word((uint32_t)acc), ors, flush ? off : kOob, 0, 0);
-      } else if constexpr (MODE == DEC_EXP) {
-        // 8 exponents: half (sw % 2) of sub-tile (sw / 2) row r, 16 bytes a sub-tile row.
-        const u32x2 ex = index_word_to_exps(nibbles_to_index_word((uint32_t)acc), a.tab);
-        const uint32_t off = (uint32_t)bl * 1024u + (sw >> 1) * 256u + (uint32_t)r * 16u + (sw & 1u) * 8u;
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) int, ex), ors,
-                                              flush ? off : kOob, 0, 0);
+    uint32_t a4 = 0;                                            // 4 x indices pending in acc
+    uint8_t* const ldsb = reinterpret_cast<uint8_t*>(img);
+    uint32_t* const dummy = blk_f + 128 + lane;
+    // One lookup's worth: append `syms` (n4 / 4 indices), consume L bits, emit a finished word.
+    auto step = [&](uint32_t syms, uint32_t n4, uint32_t L, uint32_t v) {
+      acc |= (uint64_t)syms << a4;
+      a4 += n4;
+      rem4 -= (int32_t)n4;
+      const int32_t sl = (int32_t)s - (int32_t)L;
+      const bool neg = sl < 0;
+      w0 = neg ? w1 : w0;
+      w1 = neg ? v : w1;
+      nxp += (uint32_t)sl >> 31;
+      s = (uint32_t)sl & 31u;
+      // a4 < 64, so bit 5 is the flush flag; it drives the store offset (out of range when
+      // clear), the accumulator shift and the offset step without a branch.
+      const uint32_t f32 = a4 & 32u;
+      const uint32_t iw = nibbles_to_index_word((uint32_t)acc);
+      if constexpr (kDirect) {
+        __builtin_amdgcn_raw_buffer_store_b32(iw, ors, woff | ((f32 ^ 32u) << 26), 0, 0);
       } else {
-        const uint32_t word_i = blk_img + (uint32_t)r * 2u + (sw >> 1) * 32u + (sw & 1u);
-        *(flush ? img + word_i : dummy) = nibbles_to_index_word((uint32_t)acc);
+        *(f32 ? reinterpret_cast<uint32_t*>(ldsb + woff) : dummy) = iw;
       }
-      acc = flush ? acc >> 32 : acc;
-      accn -= flush ? 8u : 0u;
-      sw += flush ? 1u : 0u;
-      const bool adv = sw == 8u;
-      cm = adv ? cm & (cm - 1u) : cm;
-      sw = adv ? 0u : sw;
-      r = cm ? __ffs(cm) - 1 : 0;
+      acc >>= f32;
+      a4 &= 31u;
+      woff += f32 >> 3;
+    };
+    // Long or invalid first code: the secondary entry, or a one-bit placeholder when invalid.
+    // (Block 0 of the secondary table is all invalid: it serves invalid primary entries.)
+    auto resolve = [&](uint32_t e, uint32_t win) -> uint32_t {
+      if (e < (1u << 29)) {
+        const uint32_t e2 = lut[kDecLut + (e & 15u) * 8u + ((win >> 19) & 7u)];
+        const bool inv = e2 < (1u << 29);
+        bad |= inv ? 1u : 0u;
+        e = inv ? (1u << 29) | (1u << 20) | (1u << 16) : e2;
+      }
+      return e;
+    };
+    while (rem4 >= 16) {
+      const uint32_t win = __builtin_amdgcn_alignbit(w0, w1, s);
+      uint32_t e = lut[win >> (32 - kDecWin)];
+      const uint32_t v = *(nxp < lastp ? nxp : lastp);           // refill candidate
+      e = resolve(e, win);
+      step(e & 0xFFFFu, e >> 27, (e >> 16) & 15u, v);
     }
-    const uint32_t pos = wi * 32u - (uint32_t)avail;          // bits consumed from the slice start
-    if (pos != p1) bad = true;
+    while (rem4 > 0) {
+      const uint32_t win = __builtin_amdgcn_alignbit(w0, w1, s);
+      uint32_t e = lut[win >> (32 - kDecWin)];
+      const uint32_t v = *(nxp < lastp ? nxp : lastp);
+      e = resolve(e, win);
+      step(e & 15u, 4u, (e >> 20) & 15u, v);
+    }
+    const uint32_t pos = (uint32_t)(nxp - stage) * 32u - 32u - s;   // bits consumed from the slice start
+    if (pos != p1) bad = 1;
   }
   if (bad) atomicOr(a.err, 1u);
-  __syncthreads();
 
-  // Write the rest of the unit's output.
-  if constexpr (MODE == DEC_IDX) {
-    // Verbatim and padding rows hold index 0.
-    for (int p = lane; p < nbu * 16; p += 64) {
-      const int b = p >> 4, rr = p & 15;
-      if (rr < rows && !((blk_f[b] >> rr) & 1u)) continue;
-#pragma unroll
-      for (int g2 = 0; g2 < 4; ++g2)
-        *reinterpret_cast<u32x2*>(a.out + ((size_t)t * a.kb + bA + b) * 512 + g2 * 128 + rr * 8) = u32x2{0, 0};
-    }
-  } else if constexpr (MODE == DEC_EXP) {
-    // Verbatim rows take their raw exponents, padding rows zeros; 16-byte piece p: block
-    // p / 64, sub-tile (p / 16) % 4, row p % 16.
-    u32x4* dst = reinterpret_cast<u32x4*>(a.out + ((size_t)t * a.kb + bA) * 1024);
-    for (int p = lane; p < nbu * 64; p += 64) {
-      const int b = p >> 6, g = (p >> 4) & 3, r = p & 15;
-      const uint32_t fb = blk_f[b];
-      if ((fb >> r) & 1u) {
-        const uint32_t v = blk_v[b] + __popc(fb & ((1u << r) - 1u));
-        dst[(b * 4 + g) * 16 + r] = *reinterpret_cast<const u32x4*>(a.vexp + (size_t)v * 64 + g * 16);
-      } else if (r >= rows) {
-        dst[(b * 4 + g) * 16 + r] = u32x4{0, 0, 0, 0};
+  // Write the unit's output in its final layout.  Row r of block b is coded unless flagged
+  // verbatim; a coded row's words sit at its rank among the block's coded rows.
+  if constexpr (kDirect) {
+    // The index words went out in decode order (this workgroup's stores are complete at the
+    // barrier); bring them back through the (now free) table scratch and stage in 1 KB steps,
+    // bypassing the vector cache, and write every line of the unit's output once.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();
+    uint8_t* const back = reinterpret_cast<uint8_t*>(img);
+    const __amdgpu_buffer_rsrc_t brs = make_rsrc(a.out + ((size_t)t * a.kb + bA) * kOutBlk, (uint32_t)nbu * 512u);
+    for (uint32_t i = 0; i < (uint32_t)nbu * 512u; i += 1024u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, (lds_ptr_t)(back + i), 16, i + (uint32_t)lane * 16u, 0, 0, 1);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();
+    if constexpr (MODE == DEC_IDX) {
+      // 16-byte piece p: block p / 32, sub-tile (p / 8) % 4, rows 2 (p % 8) and 2 (p % 8) + 1.
+      u32x4* dst = reinterpret_cast<u32x4*>(a.out + ((size_t)t * a.kb + bA) * 512);
+      for (int p = lane; p < nbu * 32; p += 64) {
+        const int b = p >> 5, g = (p >> 3) & 3, r = (p & 7) * 2;
+        const uint32_t coded = realmask & ~blk_f[b];
+        const uint32_t q = __popc(coded & ((1u << r) - 1u));
+        const u32x2* src = reinterpret_cast<const u32x2*>(back + b * 512 + g * 8);
+        const u32x2 z{0, 0};
+        const u32x2 w0 = ((coded >> r) & 1u) ? src[q * 4] : z;
+        const u32x2 w1 = ((coded >> (r + 1)) & 1u) ? src[(q + ((coded >> r) & 1u)) * 4] : z;
+        dst[p] = u32x4{w0.x, w0.y, w1.x, w1.y};
+      }
+    } else {
+      // 16-byte piece p: block p / 64, sub-tile (p / 16) % 4, row p % 16.  Verbatim rows
+      // take their raw exponents, padding rows zeros.
+      u32x4* dst = reinterpret_cast<u32x4*>(a.out + ((size_t)t * a.kb + bA) * 1024);
+      for (int p = lane; p < nbu * 64; p += 64) {
+        const int b = p >> 6, g = (p >> 4) & 3, r = p & 15;
+        const uint32_t fb = blk_f[b];
+        u32x4 o{0, 0, 0, 0};
+        if ((fb >> r) & 1u) {
+          const uint32_t v = blk_v[b] + __popc(fb & ((1u << r) - 1u));
+          o = *reinterpret_cast<const u32x4*>(a.vexp + (size_t)v * 64 + g * 16);
+        } else if (r < rows) {
+          const uint32_t q = (uint32_t)r - __popc(fb & ((1u << r) - 1u));
+          const u32x2 iw = *reinterpret_cast<const u32x2*>(back + b * 512 + q * 32 + g * 8);
+          const u32x2 e0 = index_word_to_exps(iw.x, a.tab), e1 = index_word_to_exps(iw.y, a.tab);
+          o = u32x4{e0.x, e0.y, e1.x, e1.y};
+        }
+        dst[p] = o;
       }
     }
   } else {
+    __syncthreads();
     // BF16 rows: 16-byte piece p = 8 weights; row p / (nbu*8), then block, sub-tile, half.
     const int per_row = nbu * 8;
     for (int p = lane; p < rows * per_row; p += 64) {
       const int r = p / per_row, q = p - r * per_row;
       const int b = q >> 3, g = (q >> 1) & 3, h = q & 1;
       const uint32_t fb = blk_f[b];
+      const uint32_t vb = __popc(fb & ((1u << r) - 1u));
       u32x2 e;
       if ((fb >> r) & 1u) {
-        const uint32_t v = blk_v[b] + __popc(fb & ((1u << r) - 1u));
-        e = *reinterpret_cast<const u32x2*>(a.vexp + (size_t)v * 64 + g * 16 + h * 8);
+        e = *reinterpret_cast<const u32x2*>(a.vexp + (size_t)(blk_v[b] + vb) * 64 + g * 16 + h * 8);
       } else {
-        e = index_word_to_exps(img[b * kImgBlk + (g * 16 + r) * 2 + h], a.tab);
+        e = index_word_to_exps(img[b * kImgBlk + ((uint32_t)r - vb) * 8 + g * 2 + h], a.tab);
       }
       const size_t sub = ((size_t)t * a.kb * 4 + (size_t)(bA + b) * 4 + g) * 16 + r;
-      const u32x2 s = *reinterpret_cast<const u32x2*>(a.sm + sub * 16 + h * 8);
+      const u32x2 sv = *reinterpret_cast<const u32x2*>(a.sm + sub * 16 + h * 8);
       u32x4 o;
-      o.x = bf16_pairs_from(s.x, e.x, 0);
-      o.y = bf16_pairs_from(s.x, e.x, 1);
-      o.z = bf16_pairs_from(s.y, e.y, 0);
-      o.w = bf16_pairs_from(s.y, e.y, 1);
+      o.x = bf16_pairs_from(sv.x, e.x, 0);
+      o.y = bf16_pairs_from(sv.x, e.x, 1);
+      o.z = bf16_pairs_from(sv.y, e.y, 0);
+      o.w = bf16_pairs_from(sv.y, e.y, 1);
       *reinterpret_cast<u32x4*>(a.out + ((size_t)(t * 16 + r) * a.k + (size_t)(bA + b) * 64 + g * 16 + h * 8) * 2) = o;
     }
   }
@@ -1714,8 +1755,7 @@ static uw_status run_decode(const uw_dmat* d, int mode, uint8_t* out, void* ws, 
   std::memcpy(a.code, d->info.code, 32);
   // Codes longer than the lookup window: their 10-bit prefixes (consecutive in a canonical
   // code) each get a block of 8 secondary entries indexed by the next 3 bits.
-  const uint32_t invalid = (1u << 3) | (1u << 7);               // n = 0, length 1
-  for (int i = 0; i < kDecSec; ++i) a.sec[i] = invalid;
+  for (int i = 0; i < kDecSec; ++i) a.sec[i] = 0;               // count 0: invalid
   a.pbase = kDecLut;
   for (int sym = 0; sym < 16; ++sym) {
     const int L = d->info.code_len[sym];
@@ -1728,15 +1768,15 @@ static uw_status run_decode(const uw_dmat* d, int mode, uint8_t* out, void* ws, 
     if (blk >= 15) return fail(UW_E_FORMAT, "long codes span too many prefixes");
     a.pmask |= 1u << blk;
     const uint32_t low = (code << (13 - L)) & 7u, cnt = 1u << (13 - L);
-    for (uint32_t q = 0; q < cnt; ++q) a.sec[(blk + 1) * 8 + low + q] = 1u | ((uint32_t)L << 3) | ((uint32_t)L << 7) | ((uint32_t)sym << 16);
+    for (uint32_t q = 0; q < cnt; ++q) a.sec[(blk + 1) * 8 + low + q] = (1u << 29) | ((uint32_t)L << 20) | ((uint32_t)L << 16) | (uint32_t)sym;
   }
   const DecLds L = dec_lds(a.nb, a.stage_words, mode != DEC_BF16);
   int dev = 0, lds_max = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
     return fail(UW_E_HIP, "cannot query the LDS size");
-  if (L.total > (uint32_t)lds_max)
-    return fail(UW_E_SHAPE, "decoder unit needs %u bytes of LDS (device allows %d)", L.total, lds_max);
+  if (L.total + kDecTableBytes > (uint32_t)lds_max)
+    return fail(UW_E_SHAPE, "decoder unit needs %u bytes of LDS (device allows %d)", L.total + kDecTableBytes, lds_max);
   const dim3 grid((unsigned)((d->info.kb + a.nb - 1) / a.nb), (unsigned)d->info.tiles);
   switch (mode) {
     case DEC_IDX: hipLaunchKernelGGL(k_decode<DEC_IDX>, grid, dim3(64), L.total, s, a); break;

@@ -88,7 +88,7 @@ def bimodal(n, k, seed):
 
 
 @pytest.mark.parametrize("name", list(CASES) + list(DECODE_ONLY))
-@pytest.mark.parametrize("chunk", [64, 512])
+@pytest.mark.parametrize("chunk", [64, 512, 1024])
 def test_decoders_bit_exact(name, chunk):
     t = torch()
     w = {**CASES, **DECODE_ONLY}[name]()
