@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode GEMM eff. weight GB/s & % HBM peak; bits/weight (8B MLP, M=1-64)"
 HBM_PEAK_GBS = 8000.0
+PEAK_MFMA_BF16_TFLOPS = 2500.0   # dense bf16 matrix peak of MI355X (no sparsity)
 ROTATE_BYTES = 512e6
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_direct_palette_gate14336x4096_m1_pmc.txt")
 
@@ -178,8 +179,9 @@ def time_torch_bf16(w, xs, steps, warmup):
 
 def diagnostic(args):
     """Diagnostic lines (not the headline): every pipeline autotuned per batch size on the
-    down_proj shape (4096 x 14336, M = 1..64) or the heavy-tail 8192^2 matrix (M = 128), timed
-    against torch BF16; or one decode step through the 32-layer MLP stack at M = 16."""
+    down_proj shape (4096 x 14336, M = 1..64), the heavy-tail 8192^2 matrix (M = 128) or the
+    gate_proj shape at large batches (14336 x 4096, M = 256..1024), timed against torch BF16; or
+    one decode step through the 32-layer MLP stack at M = 16."""
     import torch
     import lossless_bf16_weight_amd as uw
     from lossless_bf16_weight_amd import autotune, synth
@@ -190,8 +192,13 @@ def diagnostic(args):
         return stack_step(args, steps, warmup)
     if args.workload == "stack-hard":
         return stack_hard_step(args, steps, warmup)
-    c = {"down": synth.config3, "heavy": synth.config5, "small": synth.config1}[args.workload]()
-    ms = {"down": (1, 8, 16, 32, 64), "heavy": (128,), "small": (1,)}[args.workload]
+    if args.workload == "large":
+        # gate_proj shape at prefill-sized batches: X drawn like the other configs' X.
+        c = synth.config2()
+        c["x"] = synth.gaussian_bf16(np.random.default_rng(11), (1024, c["w"].shape[1]), 1.0)
+    else:
+        c = {"down": synth.config3, "heavy": synth.config5, "small": synth.config1}[args.workload]()
+    ms = {"down": (1, 8, 16, 32, 64), "heavy": (128,), "small": (1,), "large": (256, 512, 1024)}[args.workload]
     w, x_all = c["w"], c["x"]
     n, k = w.shape
     tuner = autotune.Tuner(w, rotate_bytes=ROTATE_BYTES)
@@ -220,6 +227,7 @@ def diagnostic(args):
                     "compressed_tb_s": round((resident + 2 * m * k + 4 * m * n) / us / 1e6, 3),
                     "eff_weight_gb_s": round(2.0 * n * k / us / 1e3, 1),
                     "tflop_s": round(2.0 * m * n * k / us / 1e6, 1),
+                    "frac_of_bf16_mfma_peak": round(2.0 * m * n * k / us / 1e6 / PEAK_MFMA_BF16_TFLOPS, 4),
                     "torch_bf16_us": round(torch_us[m], 3),
                     "own_bf16_us": round(bf.us, 3) if bf else None,
                     "speedup_vs_torch_bf16": round(torch_us[m] / us, 3)})
@@ -373,11 +381,11 @@ def main():
                     help="BF16 GEMV variant with --variant (default: the library's choice for the shape)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run three device copies of 512 MiB (HBM counter calibration) and exit")
-    ap.add_argument("--workload", default="gate", choices=("gate", "down", "heavy", "stack", "stack-hard", "small"),
-                    help="gate (default: the headline line); down, heavy, stack, stack-hard, small: diagnostic "
-                         "lines for the down_proj batch sweep, the 8192^2 heavy-tail matrix at M=128, the 32-layer "
-                         "stack, the same stack with hard (bundle-only) layers decoded ahead on a side stream, and "
-                         "the 1024^2 single-matrix case")
+    ap.add_argument("--workload", default="gate", choices=("gate", "down", "heavy", "stack", "stack-hard", "small", "large"),
+                    help="gate (default: the headline line); down, heavy, stack, stack-hard, small, large: "
+                         "diagnostic lines for the down_proj batch sweep, the 8192^2 heavy-tail matrix at M=128, the "
+                         "32-layer stack, the same stack with hard (bundle-only) layers decoded ahead on a side "
+                         "stream, the 1024^2 single-matrix case, and gate_proj at M = 256, 512, 1024")
     args = ap.parse_args()
     if args.copy_calibration:
         import torch

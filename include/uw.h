@@ -82,7 +82,7 @@ enum {
   UW_PIPE_DIRECT_PALETTE = 4, /* resident 4-bit indices (bound at uw_dmat_bind), palette GEMM */
   UW_PIPE_BF16 = 5            /* autotune key of the uncompressed uw_gemm_bf16 (not a uw_gemm pipeline) */
 };
-#define UW_MAX_M 256
+#define UW_MAX_M 1024
 #define UW_MAX_CHUNK 4096
 
 /* Message for the last failing call on this thread ("" if none). */

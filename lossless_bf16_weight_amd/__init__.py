@@ -21,7 +21,7 @@ UW_OK, UW_E_ARG, UW_E_SHAPE, UW_E_FORMAT, UW_E_NOMEM, UW_E_WORKSPACE, UW_E_HIP, 
 UW_PIPE_AUTO, UW_PIPE_FULL_DECODE, UW_PIPE_EXP_ONLY, UW_PIPE_TRANSCODE, UW_PIPE_DIRECT_PALETTE = 0, 1, 2, 3, 4
 UW_PIPE_BF16 = 5
 UW_OP_DECODE_FULL, UW_OP_TRANSCODE, UW_OP_DECODE_EXP = 16, 17, 18
-UW_MAX_M = 256
+UW_MAX_M = 1024
 PIPELINES = {"full": UW_PIPE_FULL_DECODE, "exp": UW_PIPE_EXP_ONLY, "transcode": UW_PIPE_TRANSCODE,
              "direct": UW_PIPE_DIRECT_PALETTE}
 

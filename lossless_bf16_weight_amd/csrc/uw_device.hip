@@ -1486,14 +1486,21 @@ static int default_variant(int64_t tiles, int64_t kb, int ct, int m) {
 
 // Multi-tile kernel: K slices so that about 2048 waves run, each slice at most 64 blocks
 // (one block per lane in the flag registers), at most kb slices.
-static int mt_slices(int64_t tiles, int R, int64_t kb) {
-  const int64_t groups = (tiles + R - 1) / R;
-  int64_t S = (2048 + groups * R - 1) / (groups * R);
-  S = std::max<int64_t>(S, (kb + 63) / 64);
-  S = std::min<int64_t>(std::max<int64_t>(S, 1), std::min<int64_t>(kb, 16));
-  return (int)S;
+// K slices of the multi-tile kernel: enough for about 2048 waves over the row groups and
+// the M chunks of 16 * col_tiles(m) columns (grid.z), and at least one per 64 blocks (the
+// palette kernels keep a slice's flags one block per lane).
+static int64_t slices_for(int64_t waves_per_slice, int64_t kb) {
+  int64_t S = (2048 + waves_per_slice - 1) / waves_per_slice;
+  S = std::min<int64_t>(std::max<int64_t>(S, 1), std::min<int64_t>(kb, kMaxSlices));
+  return std::max<int64_t>(S, (kb + 63) / 64);
 }
-static int64_t mt_max_slices(int64_t kb) { return std::max<int64_t>(kMaxSlices, (kb + 63) / 64); }
+static int64_t m_chunks(int m) { return (m + 16 * col_tiles(m) - 1) / (16 * col_tiles(m)); }
+static int mt_slices(int64_t tiles, int R, int64_t kb, int m) {
+  const int64_t groups = (tiles + R - 1) / R;
+  return (int)slices_for(groups * R * m_chunks(m), kb);
+}
+// Upper bound of mt_slices over the wave counts R (groups * R >= tiles).
+static int64_t mt_max_slices(int64_t kb, int64_t tiles, int m) { return slices_for(tiles * m_chunks(m), kb); }
 
 template <int SRC, int CT, int U, int R>
 static hipError_t launch_mt_t(const GemmArgs& a, int64_t tiles, int S, float* part, hipStream_t s) {
@@ -1641,7 +1648,7 @@ static int plan_gemm(int src, const GemmArgs& a, int64_t tiles, int* variant, co
   if (*variant < 0) *variant = a.m > 16 ? kMtDefault : default_variant(tiles, a.kb, ct, a.m);
   if (kVariants[*variant].kind != 1) return 0;
   const int R = kVariants[*variant].waves;
-  int S = mt_slices(tiles, R, a.kb);
+  int S = mt_slices(tiles, R, a.kb, a.m);
   const size_t plane = (size_t)a.m * a.n * sizeof(float);
   if (S > 1 && (!part || part_bytes < (size_t)S * plane))
     S = part ? (int)std::min<size_t>(part_bytes / plane, (size_t)S) : 1;
@@ -1884,7 +1891,8 @@ uw_status uw_workspace_size(const uw_dmat* d, int32_t m, int32_t op, size_t* byt
     int32_t v;
     if (!autotune_lookup(n, k, m, &pipe, &v)) pipe = UW_PIPE_DIRECT_PALETTE;
   }
-  const uint64_t parts = (uint64_t)mt_max_slices((int64_t)d->info.kb) * (uint64_t)std::max(m, 1) * n * sizeof(float);
+  const uint64_t parts = (uint64_t)mt_max_slices((int64_t)d->info.kb, (int64_t)d->info.tiles, std::max(m, 1)) *
+                         (uint64_t)std::max(m, 1) * n * sizeof(float);
   switch (pipe) {
     case UW_PIPE_FULL_DECODE: *bytes = kErrBytes + align_up(2 * n * k, kAlign) + parts; break;
     case UW_PIPE_EXP_ONLY: *bytes = kErrBytes + align_up(np * k, kAlign) + parts; break;

@@ -256,6 +256,26 @@ def test_config1_end_to_end():
     assert cm.info["n_verb"] > 0 and cm.info["affine"] == 1
 
 
+@pytest.mark.parametrize("name", ["ragged_37x192", "tiles_160x1024", "bimodal_lut_96x512", "all_verbatim_20x128"])
+@pytest.mark.parametrize("m", [256, 300, 1024])
+def test_gemm_large_batch(name, m):
+    """Batches up to the largest M the library takes: every pipeline against the fp64
+    oracle bound, M split into several column chunks (and a ragged last chunk at 300)."""
+    t = torch()
+    w = CASES[name]()
+    n, k = w.shape
+    x = synth.gaussian_bf16(np.random.default_rng(7 + m), (m, k), 1.0)
+    cm = uw.CompressedMatrix(w, chunk=256)
+    xd = dev_u16(x)
+    for pipe in ALL_PIPES:
+        ws = cm.workspace(m, pipe)
+        y = t.full((m, n), float("nan"), dtype=t.float32, device="cuda")
+        uw.uw_gemm(cm.d, xd, y, m, pipe, ws)
+        if ws is not None:
+            uw.uw_check(ws)
+        check_gemm(y, x, w)
+
+
 def test_corrupt_stream_matches_oracle():
     """Flipped stream bits (tables intact, every read in bounds).  Where the oracle's
     chunk-end check detects the corruption the GPU must report UW_E_DATA; where a flip
