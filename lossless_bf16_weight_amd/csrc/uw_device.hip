@@ -26,6 +26,7 @@
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -620,10 +621,12 @@ struct MtCfg {
   static constexpr int kDmas = kRows * kGpr / 64;         // 1 KB LDS-DMA instructions per batch
 };
 
-// Rebuild the lane's 16 weights of one block as two bf16x8 MFMA operands.
+// Rebuild the lane's 16 weights of one block as two bf16x8 MFMA operands.  fany: nonzero
+// (wave-uniform) when some row the wave rebuilds has a verbatim segment in this block; f:
+// the verbatim flags of the lane's own tile (bit r: its row).
 template <int SRC>
-__device__ __forceinline__ void rebuild_block(const GemmArgs& a, const WRegs<SRC>& w, uint32_t f, int r,
-                                              const u32x4& ev, u32x4& A0, u32x4& A1) {
+__device__ __forceinline__ void rebuild_block(const GemmArgs& a, const WRegs<SRC>& w, uint32_t fany, uint32_t f,
+                                              int r, const u32x4& ev, u32x4& A0, u32x4& A1) {
   if constexpr (SRC == SRC_BF16) {
     A0 = w.w0;
     A1 = w.w1;
@@ -640,7 +643,7 @@ __device__ __forceinline__ void rebuild_block(const GemmArgs& a, const WRegs<SRC
       exps_raw(w.e.z, w.e.w, T1);
     }
     if constexpr (SRC <= SRC_PAL_LUT) {
-      if (f) {  // uniform: some row of this tile has a verbatim segment in this block
+      if (fany) {
         uint32_t R0[4], R1[4];
         exps_raw(ev.x, ev.y, R0);
         exps_raw(ev.z, ev.w, R1);
@@ -796,7 +799,7 @@ __global__ __launch_bounds__(64 * R) void k_gemm_mt(GemmArgs a, float* part, int
     uint32_t f = 0;
     if constexpr (kPal) f = __builtin_amdgcn_readlane(wfl, b - bs);
     u32x4 A0, A1;
-    rebuild_block<SRC>(a, sl.w, f, r, sl.ev, A0, A1);
+    rebuild_block<SRC>(a, sl.w, f, f, r, sl.ev, A0, A1);
     const bf16x8 a0 = __builtin_bit_cast(bf16x8, A0), a1 = __builtin_bit_cast(bf16x8, A1);
 #pragma unroll
     for (int c = 0; c < CT; ++c)
@@ -936,6 +939,216 @@ __global__ __launch_bounds__(64 * R) void k_gemm_mt(GemmArgs a, float* part, int
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         if (n0 + j < a.n) yp[j] = acc[c][j];
+    }
+  }
+}
+
+// =========================================================================================
+// Wide-tile reconstructive GEMM for large batches (palette sources).
+//
+// At M in the hundreds the multi-tile kernel above is bound by LDS reads of X: every 16x32
+// B fragment read feeds one 16-row tile.  Here a wave owns a pair of row tiles (32 rows) and
+// uses 32x32x16 MFMAs, so one B fragment (32 X rows x 16 k) feeds 32 weight rows: half the
+// LDS bytes and half the MFMA instructions per flop.  A workgroup of R waves holds R pairs
+// and a chunk of 32*CW X rows (grid.z), staged per batch of U blocks in LDS exactly as in
+// the multi-tile kernel; K slices (grid.y) write partial sums the same way.
+// A fragments: lane l rebuilds row (l % 32) of the pair (tile (l / 16) % 2, row l % 16)
+// for k = 32 h .. 32 h + 31 of each block (h = l / 32): the stored 16-weight groups of
+// lanes r + 32 h and r + 32 h + 16 of its tile, rebuilt as in the other kernels.  MFMA step
+// s (0..3) takes k = 32 h + 8 s .. + 7 from lane half h, so X granule 4 h + s.
+// =========================================================================================
+template <int SRC>
+struct WideSlot {
+  WRegs<SRC> wa, wb;
+  u32x4 eva, evb;
+};
+
+template <int SRC, int CW, int U, int R>
+__global__ __launch_bounds__(64 * R) void k_gemm_wide(GemmArgs a, float* part, int S) {
+  static_assert(SRC <= SRC_PAL_LUT, "palette sources only");
+  using C = MtCfg<2 * CW, U>;
+  static_assert(C::kDmas % R == 0, "every wave issues the same number of X DMAs");
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  constexpr int kRowsPerDma = 64 / C::kGpr;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, tsel = (lane >> 4) & 1, h = lane >> 5;
+  const int tiles = (a.n + 15) >> 4;
+  const int t0 = (blockIdx.x * R + wave) * 2;           // first tile of the wave's pair
+  const int npt = max(0, min(2, tiles - t0));           // tiles of the pair (wave-uniform)
+  const bool mine = tsel < npt;
+  const int s = blockIdx.y;
+  const int bs = (int)((int64_t)s * a.kb / S), be = (int)((int64_t)(s + 1) * a.kb / S);
+  const int nbatch = (be - bs + U - 1) / U;
+  const int mcol0 = blockIdx.z * 32 * CW;   // M chunks vary slowest: the row groups running
+  const int mv = min(32 * CW, a.m - mcol0);   // together share one X chunk in L2
+
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.x + (size_t)mcol0 * a.k, (uint32_t)mv * a.k * 2);
+  auto issue_x = [&](int batch, uint8_t* buf) {
+    const int bb = bs + batch * U;
+#pragma unroll
+    for (int jj = 0; jj < C::kDmas / R; ++jj) {
+      const int j = wave + jj * R;
+      const int m = j * kRowsPerDma + lane / C::kGpr;
+      const int q = (lane % C::kGpr) ^ (m & C::kSwz);
+      const int blk = bb + (q >> 3);
+      const uint32_t voff = (m < mv && blk < be) ? (uint32_t)(m * a.k + blk * 64 + (q & 7) * 8) * 2 : kOob;
+      lds_dma16(xrs, buf + j * 1024, voff);
+    }
+  };
+
+  // Both tiles of the pair behind one descriptor each (sign+mantissa, indices, flags).
+  const size_t pair_sm = npt ? (size_t)t0 * a.k * 16 : 0;
+  const __amdgpu_buffer_rsrc_t srs = make_rsrc(a.sm + pair_sm, (uint32_t)npt * a.k * 16);
+  const __amdgpu_buffer_rsrc_t irs = make_rsrc(a.aux + pair_sm / 2, (uint32_t)npt * a.k * 8);
+  const uint32_t so = mine ? (uint32_t)(tsel * a.k * 16 + (r + 32 * h) * 16) : kOob;
+  const uint32_t io = mine ? (uint32_t)(tsel * a.k * 8 + (r + 32 * h) * 8) : kOob;
+  const __amdgpu_buffer_rsrc_t frs = make_rsrc(a.flags + (npt ? (size_t)t0 * a.kb : 0), (uint32_t)npt * a.kb * 2);
+
+  // Verbatim bookkeeping per tile i of the pair: flags of block bs + j in lane j (wfl[i]) and
+  // each block's first rank among the pair's verbatim segments (wvp[i]).
+  uint32_t wfl[2], wvp[2], fpre[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    wfl[i] = __builtin_amdgcn_raw_buffer_load_b16(frs, (i < npt && lane < be - bs) ? (uint32_t)(i * a.kb + bs + lane) * 2
+                                                                                     : kOob, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int b = j * 64 + lane;
+      fpre[i][j] = __builtin_amdgcn_raw_buffer_load_b16(frs, (i < npt && b < bs) ? (uint32_t)(i * a.kb + b) * 2 : kOob,
+                                                        0, 0);
+    }
+  }
+  auto load_w = [&](int b, WideSlot<SRC>& sl) {
+    const bool ok = b < be;
+    sl.wa.s = bload16_nt(srs, ok ? so : kOob, b * 1024);
+    sl.wb.s = bload16_nt(srs, ok && so != kOob ? so + 256 : kOob, b * 1024);
+    sl.wa.i = bload8_nt(irs, ok ? io : kOob, b * 512);
+    sl.wb.i = bload8_nt(irs, ok && io != kOob ? io + 128 : kOob, b * 512);
+  };
+  __amdgpu_buffer_rsrc_t vrs = make_rsrc(a.vexp, 0);
+  auto load_ev = [&](int b, WideSlot<SRC>& sl) {
+    const bool ok = b < be;
+    const int jb = ok ? b - bs : 0;
+    const uint32_t f0 = __builtin_amdgcn_readlane(wfl[0], jb), f1 = __builtin_amdgcn_readlane(wfl[1], jb);
+    const uint32_t p0 = __builtin_amdgcn_readlane(wvp[0], jb), p1 = __builtin_amdgcn_readlane(wvp[1], jb);
+    const uint32_t f = tsel ? f1 : f0;
+    const uint32_t rank = (tsel ? p1 : p0) + (uint32_t)__popc(f & ((1u << r) - 1u));
+    const bool verb = ok && mine && ((f >> r) & 1u);
+    sl.eva = bload16(vrs, verb ? rank * 64 + 32 * h : kOob);
+    sl.evb = bload16(vrs, verb ? rank * 64 + 32 * h + 16 : kOob);
+  };
+  auto load_batch = [&](int i, WideSlot<SRC>* sl) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      load_w(bs + i * U + u, sl[u]);
+      load_ev(bs + i * U + u, sl[u]);
+    }
+  };
+
+  floatx16 acc[CW];
+#pragma unroll
+  for (int c = 0; c < CW; ++c)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[c][e] = 0.f;
+  const int xr = lane & 31;                 // X row of the B fragment within a 32-row tile
+  // One block: rebuild the lane's 32 weights, then 4 * CW MFMAs (4 k-steps x CW column tiles).
+  auto mma_block = [&](int b, int u, const WideSlot<SRC>& sl, const uint8_t* xbuf) {
+    const uint32_t f0 = __builtin_amdgcn_readlane(wfl[0], b - bs), f1 = __builtin_amdgcn_readlane(wfl[1], b - bs);
+    u32x4 A[4];
+    rebuild_block<SRC>(a, sl.wa, f0 | f1, tsel ? f1 : f0, r, sl.eva, A[0], A[1]);
+    rebuild_block<SRC>(a, sl.wb, f0 | f1, tsel ? f1 : f0, r, sl.evb, A[2], A[3]);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int q = u * 8 + 4 * h + st;
+      const bf16x8 av = __builtin_bit_cast(bf16x8, A[st]);
+#pragma unroll
+      for (int c = 0; c < CW; ++c) {
+        const int m = 32 * c + xr;
+        const u32x4 xv = *reinterpret_cast<const u32x4*>(xbuf + (m * C::kGpr + (q ^ (m & C::kSwz))) * 16);
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8, xv), acc[c], 0, 0, 0);
+      }
+    }
+  };
+  auto compute_batch = [&](int i, const WideSlot<SRC>* sl, const uint8_t* xbuf) {
+    const int b = bs + i * U;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (b + u >= be) break;
+      mma_block(b + u, u, sl[u], xbuf);
+    }
+  };
+
+  WideSlot<SRC> sa[U], sb[U];
+  uint8_t* const xb1 = smem + C::kBufBytes;
+  issue_x(0, smem);
+#pragma unroll
+  for (int u = 0; u < U; ++u) load_w(bs + u, sa[u]);
+  {
+    const int tv = npt ? t0 : 0;
+    const uint32_t v0 = a.vprefix[tv];
+    const uint32_t v1 = npt ? a.vprefix[tv + 1] : v0, v2 = npt ? a.vprefix[tv + npt] : v0;
+    vrs = make_rsrc(a.vexp + (size_t)v0 * 64, (v2 - v0) * 64);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      uint32_t before = (uint32_t)__popc(fpre[i][0]) + __popc(fpre[i][1]) + __popc(fpre[i][2]) + __popc(fpre[i][3]);
+      for (int j = 256; j < bs; j += 64) {  // tile rows of more than 256 + 64 blocks
+        const int b = j + lane;
+        before += __popc((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(
+            frs, (i < npt && b < bs) ? (uint32_t)(i * a.kb + b) * 2 : kOob, 0, 0));
+      }
+      uint32_t tot;
+      wave_excl_prefix_small<9>(before, &tot);
+      wvp[i] = (i ? v1 - v0 : 0u) + tot + wave_excl_prefix_small<5>((uint32_t)__popc(wfl[i]), &tot);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) load_ev(bs + u, sa[u]);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int i = 0; i < nbatch; i += 2) {
+    if (i > 0) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+    if (i + 1 < nbatch) {
+      load_batch(i + 1, sb);
+      issue_x(i + 1, xb1);
+    }
+    compute_batch(i, sa, smem);
+    if (i + 1 >= nbatch) break;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (i + 2 < nbatch) {
+      load_batch(i + 2, sa);
+      issue_x(i + 2, smem);
+    }
+    compute_batch(i + 1, sb, xb1);
+  }
+  if (!npt) return;
+  // D lane layout (32x32): column lane % 32 of column tile c; register e holds pair row
+  // 8 (e / 4) + 4 h + e % 4.
+#pragma unroll
+  for (int c = 0; c < CW; ++c) {
+    const int mm = mcol0 + 32 * c + xr;
+    if (mm >= a.m) continue;
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) {
+      const int n0 = t0 * 16 + 8 * qd + 4 * h;
+      if (n0 >= a.n) continue;
+      const floatx4 v{acc[c][4 * qd], acc[c][4 * qd + 1], acc[c][4 * qd + 2], acc[c][4 * qd + 3]};
+      if (!part) {
+        store_out4(a, mm, n0, v);
+        continue;
+      }
+      float* yp = part + (size_t)s * a.m * a.n + (size_t)mm * a.n + n0;
+      if (n0 + 3 < a.n && (a.n & 3) == 0) {
+        *reinterpret_cast<floatx4*>(yp) = v;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (n0 + j < a.n) yp[j] = v[j];
+      }
     }
   }
 }
@@ -1454,7 +1667,9 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* y, uint16_t* x, in
 // Kernel variants: kind 0 = per-tile kernel (waves split the tile's blocks; `unroll` blocks
 // a batch), kind 1 = multi-tile kernel (`waves` row tiles a workgroup, X batches of `unroll`
 // blocks in LDS, K split over workgroups), kind 2 = per-tile kernel with shared X (`waves`
-// whole tiles a workgroup, all X rows in LDS once; M <= 16, k <= 4096, palette sources).
+// whole tiles a workgroup, all X rows in LDS once; M <= 16, k <= 4096, palette sources),
+// kind 3 = wide-tile kernel (`waves` tile pairs a workgroup, 128 X rows a chunk, batches of
+// `unroll` blocks; palette sources, other sources run the default multi-tile variant).
 struct Variant {
   int kind;
   int waves;
@@ -1462,7 +1677,7 @@ struct Variant {
 };
 static const Variant kVariants[] = {{0, 4, 8}, {0, 2, 8}, {0, 8, 8},  {0, 16, 8}, {0, 1, 8}, {0, 4, 4}, {0, 2, 4},
                                     {0, 8, 4}, {0, 16, 4}, {0, 1, 4}, {1, 8, 4},  {1, 4, 4}, {1, 8, 2}, {1, 4, 2},
-                                    {2, 2, 4}, {2, 4, 4}};
+                                    {2, 2, 4}, {2, 4, 4}, {3, 4, 2}, {3, 8, 2}};
 static constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 static constexpr int kMtDefault = 10;   // {1, 8, 4}
 
@@ -1499,8 +1714,36 @@ static int mt_slices(int64_t tiles, int R, int64_t kb, int m) {
   const int64_t groups = (tiles + R - 1) / R;
   return (int)slices_for(groups * R * m_chunks(m), kb);
 }
-// Upper bound of mt_slices over the wave counts R (groups * R >= tiles).
-static int64_t mt_max_slices(int64_t kb, int64_t tiles, int m) { return slices_for(tiles * m_chunks(m), kb); }
+constexpr int kWideCW = 4;   // 32-row X tiles per wide-tile workgroup (128 X rows a chunk)
+static int64_t wide_chunks(int m) { return (m + 32 * kWideCW - 1) / (32 * kWideCW); }
+static int wide_slices(int64_t tiles, int R, int64_t kb, int m) {
+  const int64_t groups = ((tiles + 1) / 2 + R - 1) / R;
+  return (int)slices_for(groups * R * wide_chunks(m), kb);
+}
+// Upper bound of mt_slices and wide_slices over the wave counts R (groups * R >= tiles or
+// tile pairs).
+static int64_t mt_max_slices(int64_t kb, int64_t tiles, int m) {
+  return std::max(slices_for(tiles * m_chunks(m), kb), slices_for((tiles + 1) / 2 * wide_chunks(m), kb));
+}
+
+// Adds the S > 1 K-slice partial sums into y (or through the SwiGLU epilogue into h, or
+// into y and the RMS-normed rows xn), in slice order.
+static hipError_t launch_reduce(const GemmArgs& a, int S, float* part, hipStream_t s) {
+  const int64_t count = (int64_t)a.m * a.n;
+  if (a.xn) {  // the caller checked rms_fusable(): n % 4 == 0, n <= 16384, aligned y and xn
+    const dim3 g((unsigned)a.m), b(1024);
+    if (a.n <= 4096)
+      hipLaunchKernelGGL((k_reduce_rmsnorm<1>), g, b, 0, s, part, a.y, a.xn, S, a.n, count, a.eps);
+    else if (a.n <= 8192)
+      hipLaunchKernelGGL((k_reduce_rmsnorm<2>), g, b, 0, s, part, a.y, a.xn, S, a.n, count, a.eps);
+    else
+      hipLaunchKernelGGL((k_reduce_rmsnorm<4>), g, b, 0, s, part, a.y, a.xn, S, a.n, count, a.eps);
+    return hipGetLastError();
+  }
+  const int64_t blocks = std::min<int64_t>((count / 4 + 255) / 256 + 1, 4096);
+  hipLaunchKernelGGL(k_reduce_parts, dim3((unsigned)blocks), dim3(256), 0, s, part, a.y, a.gate, a.h, S, count);
+  return hipGetLastError();
+}
 
 template <int SRC, int CT, int U, int R>
 static hipError_t launch_mt_t(const GemmArgs& a, int64_t tiles, int S, float* part, hipStream_t s) {
@@ -1522,22 +1765,9 @@ static hipError_t launch_mt_t(const GemmArgs& a, int64_t tiles, int S, float* pa
     }
   }
   if (!deep) hipLaunchKernelGGL((k_gemm_mt<SRC, CT, U, R, 0>), grid, dim3(64 * R), 2 * C::kBufBytes, s, a, pp, S);
-  hipError_t e = hipGetLastError();
+  const hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
-  const int64_t count = (int64_t)a.m * a.n;
-  if (a.xn) {  // the caller checked rms_fusable(): n % 4 == 0, n <= 16384, aligned y and xn
-    const dim3 g((unsigned)a.m), b(1024);
-    if (a.n <= 4096)
-      hipLaunchKernelGGL((k_reduce_rmsnorm<1>), g, b, 0, s, part, a.y, a.xn, S, a.n, count, a.eps);
-    else if (a.n <= 8192)
-      hipLaunchKernelGGL((k_reduce_rmsnorm<2>), g, b, 0, s, part, a.y, a.xn, S, a.n, count, a.eps);
-    else
-      hipLaunchKernelGGL((k_reduce_rmsnorm<4>), g, b, 0, s, part, a.y, a.xn, S, a.n, count, a.eps);
-    return hipGetLastError();
-  }
-  const int64_t blocks = std::min<int64_t>((count / 4 + 255) / 256 + 1, 4096);
-  hipLaunchKernelGGL(k_reduce_parts, dim3((unsigned)blocks), dim3(256), 0, s, part, a.y, a.gate, a.h, S, count);
-  return hipGetLastError();
+  return launch_reduce(a, S, part, s);
 }
 
 template <int SRC, int CT>
@@ -1564,6 +1794,24 @@ static hipError_t launch_mt(const GemmArgs& a, int64_t tiles, int R, int U, int 
     case 4: return launch_mt_c<SRC, 4>(a, tiles, R, U, S, part, s);
     default: return launch_mt_c<SRC, 8>(a, tiles, R, U, S, part, s);
   }
+}
+
+template <int SRC, int U, int R>
+static hipError_t launch_wide_t(const GemmArgs& a, int64_t tiles, int S, float* part, hipStream_t s) {
+  using C = MtCfg<2 * kWideCW, U>;
+  const int64_t pairs = (tiles + 1) / 2;
+  const dim3 grid((unsigned)((pairs + R - 1) / R), (unsigned)S, (unsigned)wide_chunks(a.m));
+  hipLaunchKernelGGL((k_gemm_wide<SRC, kWideCW, U, R>), grid, dim3(64 * R), 2 * C::kBufBytes, s, a,
+                     S > 1 ? part : nullptr, S);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess || S == 1) return e;
+  return launch_reduce(a, S, part, s);
+}
+
+// Batches of 2 blocks only: 4 would spill at 8 waves a workgroup.
+template <int SRC>
+static hipError_t launch_wide(const GemmArgs& a, int64_t tiles, int R, int S, float* part, hipStream_t s) {
+  return R == 8 ? launch_wide_t<SRC, 2, 8>(a, tiles, S, part, s) : launch_wide_t<SRC, 2, 4>(a, tiles, S, part, s);
 }
 
 struct Launch {
@@ -1645,14 +1893,16 @@ static hipError_t launch_gemm_c(const GemmArgs& a, int ct, const Launch& L, hipS
 // multi-tile variant cannot run: not enough workspace for its slices).
 static int plan_gemm(int src, const GemmArgs& a, int64_t tiles, int* variant, const float* part, size_t part_bytes) {
   const int ct = col_tiles(a.m);
+  const bool pal = src <= SRC_PAL_LUT;
   if (*variant < 0) *variant = a.m > 16 ? kMtDefault : default_variant(tiles, a.kb, ct, a.m);
-  if (kVariants[*variant].kind != 1) return 0;
+  if (kVariants[*variant].kind == 3 && !pal) *variant = kMtDefault;
+  const int kind = kVariants[*variant].kind;
+  if (kind != 1 && kind != 3) return 0;
   const int R = kVariants[*variant].waves;
-  int S = mt_slices(tiles, R, a.kb, a.m);
+  int S = kind == 3 ? wide_slices(tiles, R, a.kb, a.m) : mt_slices(tiles, R, a.kb, a.m);
   const size_t plane = (size_t)a.m * a.n * sizeof(float);
   if (S > 1 && (!part || part_bytes < (size_t)S * plane))
     S = part ? (int)std::min<size_t>(part_bytes / plane, (size_t)S) : 1;
-  const bool pal = src <= SRC_PAL_LUT;
   if (S < 1 || (pal && (a.kb + S - 1) / S > 64)) {
     *variant = default_variant(tiles, a.kb, ct, a.m);
     return 0;
@@ -1678,6 +1928,13 @@ static uw_status run_gemm(int src, const GemmArgs& a, int64_t tiles, int variant
                           size_t part_bytes, hipStream_t s) {
   int ct = col_tiles(a.m);
   const int S = plan_gemm(src, a, tiles, &variant, part, part_bytes);
+  if (S > 0 && kVariants[variant].kind == 3) {
+    const int R = kVariants[variant].waves;
+    const hipError_t e = src == SRC_PAL_AFFINE ? launch_wide<SRC_PAL_AFFINE>(a, tiles, R, S, part, s)
+                                               : launch_wide<SRC_PAL_LUT>(a, tiles, R, S, part, s);
+    if (e != hipSuccess) return fail(UW_E_HIP, "gemm launch: %s", hipGetErrorString(e));
+    return UW_OK;
+  }
   if (S > 0) {
     const int R = kVariants[variant].waves, U = kVariants[variant].unroll;
     hipError_t e;
@@ -1935,6 +2192,9 @@ const char* uw_variant_name(int32_t variant) {
              kVariants[variant].unroll);
   else if (kVariants[variant].kind == 2)
     snprintf(names[variant], sizeof(names[variant]), "shared-x tiles=%d unroll=%d", kVariants[variant].waves,
+             kVariants[variant].unroll);
+  else if (kVariants[variant].kind == 3)
+    snprintf(names[variant], sizeof(names[variant]), "wide pairs=%d unroll=%d", kVariants[variant].waves,
              kVariants[variant].unroll);
   else
     snprintf(names[variant], sizeof(names[variant]), "multitile tiles=%d unroll=%d", kVariants[variant].waves,

@@ -131,8 +131,9 @@ def test_gemm_all_pipelines(name, m):
         check_gemm(y, x, w)
 
 
-N_VARIANTS = 16
+N_VARIANTS = 18
 SHARED_X_VARIANTS = (14, 15)   # kind 2: whole tiles per wave, X rows shared in LDS
+WIDE_VARIANTS = (16, 17)       # kind 3: tile pairs per wave, 32x32 MFMAs (palette sources)
 
 
 def test_variant_count():
@@ -180,6 +181,33 @@ def test_gemm_long_k_every_variant(variant):
         yb = t.full((m, 70), float("nan"), dtype=t.float32, device="cuda")
         uw.uw_gemm_bf16(dev_u16(w), dev_u16(x), yb, m, variant)
         check_gemm(yb, x, w)
+
+
+@pytest.mark.parametrize("variant", WIDE_VARIANTS)
+@pytest.mark.parametrize("case", ["odd_pairs", "lut_palette", "long_k"])
+def test_gemm_wide_tiles(variant, case):
+    """The wide-tile kernel (a wave rebuilds two row tiles, 32x32 MFMAs): an odd tile count
+    (the last pair holds one tile) and ragged rows, the table-lookup palette, and k = 9216
+    (several K slices, flag words past the first 64 blocks), with and without room for the
+    partial sums, across 1, 2 and 3 column chunks of 128 X rows and a ragged last chunk."""
+    t = torch()
+    w = {"odd_pairs": lambda: synth.small_gaussian(200, 2048, seed=19, plant_frac=0.05)["w"],
+         "lut_palette": lambda: bimodal(96, 512, 6),
+         "long_k": lambda: synth.small_gaussian(70, 9216, seed=23, plant_frac=0.1)["w"]}[case]()
+    n, k = w.shape
+    cm = uw.CompressedMatrix(w)
+    assert uw.uw_variant_name(variant).startswith("wide ")
+    for m in (17, 128, 129, 300):
+        x = synth.gaussian_bf16(np.random.default_rng(900 + m), (m, k), 1.0)
+        for pipe in (uw.UW_PIPE_DIRECT_PALETTE, uw.UW_PIPE_TRANSCODE):
+            for ws in (None, cm.workspace(m, pipe)):
+                if pipe == uw.UW_PIPE_TRANSCODE and ws is None:
+                    continue
+                y = t.full((m, n), float("nan"), dtype=t.float32, device="cuda")
+                uw.uw_gemm_variant(cm.d, dev_u16(x), y, m, pipe, variant, ws)
+                if ws is not None:
+                    uw.uw_check(ws)
+                check_gemm(y, x, w)
 
 
 @pytest.mark.parametrize("variant", SHARED_X_VARIANTS)
