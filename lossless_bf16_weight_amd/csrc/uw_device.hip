@@ -1202,16 +1202,17 @@ __global__ __launch_bounds__(256) void k_reduce_parts(const float* part, float* 
 //      frequency) has count 0 and points to a block of a secondary table indexed by the next
 //      3 bits.  The bit window is two stream words and a funnel-shift amount; the loop body
 //      is branch-free apart from the long-code case: the refill word is read every step and
-//      used or not, and every step stores a word (to its place when 8 indices are ready,
-//      else out of range or to a per-lane dummy slot).  While four or more symbols remain,
+//      used or not, and every step issues a store (to its place when 8 indices are ready,
+//      else to an offset out of the buffer's range).  While four or more symbols remain,
 //      a lookup takes all the symbols of its entry; the last one to three take one a step.
-//   3. Index and exponent modes store each finished 8-index word (or its 8 exponents)
-//      straight to global memory with a bounds-checked buffer store (out of range when a lane
-//      has nothing to store, so the loop stays branch-free); without an output image the
-//      workgroup needs ~19 KB of LDS and eight fit on a CU.  The partial-line stores cost
-//      write bandwidth (about 5x / 2.5x the output bytes) that the decode arithmetic hides.
-//      The BF16 mode collects indices in an LDS image of the unit's output and merges them
-//      with the sign+mantissa bytes while writing whole lines.
+//   3. Every mode stores each finished 8-index word straight to global memory, in decode
+//      order (a lane's words are consecutive, so lines fill from one lane and the L2 does not
+//      write partial lines back): the index and exponent modes into the unit's own output
+//      range, the BF16 mode into the first 32 bytes a block of the tile's output rows (row q
+//      holds the words of each block's q-th coded row).  After a barrier the workgroup reloads
+//      its words into LDS (over the table scratch and the stage) and writes every output line
+//      once, whole: indices (verbatim and padding rows 0), exponents (verbatim rows raw), or
+//      BF16 weights merged with the sign+mantissa bytes.
 // =========================================================================================
 enum DecMode { DEC_IDX = 0, DEC_EXP = 1, DEC_BF16 = 2 };
 
@@ -1241,29 +1242,24 @@ struct DecArgs {
   uint32_t sec[kDecSec];   // secondary entries (same format as the primary ones)
 };
 
-// Image of a unit's index words in decode order: a block's coded rows take 8 words each (128
-// at most); blocks sit kImgBlk words apart so that lanes at the same point of different
-// blocks hit different LDS banks.
-constexpr int kImgBlk = 132;
 
 struct DecLds {            // offsets (bytes) into the dynamic LDS block (the table is static)
-  uint32_t image, stage, blk, total;
+  uint32_t image, stage, blk, total;   // image: table-build scratch, then the reloaded words
 };
 constexpr uint32_t kDecTableBytes = (kDecLut + kDecSec) * 4u;
 
 // stage_words: a multiple of 256 (the bitstream slice is staged in 1 KB DMA steps).  direct:
-// the index mode writes straight to global memory and needs no image (the region then only
-// holds the table-build scratch).
+// index or exponent mode (the unit's words come back as one run of 512 bytes a block);
+// otherwise BF16 mode (16 rows of 32 bytes a block, each row padded to 1 KB steps).
+__host__ __device__ inline uint32_t dec_row_stride(int nb) { return ((uint32_t)nb * 32u + 1023u) & ~1023u; }
 __host__ __device__ inline DecLds dec_lds(int nb, uint32_t stage_words, bool direct) {
   DecLds L;
   L.image = 0;
-  const uint32_t img = direct ? kDecLut * 2u : std::max<uint32_t>((uint32_t)nb * kImgBlk * 4u, kDecLut * 2u);
-  L.stage = L.image + ((img + 15u) & ~15u);
+  L.stage = kDecLut * 2u;
   L.blk = L.stage + stage_words * 4;
-  // The direct modes reload the unit's index words (512 bytes a block, in 1 KB steps) over
-  // the table scratch and the stage once decoding is done.
-  if (direct) L.blk = std::max<uint32_t>(L.blk, ((uint32_t)nb * 512u + 1023u) & ~1023u);
-  L.total = L.blk + 3u * 64u * 4u;   // block flags, verbatim ranks, per-lane dummy slots
+  const uint32_t back = direct ? ((uint32_t)nb * 512u + 1023u) & ~1023u : 16u * dec_row_stride(nb);
+  L.blk = std::max<uint32_t>(L.blk, back);
+  L.total = L.blk + 2u * 64u * 4u;   // block flags, verbatim ranks
   return L;
 }
 
@@ -1391,8 +1387,12 @@ __global__ __launch_bounds__(64) void k_decode(DecArgs a) {
   __syncthreads();
   // Index and exponent modes: results go straight to the unit's output range (a lane without
   // a finished word stores out of range, which writes nothing).
-  constexpr uint32_t kOutBlk = MODE == DEC_IDX ? 512u : 1024u;   // output bytes per block
-  const __amdgpu_buffer_rsrc_t ors = make_rsrc(a.out + ((size_t)t * a.kb + bA) * kOutBlk, (uint32_t)nbu * kOutBlk);
+  constexpr uint32_t kOutBlk = MODE == DEC_IDX ? 512u : 1024u;   // output bytes per block (direct modes)
+  const uint32_t rowb = (uint32_t)a.k * 2u;                       // BF16 output row, bytes
+  uint8_t* const obase = kDirect ? a.out + ((size_t)t * a.kb + bA) * kOutBlk
+                                 : a.out + ((size_t)t * 16 * a.k + (size_t)bA * 64) * 2;
+  const __amdgpu_buffer_rsrc_t ors =
+      make_rsrc(obase, kDirect ? (uint32_t)nbu * kOutBlk : (uint32_t)(rows - 1) * rowb + (uint32_t)nbu * 128u);
 
   // Decode: lane -> (block in unit, chunk in block).
   const int bl = lane / a.cpb, j = lane % a.cpb;
@@ -1414,14 +1414,12 @@ __global__ __launch_bounds__(64) void k_decode(DecArgs a) {
     const uint32_t* const lastp = stage + (nst ? nst - 1 : 0);
     uint32_t s = b0 ? 32u - b0 : 0u;
     // Output, in decode order: the q-th coded row of block bl holds its 8 index words at
-    // bl * stride + q * 32 (the chunk's rows are consecutive coded rows), so a lane fills
-    // its own run of bytes; the final layout is written from these runs afterwards.
-    constexpr uint32_t kBlkStride = MODE == DEC_BF16 ? kImgBlk * 4u : 512u;
-    uint32_t woff = (uint32_t)bl * kBlkStride + (uint32_t)(j * a.spc) * 32u;
+    // bl * 512 + q * 32 (the chunk's rows are consecutive coded rows), so a lane fills its
+    // own run of bytes; BF16 mode: at q * rowb + bl * 32 (woff counts q * 32 + word * 4).
+    uint32_t woff = (kDirect ? (uint32_t)bl * 512u : 0u) + (uint32_t)(j * a.spc) * 32u;
+    const uint32_t lb32 = (uint32_t)bl * 32u;
     uint64_t acc = 0;
     uint32_t a4 = 0;                                            // 4 x indices pending in acc
-    uint8_t* const ldsb = reinterpret_cast<uint8_t*>(img);
-    uint32_t* const dummy = blk_f + 128 + lane;
     // One lookup's worth: append `syms` (n4 / 4 indices), consume L bits, emit a finished word.
     auto step = [&](uint32_t syms, uint32_t n4, uint32_t L, uint32_t v) {
       acc |= (uint64_t)syms << a4;
@@ -1437,11 +1435,8 @@ __global__ __launch_bounds__(64) void k_decode(DecArgs a) {
       // clear), the accumulator shift and the offset step without a branch.
       const uint32_t f32 = a4 & 32u;
       const uint32_t iw = nibbles_to_index_word((uint32_t)acc);
-      if constexpr (kDirect) {
-        __builtin_amdgcn_raw_buffer_store_b32(iw, ors, woff | ((f32 ^ 32u) << 26), 0, 0);
-      } else {
-        *(f32 ? reinterpret_cast<uint32_t*>(ldsb + woff) : dummy) = iw;
-      }
+      const uint32_t po = kDirect ? woff : (woff >> 5) * rowb + lb32 + (woff & 31u);
+      __builtin_amdgcn_raw_buffer_store_b32(iw, ors, po | ((f32 ^ 32u) << 26), 0, 0);
       acc >>= f32;
       a4 &= 31u;
       woff += f32 >> 3;
@@ -1477,55 +1472,62 @@ __global__ __launch_bounds__(64) void k_decode(DecArgs a) {
   if (bad) atomicOr(a.err, 1u);
 
   // Write the unit's output in its final layout.  Row r of block b is coded unless flagged
-  // verbatim; a coded row's words sit at its rank among the block's coded rows.
+  // verbatim; a coded row's words sit at its rank among the block's coded rows.  The words
+  // went out in decode order (this workgroup's stores are complete at the barrier); they come
+  // back through the (now free) table scratch and stage in 1 KB LDS-DMA steps, bypassing the
+  // vector cache, and every line of the unit's output is written once.
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  __syncthreads();
+  uint8_t* const back = reinterpret_cast<uint8_t*>(img);
   if constexpr (kDirect) {
-    // The index words went out in decode order (this workgroup's stores are complete at the
-    // barrier); bring them back through the (now free) table scratch and stage in 1 KB steps,
-    // bypassing the vector cache, and write every line of the unit's output once.
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    __syncthreads();
-    uint8_t* const back = reinterpret_cast<uint8_t*>(img);
-    const __amdgpu_buffer_rsrc_t brs = make_rsrc(a.out + ((size_t)t * a.kb + bA) * kOutBlk, (uint32_t)nbu * 512u);
     for (uint32_t i = 0; i < (uint32_t)nbu * 512u; i += 1024u)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, (lds_ptr_t)(back + i), 16, i + (uint32_t)lane * 16u, 0, 0, 1);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    __syncthreads();
-    if constexpr (MODE == DEC_IDX) {
-      // 16-byte piece p: block p / 32, sub-tile (p / 8) % 4, rows 2 (p % 8) and 2 (p % 8) + 1.
-      u32x4* dst = reinterpret_cast<u32x4*>(a.out + ((size_t)t * a.kb + bA) * 512);
-      for (int p = lane; p < nbu * 32; p += 64) {
-        const int b = p >> 5, g = (p >> 3) & 3, r = (p & 7) * 2;
-        const uint32_t coded = realmask & ~blk_f[b];
-        const uint32_t q = __popc(coded & ((1u << r) - 1u));
-        const u32x2* src = reinterpret_cast<const u32x2*>(back + b * 512 + g * 8);
-        const u32x2 z{0, 0};
-        const u32x2 w0 = ((coded >> r) & 1u) ? src[q * 4] : z;
-        const u32x2 w1 = ((coded >> (r + 1)) & 1u) ? src[(q + ((coded >> r) & 1u)) * 4] : z;
-        dst[p] = u32x4{w0.x, w0.y, w1.x, w1.y};
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ors, (lds_ptr_t)(back + i), 16, i + (uint32_t)lane * 16u, 0, 0, 1);
+  } else {
+    const uint32_t rs = dec_row_stride(a.nb), run = (uint32_t)nbu * 32u;
+    for (int q = 0; q < rows; ++q)
+      for (uint32_t c = 0; c < run; c += 1024u) {
+        const uint32_t o = c + (uint32_t)lane * 16u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ors, (lds_ptr_t)(back + q * rs + c), 16,
+                                                 o < run ? (uint32_t)q * rowb + o : kOob, 0, 0, 1);
       }
-    } else {
-      // 16-byte piece p: block p / 64, sub-tile (p / 16) % 4, row p % 16.  Verbatim rows
-      // take their raw exponents, padding rows zeros.
-      u32x4* dst = reinterpret_cast<u32x4*>(a.out + ((size_t)t * a.kb + bA) * 1024);
-      for (int p = lane; p < nbu * 64; p += 64) {
-        const int b = p >> 6, g = (p >> 4) & 3, r = p & 15;
-        const uint32_t fb = blk_f[b];
-        u32x4 o{0, 0, 0, 0};
-        if ((fb >> r) & 1u) {
-          const uint32_t v = blk_v[b] + __popc(fb & ((1u << r) - 1u));
-          o = *reinterpret_cast<const u32x4*>(a.vexp + (size_t)v * 64 + g * 16);
-        } else if (r < rows) {
-          const uint32_t q = (uint32_t)r - __popc(fb & ((1u << r) - 1u));
-          const u32x2 iw = *reinterpret_cast<const u32x2*>(back + b * 512 + q * 32 + g * 8);
-          const u32x2 e0 = index_word_to_exps(iw.x, a.tab), e1 = index_word_to_exps(iw.y, a.tab);
-          o = u32x4{e0.x, e0.y, e1.x, e1.y};
-        }
-        dst[p] = o;
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  __syncthreads();
+  if constexpr (MODE == DEC_IDX) {
+    // 16-byte piece p: block p / 32, sub-tile (p / 8) % 4, rows 2 (p % 8) and 2 (p % 8) + 1.
+    u32x4* dst = reinterpret_cast<u32x4*>(obase);
+    for (int p = lane; p < nbu * 32; p += 64) {
+      const int b = p >> 5, g = (p >> 3) & 3, r = (p & 7) * 2;
+      const uint32_t coded = realmask & ~blk_f[b];
+      const uint32_t q = __popc(coded & ((1u << r) - 1u));
+      const u32x2* src = reinterpret_cast<const u32x2*>(back + b * 512 + g * 8);
+      const u32x2 z{0, 0};
+      const u32x2 w0 = ((coded >> r) & 1u) ? src[q * 4] : z;
+      const u32x2 w1 = ((coded >> (r + 1)) & 1u) ? src[(q + ((coded >> r) & 1u)) * 4] : z;
+      dst[p] = u32x4{w0.x, w0.y, w1.x, w1.y};
+    }
+  } else if constexpr (MODE == DEC_EXP) {
+    // 16-byte piece p: block p / 64, sub-tile (p / 16) % 4, row p % 16.  Verbatim rows take
+    // their raw exponents, padding rows zeros.
+    u32x4* dst = reinterpret_cast<u32x4*>(obase);
+    for (int p = lane; p < nbu * 64; p += 64) {
+      const int b = p >> 6, g = (p >> 4) & 3, r = p & 15;
+      const uint32_t fb = blk_f[b];
+      u32x4 o{0, 0, 0, 0};
+      if ((fb >> r) & 1u) {
+        const uint32_t v = blk_v[b] + __popc(fb & ((1u << r) - 1u));
+        o = *reinterpret_cast<const u32x4*>(a.vexp + (size_t)v * 64 + g * 16);
+      } else if (r < rows) {
+        const uint32_t q = (uint32_t)r - __popc(fb & ((1u << r) - 1u));
+        const u32x2 iw = *reinterpret_cast<const u32x2*>(back + b * 512 + q * 32 + g * 8);
+        const u32x2 e0 = index_word_to_exps(iw.x, a.tab), e1 = index_word_to_exps(iw.y, a.tab);
+        o = u32x4{e0.x, e0.y, e1.x, e1.y};
       }
+      dst[p] = o;
     }
   } else {
-    __syncthreads();
     // BF16 rows: 16-byte piece p = 8 weights; row p / (nbu*8), then block, sub-tile, half.
+    const uint32_t rs = dec_row_stride(a.nb);
     const int per_row = nbu * 8;
     for (int p = lane; p < rows * per_row; p += 64) {
       const int r = p / per_row, q = p - r * per_row;
@@ -1536,7 +1538,8 @@ __global__ __launch_bounds__(64) void k_decode(DecArgs a) {
       if ((fb >> r) & 1u) {
         e = *reinterpret_cast<const u32x2*>(a.vexp + (size_t)(blk_v[b] + vb) * 64 + g * 16 + h * 8);
       } else {
-        e = index_word_to_exps(img[b * kImgBlk + ((uint32_t)r - vb) * 8 + g * 2 + h], a.tab);
+        e = index_word_to_exps(*reinterpret_cast<const uint32_t*>(back + ((uint32_t)r - vb) * rs + b * 32 + (g * 2 + h) * 4),
+                               a.tab);
       }
       const size_t sub = ((size_t)t * a.kb * 4 + (size_t)(bA + b) * 4 + g) * 16 + r;
       const u32x2 sv = *reinterpret_cast<const u32x2*>(a.sm + sub * 16 + h * 8);
@@ -1545,7 +1548,7 @@ __global__ __launch_bounds__(64) void k_decode(DecArgs a) {
       o.y = bf16_pairs_from(sv.x, e.x, 1);
       o.z = bf16_pairs_from(sv.y, e.y, 0);
       o.w = bf16_pairs_from(sv.y, e.y, 1);
-      *reinterpret_cast<u32x4*>(a.out + ((size_t)(t * 16 + r) * a.k + (size_t)(bA + b) * 64 + g * 16 + h * 8) * 2) = o;
+      *reinterpret_cast<u32x4*>(obase + ((size_t)r * a.k + (size_t)b * 64 + g * 16 + h * 8) * 2) = o;
     }
   }
 }
