@@ -151,7 +151,8 @@ uw_status uw_dmat_get_info(const uw_dmat* d, uw_info* out);
 
 /* Workspace bytes a call needs.  op: a UW_PIPE_* value for uw_gemm, or one of the decode
  * targets below.  Layout: [256 bytes: error word][decoded matrix, decode pipelines only]
- * [fp32 K-slice partial sums of the multi-tile kernel: up to 16 slices of m x n].
+ * [fp32 K-slice partial sums of the multi-tile and wide-tile kernels: up to 16 slices of m x n,
+ *  fewer at large m].
  * The first 256 bytes must be zero before the first use (uw_check clears the word again); the
  * rest needs no initialisation.  One workspace may serve any sequence of calls (any matrix, m,
  * pipeline) issued in order on one stream; calls that may overlap need workspaces of their own.
@@ -162,7 +163,10 @@ enum { UW_OP_DECODE_FULL = 16, UW_OP_TRANSCODE = 17, UW_OP_DECODE_EXP = 18 };
 uw_status uw_workspace_size(const uw_dmat* d, int32_t m, int32_t op, size_t* bytes);
 
 /* Full Huffman decode (pipeline 1's preprocessing): w_out (device, n*k uint16, row-major) is
- * bit-identical to the encoded W.  ws: workspace of uw_workspace_size(.., UW_OP_DECODE_FULL). */
+ * bit-identical to the encoded W.  ws: workspace of uw_workspace_size(.., UW_OP_DECODE_FULL).
+ * The three decode entry points write intermediate data into their output buffer before its
+ * final contents (decoded index words, in decode order), so the output must not alias an input
+ * and must not be read until the call has completed on its stream. */
 uw_status uw_decode_full(const uw_dmat* d, uint16_t* w_out, void* ws, size_t ws_bytes,
                          hipStream_t s);
 
@@ -195,7 +199,11 @@ uw_status uw_gemm_variant(const uw_dmat* d, const uint16_t* x, float* y, int32_t
 uw_status uw_gemm_bf16(const uint16_t* w, int64_t n, int64_t k, const uint16_t* x, float* y,
                        int32_t m, int32_t variant, hipStream_t s);
 
-/* Kernel variants: count, and a description string ("waves=4 unroll=2") of one. */
+/* Kernel variants: count, and a description string of one: "waves=W unroll=U" (per-tile
+ * kernel), "multitile tiles=W unroll=U", "shared-x tiles=W unroll=U" (M <= 16) or
+ * "wide pairs=W unroll=U" (large batches, palette sources; others run the default
+ * multi-tile variant).  Every variant computes any shape and batch size the entry points
+ * accept; a variant whose conditions a call does not meet runs a default instead. */
 int32_t uw_variant_count(void);
 const char* uw_variant_name(int32_t variant);
 
@@ -279,7 +287,7 @@ uw_status uw_gemm_rmsnorm(const uw_dmat* d, const uint16_t* x, float* y, uint16_
  * The scheduler holds host state and four HIP events (no device memory): the caller allocates
  * uw_sched_size() bytes for it and ends its use with uw_sched_release.  Errors: UW_E_ARG (null
  * pointer, bad shape or stream), UW_E_SHAPE (a matrix not of its layer shape, m outside
- * [1, 256]), UW_E_WORKSPACE (slot_bytes or a buffer too small), UW_E_NOMEM, UW_E_HIP; on an
+ * [1, UW_MAX_M]), UW_E_WORKSPACE (slot_bytes or a buffer too small), UW_E_NOMEM, UW_E_HIP; on an
  * error nothing was launched. */
 typedef struct uw_sched uw_sched;
 size_t uw_sched_size(void);
