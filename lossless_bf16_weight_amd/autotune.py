@@ -56,6 +56,12 @@ class Table:
         if key not in self.best_variant or e.us < self.best_variant[key].us:
             self.best_variant[key] = e
 
+    def merge(self, other: "Table"):
+        """Add every measurement of another table (e.g. another weight shape of the same model)."""
+        for e in other.all_times:
+            self.add(e)
+        return self
+
     def best_pipeline(self, n, k, m):
         """Fastest compressed pipeline at (n, k, m) (the uncompressed key is not a choice of uw_gemm)."""
         c = [e for (a, b, mm, p), e in self.best_variant.items() if (a, b, mm) == (n, k, m) and p != UW_PIPE_BF16]
@@ -187,9 +193,11 @@ class Tuner:
 
 
 def main(argv=None):
-    ap = argparse.ArgumentParser(description="Autotune pipelines and kernel variants for one weight shape "
-                                             "(synthetic N(0, std^2) BF16 weights of that shape).")
-    ap.add_argument("--shape", required=True, help="NxK, e.g. 4096x14336")
+    ap = argparse.ArgumentParser(description="Autotune pipelines and kernel variants for one or more weight shapes "
+                                             "(synthetic N(0, std^2) BF16 weights of each shape) into one table "
+                                             "file, e.g. every projection shape of a model.")
+    ap.add_argument("--shape", required=True,
+                    help="NxK, or several comma-separated, e.g. 14336x4096,4096x14336 (a Llama-3.1-8B MLP layer)")
     ap.add_argument("--m", default="1,8,32,64", help="comma-separated batch sizes")
     ap.add_argument("--std", type=float, default=0.02)
     ap.add_argument("--seed", type=int, default=0)
@@ -198,12 +206,15 @@ def main(argv=None):
     ap.add_argument("--rounds", type=int, default=5)
     a = ap.parse_args(argv)
     from . import synth
-    n, k = (int(v) for v in a.shape.lower().split("x"))
     rng = np.random.default_rng(a.seed)
-    w = synth.gaussian_bf16(rng, (n, k), a.std)
-    t = Tuner(w)
-    table = t.tune([int(v) for v in a.m.split(",")], launches=a.launches, rounds=a.rounds,
-                   log=lambda s: print(s, file=sys.stderr, flush=True))
+    table = Table()
+    for shape in a.shape.split(","):
+        n, k = (int(v) for v in shape.lower().split("x"))
+        w = synth.gaussian_bf16(rng, (n, k), a.std)
+        t = Tuner(w)
+        table.merge(t.tune([int(v) for v in a.m.split(",")], launches=a.launches, rounds=a.rounds,
+                           log=lambda s: print(s, file=sys.stderr, flush=True)))
+        del t   # its rotated device copies
     table.save(a.out)
     sys.stdout.write(table.text())
 

@@ -168,6 +168,33 @@ def test_autotune_table_roundtrip(tmp_path):
     uw.uw_autotune_clear()
 
 
+def test_autotune_model_table_merge(tmp_path):
+    """A model's projection shapes tuned separately merge into one table file that the C ABI
+    loads: per (n, k, m) the fastest compressed pipeline becomes the AUTO entry, every
+    pipeline keeps its own best variant, and a slower later measurement changes nothing."""
+    from lossless_bf16_weight_amd import autotune as at
+    gate, down = at.Table(), at.Table()
+    gate.add(at.Entry(14336, 4096, 16, uw.UW_PIPE_DIRECT_PALETTE, 14, 17.9))
+    gate.add(at.Entry(14336, 4096, 16, uw.UW_PIPE_DIRECT_PALETTE, 10, 23.1))
+    gate.add(at.Entry(14336, 4096, 16, uw.UW_PIPE_TRANSCODE, 10, 80.0))
+    gate.add(at.Entry(14336, 4096, 16, uw.UW_PIPE_BF16, 3, 25.0))
+    down.add(at.Entry(4096, 14336, 16, uw.UW_PIPE_EXP_ONLY, 11, 40.0))
+    down.add(at.Entry(4096, 14336, 16, uw.UW_PIPE_DIRECT_PALETTE, 12, 18.8))
+    model = at.Table().merge(gate).merge(down)
+    model.add(at.Entry(4096, 14336, 16, uw.UW_PIPE_DIRECT_PALETTE, 13, 19.5))   # slower: ignored
+    assert model.shapes() == [(4096, 14336, 16), (14336, 4096, 16)]
+    p = tmp_path / "model.txt"
+    model.save(str(p))
+    uw.uw_autotune_clear()
+    uw.uw_autotune_load(str(p))
+    assert uw.uw_autotune_get(14336, 4096, 16) == (uw.UW_PIPE_DIRECT_PALETTE, 14)
+    assert uw.uw_autotune_get(4096, 14336, 16) == (uw.UW_PIPE_DIRECT_PALETTE, 12)
+    assert uw.uw_autotune_get_variant(14336, 4096, 16, uw.UW_PIPE_TRANSCODE) == 10
+    assert uw.uw_autotune_get_variant(14336, 4096, 16, uw.UW_PIPE_BF16) == 3
+    assert uw.uw_autotune_get_variant(4096, 14336, 16, uw.UW_PIPE_EXP_ONLY) == 11
+    uw.uw_autotune_clear()
+
+
 def test_autotune_variant_entries(tmp_path):
     uw.uw_autotune_clear()
     assert uw.uw_autotune_get_variant(14336, 4096, 1, uw.UW_PIPE_BF16) == -1
