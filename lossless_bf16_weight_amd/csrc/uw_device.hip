@@ -1248,17 +1248,15 @@ struct DecLds {            // offsets (bytes) into the dynamic LDS block (the ta
 };
 constexpr uint32_t kDecTableBytes = (kDecLut + kDecSec) * 4u;
 
-// stage_words: a multiple of 256 (the bitstream slice is staged in 1 KB DMA steps).  direct:
-// index or exponent mode (the unit's words come back as one run of 512 bytes a block);
-// otherwise BF16 mode (16 rows of 32 bytes a block, each row padded to 1 KB steps).
-__host__ __device__ inline uint32_t dec_row_stride(int nb) { return ((uint32_t)nb * 32u + 1023u) & ~1023u; }
-__host__ __device__ inline DecLds dec_lds(int nb, uint32_t stage_words, bool direct) {
+// stage_words: a multiple of 256 (the bitstream slice is staged in 1 KB DMA steps).  The unit's
+// index words come back as 512 bytes a block (index and exponent modes: one run; BF16 mode: at
+// most 16 rows of 32 bytes a block, back to back), reloaded in 1 KB steps.
+__host__ __device__ inline DecLds dec_lds(int nb, uint32_t stage_words) {
   DecLds L;
   L.image = 0;
   L.stage = kDecLut * 2u;
   L.blk = L.stage + stage_words * 4;
-  const uint32_t back = direct ? ((uint32_t)nb * 512u + 1023u) & ~1023u : 16u * dec_row_stride(nb);
-  L.blk = std::max<uint32_t>(L.blk, back);
+  L.blk = std::max<uint32_t>(L.blk, ((uint32_t)nb * 512u + 1023u) & ~1023u);
   L.total = L.blk + 2u * 64u * 4u;   // block flags, verbatim ranks
   return L;
 }
@@ -1330,7 +1328,7 @@ __global__ __launch_bounds__(64) void k_decode(DecArgs a) {
   extern __shared__ __align__(16) uint8_t dsh[];
   constexpr bool kDirect = MODE != DEC_BF16;
   __shared__ uint32_t lut[kDecLut + kDecSec];
-  const DecLds Ls = dec_lds(a.nb, a.stage_words, kDirect);
+  const DecLds Ls = dec_lds(a.nb, a.stage_words);
   uint32_t* img = reinterpret_cast<uint32_t*>(dsh + Ls.image);
   uint32_t* stage = reinterpret_cast<uint32_t*>(dsh + Ls.stage);
   uint32_t* blk_f = reinterpret_cast<uint32_t*>(dsh + Ls.blk);       // flags per block of the unit
@@ -1483,13 +1481,13 @@ __global__ __launch_bounds__(64) void k_decode(DecArgs a) {
     for (uint32_t i = 0; i < (uint32_t)nbu * 512u; i += 1024u)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ors, (lds_ptr_t)(back + i), 16, i + (uint32_t)lane * 16u, 0, 0, 1);
   } else {
-    const uint32_t rs = dec_row_stride(a.nb), run = (uint32_t)nbu * 32u;
-    for (int q = 0; q < rows; ++q)
-      for (uint32_t c = 0; c < run; c += 1024u) {
-        const uint32_t o = c + (uint32_t)lane * 16u;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ors, (lds_ptr_t)(back + q * rs + c), 16,
-                                                 o < run ? (uint32_t)q * rowb + o : kOob, 0, 0, 1);
-      }
+    // Row q's run of nbu * 32 bytes lands at back + q * run: a 1 KB step covers several rows.
+    const uint32_t run = (uint32_t)nbu * 32u, total = (uint32_t)rows * run;
+    for (uint32_t i = 0; i < total; i += 1024u) {
+      const uint32_t o = i + (uint32_t)lane * 16u, q = o / run;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ors, (lds_ptr_t)(back + i), 16, o < total ? q * rowb + (o - q * run) : kOob,
+                                               0, 0, 1);
+    }
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __syncthreads();
@@ -1527,7 +1525,7 @@ __global__ __launch_bounds__(64) void k_decode(DecArgs a) {
     }
   } else {
     // BF16 rows: 16-byte piece p = 8 weights; row p / (nbu*8), then block, sub-tile, half.
-    const uint32_t rs = dec_row_stride(a.nb);
+    const uint32_t rs = (uint32_t)nbu * 32u;
     const int per_row = nbu * 8;
     for (int p = lane; p < rows * per_row; p += 64) {
       const int r = p / per_row, q = p - r * per_row;
@@ -2037,7 +2035,7 @@ static uw_status run_decode(const uw_dmat* d, int mode, uint8_t* out, void* ws, 
     const uint32_t low = (code << (13 - L)) & 7u, cnt = 1u << (13 - L);
     for (uint32_t q = 0; q < cnt; ++q) a.sec[(blk + 1) * 8 + low + q] = (1u << 29) | ((uint32_t)L << 20) | ((uint32_t)L << 16) | (uint32_t)sym;
   }
-  const DecLds L = dec_lds(a.nb, a.stage_words, mode != DEC_BF16);
+  const DecLds L = dec_lds(a.nb, a.stage_words);
   int dev = 0, lds_max = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
