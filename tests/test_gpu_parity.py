@@ -304,6 +304,54 @@ def test_gemm_large_batch(name, m):
         check_gemm(y, x, w)
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_random_shapes_every_entry_point(seed):
+    """Seeded random sweep: row counts 1..300 (ragged tiles), k = 64..1536, chunk 64..1024,
+    Gaussian / Student-t / two-scale values with 0-20 % planted outlier rows.  The blob equals
+    the oracle's byte for byte; the three decoders equal the oracle's decodes; every pipeline
+    (and the wide-tile variant for M > 16) is within the oracle's GEMM bound."""
+    t = torch()
+    rng = np.random.default_rng(1000 + seed)
+    n, k = int(rng.integers(1, 301)), 64 * int(rng.integers(1, 25))
+    chunk = 64 * int(rng.integers(1, 17))
+    kind = seed % 3
+    if kind == 0:
+        w = synth.gaussian_bf16(rng, (n, k), float(rng.uniform(0.005, 0.05)))
+    elif kind == 1:
+        w = synth.student_t_bf16(rng, (n, k), 3, 0.02)
+    else:
+        w = bimodal(n, k, 3000 + seed)
+    synth.plant_outliers(rng, w, float(rng.choice([0.0, 0.01, 0.2])))
+    blob = uw.uw_encode(w, chunk)
+    ref_blob = codec.serialize(codec.encode(w, n, k, chunk=chunk))
+    assert blob.tobytes() == ref_blob, "n=%d k=%d chunk=%d" % (n, k, chunk)
+    cm = uw.CompressedMatrix(w, chunk=chunk, blob=blob)
+    ws = err_ws()
+    out = t.empty((n, k), dtype=t.int16, device="cuda")
+    uw.uw_decode_full(cm.d, out, ws)
+    uw.uw_check(ws)
+    assert np.array_equal(host_u16(out), w)
+    assert cm.idx.cpu().numpy().tobytes() == codec.transcode_blob(ref_blob).tobytes()
+    ex = t.empty(int(cm.info["np"]) * k, dtype=t.uint8, device="cuda")
+    uw.uw_decode_exponents(cm.d, ex, ws)
+    uw.uw_check(ws)
+    assert ex.cpu().numpy().tobytes() == codec.exponent_stream_blob(ref_blob).tobytes()
+    for m in (1, int(rng.integers(2, 17)), int(rng.integers(17, 200))):
+        x = synth.gaussian_bf16(rng, (m, k), 1.0)
+        for pipe in ALL_PIPES:
+            wsp = cm.workspace(m, pipe)
+            y = t.full((m, n), float("nan"), dtype=t.float32, device="cuda")
+            uw.uw_gemm(cm.d, dev_u16(x), y, m, pipe, wsp)
+            if wsp is not None:
+                uw.uw_check(wsp)
+            check_gemm(y, x, w)
+        if m > 16:
+            y = t.full((m, n), float("nan"), dtype=t.float32, device="cuda")
+            uw.uw_gemm_variant(cm.d, dev_u16(x), y, m, uw.UW_PIPE_DIRECT_PALETTE, WIDE_VARIANTS[-1],
+                               cm.workspace(m, uw.UW_PIPE_DIRECT_PALETTE))
+            check_gemm(y, x, w)
+
+
 def test_corrupt_stream_matches_oracle():
     """Flipped stream bits (tables intact, every read in bounds).  Where the oracle's
     chunk-end check detects the corruption the GPU must report UW_E_DATA; where a flip
