@@ -1525,28 +1525,40 @@ __global__ __launch_bounds__(64) void k_decode(DecArgs a) {
     }
   } else {
     // BF16 rows: 16-byte piece p = 8 weights; row p / (nbu*8), then block, sub-tile, half.
+    // Four pieces a lane at a time: their loads all go out before the first store.
     const uint32_t rs = (uint32_t)nbu * 32u;
-    const int per_row = nbu * 8;
-    for (int p = lane; p < rows * per_row; p += 64) {
-      const int r = p / per_row, q = p - r * per_row;
-      const int b = q >> 3, g = (q >> 1) & 3, h = q & 1;
-      const uint32_t fb = blk_f[b];
-      const uint32_t vb = __popc(fb & ((1u << r) - 1u));
-      u32x2 e;
-      if ((fb >> r) & 1u) {
-        e = *reinterpret_cast<const u32x2*>(a.vexp + (size_t)(blk_v[b] + vb) * 64 + g * 16 + h * 8);
-      } else {
-        e = index_word_to_exps(*reinterpret_cast<const uint32_t*>(back + ((uint32_t)r - vb) * rs + b * 32 + (g * 2 + h) * 4),
-                               a.tab);
+    const int per_row = nbu * 8, total = rows * per_row;
+    constexpr int kPieces = 4;
+    for (int p0 = lane; p0 < total; p0 += 64 * kPieces) {
+      u32x2 sv[kPieces], e[kPieces];
+      size_t dsto[kPieces];
+#pragma unroll
+      for (int u = 0; u < kPieces; ++u) {
+        const int p = min(p0 + 64 * u, total - 1);
+        const int r = p / per_row, q = p - r * per_row;
+        const int b = q >> 3, g = (q >> 1) & 3, h = q & 1;
+        const uint32_t fb = blk_f[b];
+        const uint32_t vb = __popc(fb & ((1u << r) - 1u));
+        if ((fb >> r) & 1u) {
+          e[u] = *reinterpret_cast<const u32x2*>(a.vexp + (size_t)(blk_v[b] + vb) * 64 + g * 16 + h * 8);
+        } else {
+          e[u] = index_word_to_exps(*reinterpret_cast<const uint32_t*>(back + ((uint32_t)r - vb) * rs + b * 32 + (g * 2 + h) * 4),
+                                    a.tab);
+        }
+        const size_t sub = ((size_t)t * a.kb * 4 + (size_t)(bA + b) * 4 + g) * 16 + r;
+        sv[u] = *reinterpret_cast<const u32x2*>(a.sm + sub * 16 + h * 8);
+        dsto[u] = ((size_t)r * a.k + (size_t)b * 64 + g * 16 + h * 8) * 2;
       }
-      const size_t sub = ((size_t)t * a.kb * 4 + (size_t)(bA + b) * 4 + g) * 16 + r;
-      const u32x2 sv = *reinterpret_cast<const u32x2*>(a.sm + sub * 16 + h * 8);
-      u32x4 o;
-      o.x = bf16_pairs_from(sv.x, e.x, 0);
-      o.y = bf16_pairs_from(sv.x, e.x, 1);
-      o.z = bf16_pairs_from(sv.y, e.y, 0);
-      o.w = bf16_pairs_from(sv.y, e.y, 1);
-      *reinterpret_cast<u32x4*>(obase + ((size_t)r * a.k + (size_t)b * 64 + g * 16 + h * 8) * 2) = o;
+#pragma unroll
+      for (int u = 0; u < kPieces; ++u) {
+        if (p0 + 64 * u >= total) break;
+        u32x4 o;
+        o.x = bf16_pairs_from(sv[u].x, e[u].x, 0);
+        o.y = bf16_pairs_from(sv[u].x, e[u].x, 1);
+        o.z = bf16_pairs_from(sv[u].y, e[u].y, 0);
+        o.w = bf16_pairs_from(sv[u].y, e[u].y, 1);
+        *reinterpret_cast<u32x4*>(obase + dsto[u]) = o;
+      }
     }
   }
 }
