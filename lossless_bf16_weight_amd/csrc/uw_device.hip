@@ -780,6 +780,13 @@ __global__ __launch_bounds__(64 * R) void k_gemm_mt(GemmArgs a, float* part, int
 #pragma unroll
   for (int c = 0; c < (kTwo ? CT : 1); ++c) acc2[c] = floatx4{0.f, 0.f, 0.f, 0.f};
   const int sw = r & C::kSwz;
+  // LDS byte offsets of this lane's X fragments in a batch (block u, MFMA step k2), column
+  // tile 0: tile c adds the constant 16 * c * kGpr * 16 (the swizzle depends on r only).
+  uint32_t xoff[U][2];
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) xoff[u][k2] = (uint32_t)(r * C::kGpr + ((u * 8 + g * 2 + k2) ^ sw)) * 16u;
 
   auto load_batch = [&](int i, MtSlot<SRC>* sl) {
 #pragma unroll
@@ -787,11 +794,10 @@ __global__ __launch_bounds__(64 * R) void k_gemm_mt(GemmArgs a, float* part, int
   };
   // X fragments of block u of the batch: column tile c, MFMA step k2 (x[c][0..1]).
   auto load_x = [&](const uint8_t* xbuf, int u, u32x4 (&x)[CT][2]) {
-    const int q0 = u * 8 + g * 2;
 #pragma unroll
     for (int c = 0; c < CT; ++c) {
-      x[c][0] = *reinterpret_cast<const u32x4*>(xbuf + ((16 * c + r) * C::kGpr + (q0 ^ sw)) * 16);
-      x[c][1] = *reinterpret_cast<const u32x4*>(xbuf + ((16 * c + r) * C::kGpr + ((q0 + 1) ^ sw)) * 16);
+      x[c][0] = *reinterpret_cast<const u32x4*>(xbuf + xoff[u][0] + c * 16 * C::kGpr * 16);
+      x[c][1] = *reinterpret_cast<const u32x4*>(xbuf + xoff[u][1] + c * 16 * C::kGpr * 16);
     }
   };
   // One block: rebuild this lane's weights, then 2*CT MFMAs against the block's X fragments.
@@ -1052,6 +1058,14 @@ __global__ __launch_bounds__(64 * R) void k_gemm_wide(GemmArgs a, float* part, i
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[c][e] = 0.f;
   const int xr = lane & 31;                 // X row of the B fragment within a 32-row tile
+  // LDS byte offsets of this lane's B fragments in a batch (block u, step st), column tile 0:
+  // tile c adds the constant 32 * c * kGpr * 16 (the swizzle depends on xr only).
+  uint32_t xoff[U][4];
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+      xoff[u][st] = (uint32_t)(xr * C::kGpr + ((u * 8 + 4 * h + st) ^ (xr & C::kSwz))) * 16u;
   // One block: rebuild the lane's 32 weights, then 4 * CW MFMAs (4 k-steps x CW column tiles).
   auto mma_block = [&](int b, int u, const WideSlot<SRC>& sl, const uint8_t* xbuf) {
     const uint32_t f0 = __builtin_amdgcn_readlane(wfl[0], b - bs), f1 = __builtin_amdgcn_readlane(wfl[1], b - bs);
@@ -1060,23 +1074,20 @@ __global__ __launch_bounds__(64 * R) void k_gemm_wide(GemmArgs a, float* part, i
     rebuild_block<SRC>(a, sl.wb, f0 | f1, tsel ? f1 : f0, r, sl.evb, A[2], A[3]);
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      const int q = u * 8 + 4 * h + st;
       const bf16x8 av = __builtin_bit_cast(bf16x8, A[st]);
 #pragma unroll
       for (int c = 0; c < CW; ++c) {
-        const int m = 32 * c + xr;
-        const u32x4 xv = *reinterpret_cast<const u32x4*>(xbuf + (m * C::kGpr + (q ^ (m & C::kSwz))) * 16);
+        const u32x4 xv = *reinterpret_cast<const u32x4*>(xbuf + xoff[u][st] + c * 32 * C::kGpr * 16);
         acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8, xv), acc[c], 0, 0, 0);
       }
     }
   };
   auto compute_batch = [&](int i, const WideSlot<SRC>* sl, const uint8_t* xbuf) {
     const int b = bs + i * U;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (b + u >= be) break;
-      mma_block(b + u, u, sl[u], xbuf);
-    }
+    static_for<0, U>([&](auto uc) {   // u a compile-time constant: xoff stays in registers
+      constexpr int u = decltype(uc)::value;
+      if (b + u < be) mma_block(b + u, u, sl[u], xbuf);
+    });
   };
 
   WideSlot<SRC> sa[U], sb[U];
