@@ -41,6 +41,9 @@ Readings taken where the post is silent or garbled (each is repeated where it is
   R8  Layout: weights are grouped in tiles of 16 rows; inside a tile the sign+mantissa,
       exponent and index streams are stored as 16x16 sub-tiles (row-major inside the
       sub-tile) ordered by K; segments are enumerated in (tile, 64-column block, row) order.
+  R15 The encoder may take its palette from the caller instead of the matrix's own
+      histogram (ascending exponents, at most 16); the post describes only the per-matrix
+      top-16, so this changes that single step and nothing after it.
 """
 from __future__ import annotations
 
@@ -88,6 +91,20 @@ def merge_fields(e, sm):
 def exponent_histogram(e):
     """Count of each of the 256 exponent values over the whole matrix."""
     return np.bincount(np.asarray(e, np.uint8).ravel(), minlength=256).astype(np.int64)
+
+
+def palette_from_exponents(exps):
+    """A palette given by its caller (the boundary's encode option): the listed exponents,
+    which must be 1..16 distinct values 0..255 in ascending order; index = list position."""
+    exps = [int(v) for v in exps]
+    if not 1 <= len(exps) <= PALETTE_SIZE or any(not 0 <= v <= 255 for v in exps):
+        raise ValueError("a palette holds 1..16 exponents in 0..255")
+    if any(b <= a for a, b in zip(exps, exps[1:])):
+        raise ValueError("palette exponents must be strictly ascending")
+    index_of = np.full(256, NONE, dtype=np.uint8)
+    for i, x in enumerate(exps):
+        index_of[x] = i
+    return np.array(exps, dtype=np.uint8), index_of
 
 
 def build_palette(hist):
@@ -280,13 +297,18 @@ def pack_bitstream_plain(symbols, lengths, codes):
 # ----------------------------------------------------------------------------------------
 # Encoder
 # ----------------------------------------------------------------------------------------
-def analyse(w, n, k):
-    """Everything the encoder derives from W, as named arrays (no serialisation)."""
+def analyse(w, n, k, palette=None):
+    """Everything the encoder derives from W, as named arrays (no serialisation).
+
+    palette: None builds W's own top-16 (exponent-distribution paragraph); a list of
+    ascending exponents replaces that one step (reading R15: a caller-supplied palette, e.g.
+    shared by several matrices).  Every later step is unchanged: segments holding an exponent
+    outside the palette are verbatim, and the code is built over the other segments' indices."""
     check_shape(n, k)
     w = np.asarray(w, dtype=np.uint16).reshape(n, k)
     e, sm = split_fields(w)
     hist = exponent_histogram(e)
-    palette, index_of = build_palette(hist)
+    palette, index_of = build_palette(hist) if palette is None else palette_from_exponents(palette)
     verb = verbatim_segments(e, index_of)
     n_pad = padded_rows(n)
     kb = k // SEG
@@ -326,11 +348,12 @@ def chunk_starts(coded_per_block, chunk):
     return np.array(starts, dtype=np.int64), np.array(cbase, dtype=np.uint32)
 
 
-def encode(w, n, k, chunk=DEFAULT_CHUNK, lmax=LMAX):
-    """W (uint16 BF16 bits, [n, k]) -> dict with every section of the format."""
+def encode(w, n, k, chunk=DEFAULT_CHUNK, lmax=LMAX, palette=None):
+    """W (uint16 BF16 bits, [n, k]) -> dict with every section of the format.
+    palette: None (W's own top-16) or the caller's ascending exponents (see analyse)."""
     if chunk % SEG or chunk <= 0:
         raise ValueError("chunk must be a positive multiple of 64")
-    a = analyse(w, n, k)
+    a = analyse(w, n, k, palette)
     lengths = package_merge_lengths(list(a["freqs"]) + [0] * (PALETTE_SIZE - len(a["freqs"])), lmax)
     codes = canonical_codes(lengths)
     words, sym_start, total = pack_bitstream(a["symbols"], lengths, codes)

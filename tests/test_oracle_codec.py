@@ -488,3 +488,93 @@ def test_parse_rejects_corruption():
     bad[128 + 16 * 6: 128 + 16 * 6 + 8] = (10 ** 9).to_bytes(8, "little")
     with pytest.raises(ValueError):
         codec.parse(bytes(bad))
+
+
+# ------------------------------------------------------------------ sizes (closed forms)
+def test_resident_palette_bytes_closed_form():
+    """Resident direct-palette bytes = sign+mantissa (1 B a padded weight) + 4-bit indices
+    (0.5 B) + one u16 flag word per (tile, block) + a u32 verbatim prefix per tile and one
+    extra + 64 raw exponent bytes per verbatim segment, with the verbatim segments counted
+    here by loops from W and a palette taken by brute force (Counter, top 16)."""
+    w = synth.small_gaussian(37, 192, seed=1, plant_frac=0.05)["w"].copy()
+    w[5, 70], w[36, 191], w[36, 0] = 0x4F80, 0xCF81, 0x4F82      # +-2^32: outside any N(0, 0.02^2) top 16
+    n, k = w.shape
+    exps = [(int(v) >> 7) & 0xFF for v in w.ravel()]
+    cnt = Counter(exps)
+    pal = set(sorted(cnt, key=lambda x: (-cnt[x], x))[:16])
+    nv = 0
+    for r in range(n):
+        for b in range(k // 64):
+            if any(((int(w[r, c]) >> 7) & 0xFF) not in pal for c in range(64 * b, 64 * b + 64)):
+                nv += 1
+    n_pad, T, KB = 48, 3, 3
+    expect = n_pad * k + n_pad * k // 2 + 2 * T * KB + 4 * (T + 1) + 64 * nv
+    enc = codec.encode(w, n, k)
+    assert nv > 0 and enc["n_verb"] == nv
+    assert codec.resident_palette_bytes(enc) == expect
+
+
+# ------------------------------------------------------------------ caller palette (R15)
+def _shifted_palette(w, shift):
+    """The matrix's own top-16 moved by `shift` octaves: a palette of another matrix, so that
+    part of W falls outside it."""
+    cnt = Counter((int(v) >> 7) & 0xFF for v in np.asarray(w).ravel())
+    own = sorted(sorted(cnt, key=lambda x: (-cnt[x], x))[:16])
+    return [min(255, max(0, x + shift)) for x in own]
+
+
+def test_caller_palette_equal_to_own_gives_the_same_blob():
+    w = synth.small_gaussian(160, 512, seed=4, plant_frac=0.02)["w"]
+    n, k = w.shape
+    own = codec.analyse(w, n, k)["palette"]
+    assert codec.serialize(codec.encode(w, n, k, palette=list(own))) == codec.serialize(codec.encode(w, n, k))
+
+
+@pytest.mark.parametrize("shift", [1, 5, -1])
+def test_caller_palette_brute_force(shift):
+    """Flags, coded symbols and the header palette under another matrix's palette, computed
+    by loops on a tiny matrix; the bundle still decodes to W bit for bit."""
+    w = synth.small_gaussian(21, 128, seed=9, plant_frac=0.05)["w"]
+    n, k = w.shape
+    pal = sorted(set(_shifted_palette(w, shift)))
+    enc = codec.encode(w, n, k, chunk=64, palette=pal)
+    a = codec.analyse(w, n, k, palette=pal)
+    assert list(enc["palette"]) == pal
+    n_pad = 32
+    flags = np.zeros((n_pad // 16, k // 64), np.uint32)
+    symbols = []
+    for t in range(n_pad // 16):
+        for b in range(k // 64):
+            for r in range(16):
+                row = 16 * t + r
+                if row >= n:
+                    continue
+                seg = [(int(w[row, c]) >> 7) & 0xFF for c in range(64 * b, 64 * b + 64)]
+                if any(x not in pal for x in seg):
+                    flags[t, b] |= 1 << r
+                else:
+                    symbols.extend(pal.index(x) for x in seg)
+    assert np.array_equal(np.asarray(enc["flags"]).reshape(flags.shape).astype(np.uint32), flags)
+    assert list(a["symbols"]) == symbols
+    assert enc["n_verb"] == sum(bin(int(f)).count("1") for f in flags.ravel())
+    assert 0 < enc["n_verb"] < n * k // 64                  # some, not all, segments verbatim
+    blob = codec.serialize(enc)
+    assert np.array_equal(codec.decode_blob(blob), w)
+    d = codec.parse(blob)
+    w2 = codec.reconstruct_from_palette(d["sm"], codec.transcode_blob(blob), d["flags"], d["vprefix"], d["vexp"],
+                                        d["palette"], n, k)
+    assert np.array_equal(w2, w)
+
+
+def test_caller_palette_outside_every_exponent_makes_everything_verbatim():
+    w = synth.small_gaussian(20, 128, seed=2)["w"]
+    enc = codec.encode(w, 20, 128, palette=[250, 251, 252])   # |w| >= 2^123: never in N(0, 0.02^2)
+    assert enc["n_coded"] == 0 and enc["total_bits"] == 0 and enc["n_verb"] == 20 * 2
+    assert np.array_equal(codec.decode_blob(codec.serialize(enc)), w)
+
+
+@pytest.mark.parametrize("bad", [[], list(range(17)), [5, 4], [3, 3], [256], [-1]])
+def test_caller_palette_rejected(bad):
+    w = synth.small_gaussian(16, 64, seed=1)["w"]
+    with pytest.raises(ValueError):
+        codec.encode(w, 16, 64, palette=bad)
