@@ -85,32 +85,107 @@ def device_info():
     return info
 
 
-def cpu_baseline(w, x, seconds=10.0):
-    """The oracle (numpy) doing the same step on a row sample: rebuild W from the
-    direct-palette format and multiply in fp64.  Single-threaded (BLAS limited to 1)."""
+def _rate(fn, seconds):
+    """Repeat fn() for at least `seconds`; returns (calls, elapsed seconds)."""
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            return reps, el
+
+
+def cpu_baseline(w, x, seconds=2.5):
+    """The oracle (numpy, as it stands) on a bounded row sample of the same workload, on this
+    host's cores: the step itself (rebuild W from the direct-palette format, fp64 GEMV) and,
+    separately, oracle encode, oracle decode (Huffman bundle -> W) and the fp64 GEMV, each at
+    every core of this process's affinity set and again at one thread (BLAS threads limited
+    with threadpoolctl; the oracle's own loops are numpy, single-threaded).  Rates are
+    uncompressed-equivalent bytes of the sample (2 B a weight) per second."""
     from threadpoolctl import threadpool_limits
     from oracle import codec, gemm
     rows = 448                                   # 28 tiles of 16 rows
     ws = w[:rows]
-    enc = codec.encode(ws, rows, ws.shape[1])
+    k = ws.shape[1]
+    nbytes = 2.0 * rows * k
+    enc = codec.encode(ws, rows, k)
     blob = codec.serialize(enc)
     d = codec.parse(blob)
     idx = codec.transcode_blob(blob)
-    reps, t0 = 0, time.perf_counter()
-    with threadpool_limits(limits=1):
-        while True:
-            wr = codec.reconstruct_from_palette(d["sm"], idx, d["flags"], d["vprefix"], d["vexp"], d["palette"],
-                                                rows, ws.shape[1])
-            y, _ = gemm.gemm_ref(x, wr)
-            reps += 1
-            el = time.perf_counter() - t0
-            if el >= seconds:
-                break
-    assert np.array_equal(wr, ws)
-    gbs = 2.0 * rows * ws.shape[1] * reps / el / 1e9
-    return dict(value=round(gbs, 4), unit="GB/s", cores=1, kind="oracle",
-                sample="%d of 14336 rows (%d tiles) x 4096, %d reps in %.1f s: oracle palette rebuild + fp64 GEMV, "
-                       "1 thread, uncompressed-equivalent bytes" % (rows, rows // 16, reps, el))
+    cores = len(os.sched_getaffinity(0))
+
+    def step():
+        wr = codec.reconstruct_from_palette(d["sm"], idx, d["flags"], d["vprefix"], d["vexp"], d["palette"], rows, k)
+        return gemm.gemm_ref(x, wr)
+
+    parts = {"step": step,
+             "encode": lambda: codec.serialize(codec.encode(ws, rows, k)),
+             "decode": lambda: codec.decode_blob(blob),
+             "gemm_fp64": lambda: gemm.gemm_ref(x, ws)}
+    detail = {}
+    for threads in (cores, 1):
+        with threadpool_limits(limits=threads):
+            for name, fn in parts.items():
+                reps, el = _rate(fn, seconds)
+                detail["%s_%dt" % (name, threads)] = {"gb_s": round(nbytes * reps / el / 1e9, 4), "calls": reps,
+                                                      "s": round(el, 2)}
+    assert np.array_equal(codec.decode_blob(blob), ws)
+    return dict(value=detail["step_%dt" % cores]["gb_s"], unit="GB/s", cores=cores, kind="oracle",
+                sample="%d of 14336 rows (%d tiles) x %d of the same matrix and X: the oracle's step (direct-palette "
+                       "rebuild + fp64 GEMV) at all %d cores of the affinity set; detail: oracle encode, decode and "
+                       "fp64 GEMV at %d cores and at 1 thread, %.1f s each; uncompressed-equivalent bytes"
+                       % (rows, rows // 16, k, cores, cores, seconds),
+                cpu_model=device_info()["cpu_model"], threads=[cores, 1], detail=detail)
+
+
+class ClockSampler:
+    """Samples the GPU's current sclk/mclk (sysfs pp_dpm_*, the starred line) in a thread
+    while the timed region runs; reports min / median / max MHz over the samples."""
+
+    def __init__(self, period_s=0.002):
+        import threading
+        self.period = period_s
+        self.counts = {}      # clock name -> MHz samples
+        self._stop = threading.Event()
+        self._files = [os.path.join(dev, f) for dev in sorted(glob.glob("/sys/class/drm/card*/device"))[:1]
+                       for f in ("pp_dpm_sclk", "pp_dpm_mclk")]
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        out = {}
+        for path in self._files:
+            try:
+                with open(path) as fh:
+                    cur = [ln.strip() for ln in fh if ln.strip().endswith("*")]
+            except OSError:
+                continue
+            m = re.search(r"(\d+)\s*Mhz", cur[0], re.I) if cur else None
+            if m:
+                out[path.split("_")[-1]] = int(m.group(1))
+        return out
+
+    def _run(self):
+        while not self._stop.is_set():
+            for name, mhz in self._read().items():
+                self.counts.setdefault(name, []).append(mhz)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._thread.join()
+
+    def summary(self):
+        """{clock: {min, median, max MHz, samples}} over the timed region, or None."""
+        out = {}
+        for name, v in self.counts.items():
+            v = sorted(v)
+            out[name + "_mhz"] = {"min": v[0], "median": v[len(v) // 2], "max": v[-1], "samples": len(v)}
+        return out or None
 
 
 SETTLE_MS = 50.0
@@ -404,7 +479,7 @@ def main():
         print(json.dumps(diagnostic(args)), flush=True)
         return
 
-    dinfo = device_info()   # before the GPU is initialised here
+    dinfo = device_info()   # GPU name filled in below; clocks again after the timed region
     import torch
     import lossless_bf16_weight_amd as uw
     from lossless_bf16_weight_amd import autotune, synth
@@ -464,7 +539,8 @@ def main():
     ok = ogemm.within_bound(y.cpu().numpy().astype(np.float64)[:, rows], yr, s)
     assert ok.all(), "parity failure in the timed configuration"
 
-    total_ms, per = time_launches(step, copies, args.steps, args.warmup, stream)
+    with ClockSampler() as clk:
+        total_ms, per = time_launches(step, copies, args.steps, args.warmup, stream)
     us = total_ms * 1e3 / args.steps
     med, p10, p90 = per[len(per) // 2] * 1e3, per[len(per) // 10] * 1e3, per[(9 * len(per)) // 10] * 1e3
     eff_gbs = 2.0 * n * k / (us * 1e-6) / 1e9
@@ -494,6 +570,8 @@ def main():
 
     cpu = None if args.no_cpu else cpu_baseline(w, x)
     traffic = traffic_from_profile()
+    dinfo.update({k: v for k, v in device_info().items() if k != "gpu" and v is not None})
+    dinfo["clocks_during_timed_region"] = clk.summary()
     out = {
         "metric": METRIC,
         "value": round(eff_gbs, 1),
@@ -514,7 +592,11 @@ def main():
                    "rotation_copies": copies, "global_batch": 1, "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic},
+                     "traffic": traffic,
+                     "traffic_source": ("FETCH_SIZE + WRITE_SIZE from the committed rocprofv3 --pmc summary "
+                                        "(%s), taken on this kernel source (sha256[:16] %s); not measured in this run"
+                                        % (os.path.relpath(PMC_SUMMARY, ROOT), kernel_source_hash()))
+                                       if traffic is not None else None},
         "cpu_baseline": cpu,
         "us_per_gemm": round(us, 3),
         "us_per_gemm_single_launch": {"median": round(med, 3), "p10": round(p10, 3), "p90": round(p90, 3)},

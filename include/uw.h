@@ -109,13 +109,19 @@ uw_status uw_encode_bound(int64_t n, int64_t k, int32_t chunk, size_t* bytes);
 
 /* Encode W into a UW1 blob (Huffman, rare-exponent and four-pipeline paragraphs).
  * w:      host, n*k BF16 bit patterns, row-major.
+ * p:      the palette to encode with, or NULL to build W's own (uw_build_palette's choice).
+ *         A caller palette (e.g. one shared by several matrices, or another matrix's) replaces
+ *         only that step: every 64-weight segment holding an exponent outside it is stored
+ *         verbatim and the Huffman code is built over the indices of the other segments.
+ *         Checked: 1 <= n <= 16, exp[0..n-1] strictly ascending, index_of[exp[i]] == i and
+ *         0xFF for every other exponent (UW_E_ARG otherwise); hist is not read.
  * chunk:  coded symbols per chunk, a multiple of 64 in [64, UW_MAX_CHUNK]; 0 = 512 (a block
  *         holds at most 1024 coded symbols, so values above 1024 act as 1024).
  * blob:   host output of `cap` bytes; NULL asks for the exact size only (two-call pattern).
  * used:   receives the blob size in bytes.
- * Errors: UW_E_ARG (null w/used), UW_E_SHAPE (k % 64, stream >= 2^32 bits), UW_E_NOMEM,
- *         UW_E_WORKSPACE (cap too small; *used holds the size needed). */
-uw_status uw_encode(const uint16_t* w, int64_t n, int64_t k, int32_t chunk,
+ * Errors: UW_E_ARG (null w/used, bad palette), UW_E_SHAPE (k % 64, stream >= 2^32 bits),
+ *         UW_E_NOMEM, UW_E_WORKSPACE (cap too small; *used holds the size needed). */
+uw_status uw_encode(const uint16_t* w, int64_t n, int64_t k, const uw_palette* p, int32_t chunk,
                     void* blob, size_t cap, size_t* used);
 
 /* Header fields of a blob, validated (host).  Sizes in bytes. */
@@ -301,6 +307,12 @@ uw_status uw_sched_init(uw_sched* s, int32_t layers, int32_t m, int32_t hidden, 
  * stream's decodes are ordered by events, and the next step's first decodes wait for this
  * step's last use of their slots. */
 uw_status uw_sched_step(uw_sched* s, const uint16_t* x, uint16_t** out);
+/* Per-layer record of every following step (for checking each GEMM of a scheduled step on its
+ * own inputs): after layer l's GEMMs the main stream copies g [m, inter] fp32, h [m, inter] BF16,
+ * y [m, hidden] fp32 and the layer output [m, hidden] BF16, back to back, to
+ * trace + l * m * (6 * inter + 6 * hidden).  trace: device, at least layers times that many
+ * bytes (UW_E_WORKSPACE otherwise), borrowed until replaced; NULL stops the recording. */
+uw_status uw_sched_trace(uw_sched* s, void* trace, size_t bytes);
 /* Releases the events and host state (waits for nothing: the caller synchronises first). */
 uw_status uw_sched_release(uw_sched* s);
 

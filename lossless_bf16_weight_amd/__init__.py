@@ -32,7 +32,7 @@ EXPORTS = ("uw_last_error", "uw_version", "uw_build_palette", "uw_encode_bound",
            "uw_variant_count", "uw_variant_name", "uw_check", "uw_autotune_load", "uw_autotune_set",
            "uw_autotune_get", "uw_autotune_set_variant", "uw_autotune_get_variant", "uw_autotune_clear", "uw_swiglu",
            "uw_gemm_swiglu", "uw_gemm_rmsnorm", "uw_rmsnorm", "uw_sched_size", "uw_sched_init", "uw_sched_step",
-           "uw_sched_release")
+           "uw_sched_trace", "uw_sched_release")
 
 
 class UwError(RuntimeError):
@@ -80,7 +80,7 @@ def lib():
         "uw_version": (_I32, []),
         "uw_build_palette": (_I32, [_P, _I64, _I64, ctypes.POINTER(Palette)]),
         "uw_encode_bound": (_I32, [_I64, _I64, _I32, ctypes.POINTER(_S)]),
-        "uw_encode": (_I32, [_P, _I64, _I64, _I32, _P, _S, ctypes.POINTER(_S)]),
+        "uw_encode": (_I32, [_P, _I64, _I64, ctypes.POINTER(Palette), _I32, _P, _S, ctypes.POINTER(_S)]),
         "uw_blob_info": (_I32, [_P, _S, ctypes.POINTER(Info)]),
         "uw_dmat_size": (_S, []),
         "uw_dmat_bind": (_I32, [_P, _P, _S, _P, _P]),
@@ -109,6 +109,7 @@ def lib():
         "uw_sched_init": (_I32, [_P, _I32, _I32, _I32, _I32, _P, _P, _P, _S, _P, _P, _P, _P, _P, _S, _P, _S, _F,
                                  _P, _P]),
         "uw_sched_step": (_I32, [_P, _P, ctypes.POINTER(ctypes.c_void_p)]),
+        "uw_sched_trace": (_I32, [_P, _P, _S]),
         "uw_sched_release": (_I32, [_P]),
     }
     for name, (res, args) in sig.items():
@@ -176,14 +177,40 @@ def uw_encode_bound(n, k, chunk=0):
     return out.value
 
 
-def uw_encode(w, chunk=0):
-    """Encode a [n, k] uint16 BF16 matrix; returns the blob as a uint8 numpy array."""
+def _palette_struct(palette):
+    """uw_palette from a uw_build_palette() dict, or from a list of exponents (index_of is the
+    list's inverse; the library checks the result)."""
+    if palette is None:
+        return None
+    p = Palette()
+    exps = list(palette["exp"]) if isinstance(palette, dict) else [int(v) for v in palette]
+    if not 1 <= len(exps) <= 16:
+        raise ValueError("a palette holds 1..16 exponents (got %d)" % len(exps))
+    p.n = len(exps)
+    for i, e in enumerate(exps):
+        p.exp[i] = e
+    if isinstance(palette, dict) and "index_of" in palette:
+        for x in range(256):
+            p.index_of[x] = int(palette["index_of"][x])
+    else:
+        for x in range(256):
+            p.index_of[x] = 0xFF
+        for i, e in enumerate(exps):
+            p.index_of[e] = i
+    return p
+
+
+def uw_encode(w, chunk=0, palette=None):
+    """Encode a [n, k] uint16 BF16 matrix; returns the blob as a uint8 numpy array.
+    palette: None (W's own top-16), a uw_build_palette() dict, or ascending exponents."""
     w = np.ascontiguousarray(w, dtype=np.uint16)
     n, k = w.shape
     used = ctypes.c_size_t()
-    _check(lib().uw_encode(w.ctypes.data, n, k, chunk, None, 0, ctypes.byref(used)))
+    p = _palette_struct(palette)
+    pp = ctypes.byref(p) if p is not None else None
+    _check(lib().uw_encode(w.ctypes.data, n, k, pp, chunk, None, 0, ctypes.byref(used)))
     blob = np.zeros(used.value, np.uint8)
-    _check(lib().uw_encode(w.ctypes.data, n, k, chunk, blob.ctypes.data, blob.size, ctypes.byref(used)))
+    _check(lib().uw_encode(w.ctypes.data, n, k, pp, chunk, blob.ctypes.data, blob.size, ctypes.byref(used)))
     return blob
 
 
@@ -374,6 +401,12 @@ class Sched:
         _check(lib().uw_sched_step(self.buf, _dev(x, "x", 2 * m_hidden, _U16), ctypes.byref(out)))
         return out.value
 
+    def trace(self, buf):
+        """Record g, h, y and the output of every layer of the following steps into buf (a
+        device tensor of layers * m * (6 * inter + 6 * hidden) bytes), or stop with None."""
+        self.trace_buf = buf
+        _check(lib().uw_sched_trace(self.buf, _dev(buf, "trace", 0, optional=True), _nbytes(buf)))
+
     def release(self):
         if self.live:
             _check(lib().uw_sched_release(self.buf))
@@ -393,9 +426,9 @@ class CompressedMatrix:
     """Encode W on the host (C++), copy the blob to the device, bind it and run the
     load-time transcode to the direct-palette index stream (a device kernel)."""
 
-    def __init__(self, w, chunk=0, device="cuda", blob=None, keep_index=True):
+    def __init__(self, w, chunk=0, device="cuda", blob=None, keep_index=True, palette=None):
         import torch
-        self.blob = uw_encode(w, chunk) if blob is None else np.ascontiguousarray(blob, np.uint8)
+        self.blob = uw_encode(w, chunk, palette) if blob is None else np.ascontiguousarray(blob, np.uint8)
         self.blob_dev = torch.from_numpy(self.blob).to(device)
         info = uw_blob_info(self.blob)
         self.idx = torch.empty(int(info["idx_bytes"]), dtype=torch.uint8, device=device) if keep_index else None

@@ -2459,7 +2459,12 @@ struct SchedImpl {
   float eps = 1e-5f;
   hipStream_t main = nullptr, side = nullptr;
   hipEvent_t dec_done[2] = {nullptr, nullptr}, use_done[2] = {nullptr, nullptr};
+  uint8_t* trace = nullptr;  // per-layer copies of g, h, y and the layer output (uw_sched_trace)
 };
+// Bytes of one layer's record in a trace: g (fp32), h (BF16), y (fp32), layer output (BF16).
+static size_t sched_trace_layer_bytes(const SchedImpl* S) {
+  return (size_t)S->m * (6 * (size_t)S->inter + 6 * (size_t)S->hidden);
+}
 constexpr uint64_t kSchedMagic = 0x3130484353575555ull;  // "UUWSCH01"
 }  // namespace uw
 
@@ -2604,6 +2609,17 @@ uw_status uw_sched_step(uw_sched* s, const uint16_t* x, uint16_t** out) {
       st = gemm_entry(&v[2], S->h, S->y, nullptr, nullptr, o, S->eps, S->m, UW_PIPE_DIRECT_PALETTE, -1, S->ws,
                           S->ws_bytes, S->main);
     if (st) return st;
+    if (S->trace) {
+      uint8_t* rec = S->trace + (size_t)l * uw::sched_trace_layer_bytes(S);
+      const size_t gi = (size_t)S->m * S->inter, hd = (size_t)S->m * S->hidden;
+      const void* src[4] = {S->g, S->h, S->y, o};
+      const size_t len[4] = {4 * gi, 2 * gi, 4 * hd, 2 * hd};
+      for (int q = 0; q < 4; ++q) {
+        if (hipMemcpyAsync(rec, src[q], len[q], hipMemcpyDeviceToDevice, S->main) != hipSuccess)
+          return fail(UW_E_HIP, "trace copy failed");
+        rec += len[q];
+      }
+    }
     if (is_hard) {
       if (hipEventRecord(S->use_done[hi & 1], S->main) != hipSuccess) return fail(UW_E_HIP, "event record failed");
       if (hi + 2 < H && (st = uw::sched_issue_decode(S, hi + 2))) return st;
@@ -2612,6 +2628,16 @@ uw_status uw_sched_step(uw_sched* s, const uint16_t* x, uint16_t** out) {
     cur = o;
   }
   *out = const_cast<uint16_t*>(cur);
+  clear_error();
+  return UW_OK;
+}
+
+uw_status uw_sched_trace(uw_sched* s, void* trace, size_t bytes) {
+  if (!s || s->magic != uw::kSchedMagic || !s->impl) return fail(UW_E_ARG, "scheduler is not initialised");
+  uw::SchedImpl* S = s->impl;
+  const size_t need = (size_t)S->layers * uw::sched_trace_layer_bytes(S);
+  if (trace && bytes < need) return fail(UW_E_WORKSPACE, "trace needs %zu bytes, got %zu", need, bytes);
+  S->trace = reinterpret_cast<uint8_t*>(trace);
   clear_error();
   return UW_OK;
 }

@@ -165,6 +165,20 @@ static void palette_from_hist(const uint64_t hist[256], uw_palette* p) {
   for (int x = 0; x < 256; ++x) p->hist[x] = hist[x];
 }
 
+// A caller palette (uw_encode's p): size 1..16, exponents strictly ascending, index_of the
+// exact inverse of exp (0xFF for every exponent outside it).
+static uw_status check_palette(const uw_palette* p) {
+  if (p->n < 1 || p->n > 16) return fail(UW_E_ARG, "palette size %u is not in 1..16", p->n);
+  for (uint32_t i = 1; i < p->n; ++i)
+    if (p->exp[i] <= p->exp[i - 1]) return fail(UW_E_ARG, "palette exponents are not strictly ascending");
+  uint8_t inv[256];
+  std::memset(inv, 0xFF, 256);
+  for (uint32_t i = 0; i < p->n; ++i) inv[p->exp[i]] = (uint8_t)i;
+  for (int x = 0; x < 256; ++x)
+    if (p->index_of[x] != inv[x]) return fail(UW_E_ARG, "palette index_of[%d] = %u, expected %u", x, p->index_of[x], inv[x]);
+  return UW_OK;
+}
+
 static uw_status check_shape(int64_t n, int64_t k) {
   if (n < 1 || k < kSeg) return fail(UW_E_ARG, "n=%lld k=%lld must be positive (k >= 64)", (long long)n, (long long)k);
   if (k % kSeg) return fail(UW_E_SHAPE, "k=%lld is not a multiple of 64", (long long)k);
@@ -263,10 +277,11 @@ static uint32_t tile_chunks(const uint16_t* flags, int64_t kb, int rows, int chu
   return (uint32_t)c;
 }
 
-static uw_status encode_impl(const uint16_t* w, int64_t n, int64_t k, int32_t chunk, uint8_t* blob, size_t cap,
-                             size_t* used) {
+static uw_status encode_impl(const uint16_t* w, int64_t n, int64_t k, const uw_palette* p_in, int32_t chunk,
+                             uint8_t* blob, size_t cap, size_t* used) {
   uw_status st = check_shape(n, k);
   if (st) return st;
+  if (p_in && (st = check_palette(p_in))) return st;
   if (chunk == 0) chunk = kDefaultChunk;
   if (chunk < kSeg || chunk > UW_MAX_CHUNK || chunk % kSeg)
     return fail(UW_E_ARG, "chunk=%d must be a multiple of 64 in [64, %d]", chunk, UW_MAX_CHUNK);
@@ -280,7 +295,12 @@ static uw_status encode_impl(const uint16_t* w, int64_t n, int64_t k, int32_t ch
   L.chunk = chunk;
 
   uw_palette pal;
-  {
+  if (p_in) {
+    std::memset(&pal, 0, sizeof(pal));
+    pal.n = p_in->n;
+    for (uint32_t i = 0; i < pal.n; ++i) pal.exp[i] = p_in->exp[i];
+    std::memcpy(pal.index_of, p_in->index_of, 256);
+  } else {
     uint64_t hist[256];
     histogram(w, n, k, hist);
     palette_from_hist(hist, &pal);
@@ -644,10 +664,11 @@ uw_status uw_encode_bound(int64_t n, int64_t k, int32_t chunk, size_t* bytes) {
   return UW_OK;
 }
 
-uw_status uw_encode(const uint16_t* w, int64_t n, int64_t k, int32_t chunk, void* blob, size_t cap, size_t* used) {
+uw_status uw_encode(const uint16_t* w, int64_t n, int64_t k, const uw_palette* p, int32_t chunk, void* blob,
+                    size_t cap, size_t* used) {
   if (!w || !used) return fail(UW_E_ARG, "null argument");
   try {
-    uw_status st = encode_impl(w, n, k, chunk, reinterpret_cast<uint8_t*>(blob), cap, used);
+    uw_status st = encode_impl(w, n, k, p, chunk, reinterpret_cast<uint8_t*>(blob), cap, used);
     if (st == UW_OK) clear_error();
     return st;
   } catch (const std::bad_alloc&) {

@@ -150,13 +150,36 @@ class HardEasyStack:
         self.sched = Sched([cm.d for cm in flat], hard, m, hidden, inter, self.slots, self.slot_bytes, self.g, self.h,
                            self.y, self.xo, self.ws, self.dws, eps, torch.cuda.current_stream(self.dev), self.side)
 
-    def step(self, x, check=True):
+    def step(self, x, check=True, trace=None):
         """One decode step from x (device int16 [m, hidden], BF16 bits) on the current stream
-        (the one bound at construction).  Returns the output half of xo."""
+        (the one bound at construction).  Returns the output half of xo.  trace: optional list
+        that receives, per layer, host copies (x_in, g, h, y, x_out) recorded by the library
+        during the step (uw_sched_trace) -- for tests; it synchronises."""
+        import torch
+        m, hid, inter = self.m, self.hidden, self.inter
+        per = m * (6 * inter + 6 * hid)
+        if trace is not None:
+            buf = torch.empty(len(self.layers) * per, dtype=torch.uint8, device=self.dev)
+            self.sched.trace(buf)
         addr = self.sched.step(x)
         out = self.xo[0] if addr == self.xo[0].data_ptr() else self.xo[1]
+        if trace is not None:
+            self.sched.trace(None)
+            torch.cuda.synchronize(self.dev)
+            host = buf.cpu().numpy()
+            cur = x.cpu().numpy()
+            for l in range(len(self.layers)):
+                rec = host[l * per:(l + 1) * per]
+                o = 0
+                parts = []
+                for cnt, dt in ((m * inter, np.float32), (m * inter, np.int16), (m * hid, np.float32),
+                                (m * hid, np.int16)):
+                    nb = cnt * np.dtype(dt).itemsize
+                    parts.append(rec[o:o + nb].view(dt).reshape(m, -1).copy())
+                    o += nb
+                trace.append((cur,) + tuple(parts))
+                cur = parts[3]
         if check:
-            import torch
             torch.cuda.synchronize(self.dev)
             uw_check(self.dws)
         return out

@@ -32,6 +32,18 @@ def gemm_ref(x_bits, w_bits):
     return x @ w.T, np.abs(x) @ np.abs(w).T
 
 
+def gemm_ref_multi(xs_bits, w_bits):
+    """gemm_ref of several inputs X against one W (W converted to fp64 once): a list of
+    (y, s) pairs, one per X."""
+    w = bf16_to_f64(w_bits)
+    aw = np.abs(w)
+    out = []
+    for xb in xs_bits:
+        x = bf16_to_f64(xb)
+        out.append((x @ w.T, np.abs(x) @ aw.T))
+    return out
+
+
 def gemm_ref_rows(x_bits, w_bits, rows):
     """gemm_ref restricted to the output columns `rows` (rows of W), for sampled checks."""
     w = np.asarray(w_bits)[np.asarray(rows)]

@@ -131,6 +131,53 @@ def test_gemm_all_pipelines(name, m):
         check_gemm(y, x, w)
 
 
+def _other_palette(w, shift, swap=0):
+    """Another matrix's palette: W's own top 16 moved by `shift` octaves; with swap > 0 its
+    `swap` smallest exponents are replaced by distant large ones (a gap makes the palette
+    non-affine, so the kernels take the table-lookup path)."""
+    n, k = w.shape
+    own = sorted(int(x) for x in codec.analyse(w, n, k)["palette"])
+    own = own[swap:] + [200 + i for i in range(swap)]
+    return sorted({min(255, max(0, x + shift)) for x in own})
+
+
+@pytest.mark.parametrize("shift,swap", [(5, 0), (0, 3), (-1, 0)], ids=["shift5", "gap_lut", "shift-1"])
+def test_caller_palette_end_to_end(shift, swap):
+    """uw_encode with a caller palette (another matrix's, so a large share of segments is
+    verbatim): the blob is the oracle's, every decoder is bit-exact, and every pipeline's GEMM
+    is within the oracle bound."""
+    t = torch()
+    w = synth.small_gaussian(200, 1024, seed=17, plant_frac=0.02)["w"]
+    n, k = w.shape
+    pal = _other_palette(w, shift, swap)
+    blob = uw.uw_encode(w, 256, palette=pal)
+    ref_blob = codec.serialize(codec.encode(w, n, k, chunk=256, palette=pal))
+    assert blob.tobytes() == ref_blob
+    info = uw.uw_blob_info(blob)
+    assert list(info["palette"][: len(pal)]) == pal and 0 < info["n_verb"] < n * k // 64
+    assert bool(info["affine"]) == (swap == 0)
+    cm = uw.CompressedMatrix(w, blob=blob)
+    ws = err_ws()
+    out = t.empty((n, k), dtype=t.int16, device="cuda")
+    uw.uw_decode_full(cm.d, out, ws)
+    uw.uw_check(ws)
+    assert np.array_equal(host_u16(out), w)
+    assert cm.idx.cpu().numpy().tobytes() == codec.transcode_blob(ref_blob).tobytes()
+    ex = t.empty(int(cm.info["np"]) * k, dtype=t.uint8, device="cuda")
+    uw.uw_decode_exponents(cm.d, ex, ws)
+    uw.uw_check(ws)
+    assert ex.cpu().numpy().tobytes() == codec.exponent_stream_blob(ref_blob).tobytes()
+    for m in (1, 16, 64):
+        x = synth.gaussian_bf16(np.random.default_rng(300 + m), (m, k), 1.0)
+        for pipe in ALL_PIPES:
+            wsp = cm.workspace(m, pipe)
+            y = t.full((m, n), float("nan"), dtype=t.float32, device="cuda")
+            uw.uw_gemm(cm.d, dev_u16(x), y, m, pipe, wsp)
+            if wsp is not None:
+                uw.uw_check(wsp)
+            check_gemm(y, x, w)
+
+
 N_VARIANTS = 18
 SHARED_X_VARIANTS = (14, 15)   # kind 2: whole tiles per wave, X rows shared in LDS
 WIDE_VARIANTS = (16, 17)       # kind 3: tile pairs per wave, 32x32 MFMAs (palette sources)
@@ -570,6 +617,68 @@ def test_hard_easy_stack_equals_plain(m, hard):
         xa, xb = a, b
     assert sched.resident_bytes() < plain.resident_bytes() + 6 * sched.slot_bytes + 1
     sched.close()
+
+
+def bf16_key(bits):
+    """Monotone integer key of BF16 bit patterns (adjacent keys = adjacent values; +0 and -0
+    share key 0)."""
+    b = np.asarray(bits, np.uint16).astype(np.int64)
+    return np.where(b & 0x8000, -(b & 0x7FFF), b)
+
+
+def check_swiglu_through_gemm_bound(h, g, x_in, w_up):
+    """The fused up GEMM + SwiGLU epilogue, checked on the device's own g and x: for every u
+    within the GEMM bound of the oracle's (|u - u_ref| <= 1e-3 S), silu(g) * u lies between
+    silu(g) * (u_ref -+ 1e-3 S); h must be within one BF16 step of the rounded ends of that
+    interval (the step covers the fp32 silu)."""
+    u_ref, s = gemm.gemm_ref(x_in, w_up)
+    g64 = np.asarray(g, np.float64)
+    with np.errstate(over="ignore"):                          # exp(-g) = inf for g << 0: silu -> -0
+        silu = g64 / (1.0 + np.exp(-g64))
+    a, b = silu * (u_ref - 1e-3 * s), silu * (u_ref + 1e-3 * s)
+    lo = bf16_key(gemm.f64_to_bf16_rne(np.minimum(a, b)))
+    hi = bf16_key(gemm.f64_to_bf16_rne(np.maximum(a, b)))
+    k = bf16_key(h)
+    ok = (k >= lo - 1) & (k <= hi + 1)
+    assert ok.all(), "%d of %d SwiGLU outputs outside the interval" % ((~ok).sum(), ok.size)
+
+
+@pytest.mark.parametrize("m", [1, 16])
+@pytest.mark.parametrize("hard", [(0, 2), (0, 1, 2, 3)], ids=["alternate", "all"])
+def test_hard_easy_stack_against_oracle(m, hard):
+    """Each GEMM of a scheduled step (hard layers decoded on the side stream) against the
+    oracle on the inputs the device fed it (teacher-forced, from the library's per-layer
+    trace): gate y = x W^T and down y = h W^T within the GEMM bound, the up GEMM through its
+    fused SwiGLU epilogue within the bound's interval, the RMS norm within one BF16 ulp; two
+    steps in a row, the second from the first's output."""
+    from lossless_bf16_weight_amd.stack import HardEasyStack
+    rng = np.random.default_rng(31)
+    hidden, inter, layers = 256, 704, 4
+    mats = [(synth.small_gaussian(inter, hidden, seed=100 + 3 * l, plant_frac=0.01)["w"],
+             synth.gaussian_bf16(rng, (inter, hidden), 0.03),
+             synth.student_t_bf16(rng, (hidden, inter), 3, 0.02)) for l in range(layers)]
+    sched = HardEasyStack(m, hidden, inter, mats, hard_layers=hard)
+    x = dev_u16(synth.gaussian_bf16(rng, (m, hidden), 1.0))
+    for step in range(2):
+        trace = []
+        out = sched.step(x, trace=trace).clone()
+        assert len(trace) == layers
+        for l, (xi, g, h, y, xo) in enumerate(trace):
+            wg, wu, wd = mats[l]
+            xi, h, xo = xi.view(np.uint16), h.view(np.uint16), xo.view(np.uint16)
+            check_gemm_host(g, xi, wg, "step %d layer %d gate" % (step, l))
+            check_swiglu_through_gemm_bound(h, g, xi, wu)
+            check_gemm_host(y, h, wd, "step %d layer %d down" % (step, l))
+            assert np.abs(xo.astype(np.int32) - gemm.rmsnorm_ref(y).astype(np.int32)).max() <= 1
+        assert np.array_equal(host_u16(out), trace[-1][4].view(np.uint16))
+        x = out
+    sched.close()
+
+
+def check_gemm_host(y, x, w, what):
+    y_ref, s = gemm.gemm_ref(x, w)
+    ok = gemm.within_bound(np.asarray(y, np.float64), y_ref, s)
+    assert ok.all(), "%s: %d outside bound" % (what, (~ok).sum())
 
 
 @pytest.mark.parametrize("k", [28672, 32768], ids=["28_blocks_a_slice", "32_blocks_a_slice"])

@@ -72,6 +72,52 @@ def test_config1_blob_equals_oracle():
     assert np.array_equal(uw.uw_encode(w), oracle_blob(w))
 
 
+def _other_palette(w, shift):
+    """Another matrix's palette: W's own top 16 moved by `shift` octaves (oracle's choice)."""
+    n, k = w.shape
+    own = [int(x) for x in codec.analyse(w, n, k)["palette"]]
+    return sorted({min(255, max(0, x + shift)) for x in own})
+
+
+@pytest.mark.parametrize("name,make", CASES[:2] + CASES[6:7], ids=[CASES[i][0] for i in (0, 1, 6)])
+@pytest.mark.parametrize("shift", [0, 1, 5])
+@pytest.mark.parametrize("chunk", [64, 512])
+def test_encoder_caller_palette_equals_oracle(name, make, shift, chunk):
+    """uw_encode with a caller palette (another matrix's, so part of W becomes verbatim) writes
+    the oracle's blob byte for byte; with W's own palette (shift 0) the blob equals the
+    palette-less encode."""
+    w = make()
+    n, k = w.shape
+    pal = _other_palette(w, shift)
+    blob = uw.uw_encode(w, chunk, palette=pal)
+    ref = np.frombuffer(codec.serialize(codec.encode(w, n, k, chunk=chunk, palette=pal)), np.uint8)
+    assert np.array_equal(blob, ref)
+    if shift == 0:
+        assert np.array_equal(blob, uw.uw_encode(w, chunk))
+        assert np.array_equal(uw.uw_encode(w, chunk, palette=uw.uw_build_palette(w)), blob)
+
+
+def test_encoder_rejects_bad_caller_palettes():
+    import ctypes
+    w = synth.small_gaussian(32, 128, seed=1)["w"]
+    good = uw._palette_struct([100, 110, 120])
+    L = uw.lib()
+    used = ctypes.c_size_t()
+
+    def status(p):
+        return L.uw_encode(w.ctypes.data, 32, 128, ctypes.byref(p), 0, None, 0, ctypes.byref(used))
+
+    assert status(good) == uw.UW_OK
+    for mutate in (lambda p: setattr(p, "n", 0), lambda p: setattr(p, "n", 17),
+                   lambda p: p.exp.__setitem__(1, 100),                 # not strictly ascending
+                   lambda p: p.index_of.__setitem__(7, 0),              # index_of not the inverse
+                   lambda p: p.index_of.__setitem__(110, 2)):
+        p = uw._palette_struct([100, 110, 120])
+        mutate(p)
+        assert status(p) == uw.UW_E_ARG
+        assert "palette" in uw.lib().uw_last_error().decode()
+
+
 def test_palette_matches_oracle():
     w = synth.small_gaussian(64, 640, seed=7, plant_frac=0.1)["w"]
     p = uw.uw_build_palette(w)

@@ -31,6 +31,20 @@ def test_gemm_ref_equals_exact_rational(m, n, k, seed):
             assert abs(Fraction(s[i, j]) - absum) <= Fraction(k, 2 ** 52) * absum
 
 
+def test_gemm_ref_multi_equals_exact_rational():
+    """The several-inputs form, pinned the same way: exact rational dot products."""
+    rng = np.random.default_rng(9)
+    w = synth.gaussian_bf16(rng, (3, 64), 0.02)
+    xs = [synth.gaussian_bf16(rng, (m, 64), 1.0) for m in (1, 2)]
+    for x, (y, s) in zip(xs, gemm.gemm_ref_multi(xs, w)):
+        for i in range(x.shape[0]):
+            for j in range(3):
+                exact = sum(frac_bf16(x[i, c]) * frac_bf16(w[j, c]) for c in range(64))
+                absum = sum(abs(frac_bf16(x[i, c]) * frac_bf16(w[j, c])) for c in range(64))
+                assert abs(Fraction(y[i, j]) - exact) <= Fraction(64, 2 ** 52) * absum
+                assert abs(Fraction(s[i, j]) - absum) <= Fraction(64, 2 ** 52) * absum
+
+
 def test_gemm_orientation_and_identity():
     """W rows that hold a single 1.0 select the matching input: y[:, j] = x[:, j]."""
     rng = np.random.default_rng(3)
