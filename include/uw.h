@@ -200,6 +200,21 @@ uw_status uw_gemm_variant(const uw_dmat* d, const uint16_t* x, float* y, int32_t
                           int32_t pipeline, int32_t variant, void* ws, size_t ws_bytes,
                           hipStream_t s);
 
+/* Allocation-free form of uw_gemm_variant(d, x, y, m, UW_PIPE_DIRECT_PALETTE, variant, ws, ...),
+ * for callers that cannot allocate device memory around the call (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): no workspace argument, and the call
+ * allocates nothing.  The K-slice partial sums of the multi-tile and wide-tile kernels go to a
+ * device array inside the library of 64 MiB per GPU (held on every GPU the library runs on until
+ * the process ends).  With the same variant the result is bit-identical to uw_gemm_variant given
+ * a workspace of uw_workspace_size(d, m, UW_PIPE_DIRECT_PALETTE) bytes.  The array is shared by
+ * every call on a GPU: calls that may overlap on one GPU (other streams, other threads) race and
+ * must be serialised by the caller.  x, y, m, variant and stream as uw_gemm_variant; d needs an
+ * index stream bound.  Errors: UW_E_ARG, UW_E_SHAPE, UW_E_HIP, and UW_E_WORKSPACE when the
+ * call's partial sums (uw_workspace_size(...) - 256 bytes) exceed 64 MiB; nothing is launched
+ * on an error. */
+uw_status uw_gemm_noalloc(const uw_dmat* d, const uint16_t* x, float* y, int32_t m, int32_t variant,
+                          hipStream_t s);
+
 /* Uncompressed baseline (the BF16 GEMM of pipeline 1): Y = X W^T for a plain BF16 W
  * (device, [n, k] row-major).  variant: -1 = the UW_PIPE_BF16 autotune entry, else default. */
 uw_status uw_gemm_bf16(const uint16_t* w, int64_t n, int64_t k, const uint16_t* x, float* y,

@@ -28,7 +28,8 @@ PIPELINES = {"full": UW_PIPE_FULL_DECODE, "exp": UW_PIPE_EXP_ONLY, "transcode": 
 # Every symbol include/uw.h declares (checked by the CPU tests).
 EXPORTS = ("uw_last_error", "uw_version", "uw_build_palette", "uw_encode_bound", "uw_encode", "uw_blob_info",
            "uw_dmat_size", "uw_dmat_bind", "uw_dmat_get_info", "uw_workspace_size", "uw_decode_full",
-           "uw_transcode_palette", "uw_decode_exponents", "uw_gemm", "uw_gemm_variant", "uw_gemm_bf16",
+           "uw_transcode_palette", "uw_decode_exponents", "uw_gemm", "uw_gemm_variant", "uw_gemm_noalloc",
+           "uw_gemm_bf16",
            "uw_variant_count", "uw_variant_name", "uw_check", "uw_autotune_load", "uw_autotune_set",
            "uw_autotune_get", "uw_autotune_set_variant", "uw_autotune_get_variant", "uw_autotune_clear", "uw_swiglu",
            "uw_gemm_swiglu", "uw_gemm_rmsnorm", "uw_rmsnorm", "uw_sched_size", "uw_sched_init", "uw_sched_step",
@@ -91,6 +92,7 @@ def lib():
         "uw_decode_exponents": (_I32, [_P, _P, _P, _S, _P]),
         "uw_gemm": (_I32, [_P, _P, _P, _I32, _I32, _P, _S, _P]),
         "uw_gemm_variant": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P, _S, _P]),
+        "uw_gemm_noalloc": (_I32, [_P, _P, _P, _I32, _I32, _P]),
         "uw_gemm_bf16": (_I32, [_P, _I64, _I64, _P, _P, _I32, _I32, _P]),
         "uw_variant_count": (_I32, []),
         "uw_variant_name": (ctypes.c_char_p, [_I32]),
@@ -287,6 +289,13 @@ def uw_gemm(d, x, y, m, pipeline=UW_PIPE_AUTO, ws=None, stream=None):
 def uw_gemm_variant(d, x, y, m, pipeline, variant, ws=None, stream=None):
     px, py, pw = _gemm_ptrs(int(d.info["n"]), int(d.info["k"]), x, y, m, ws)
     _check(lib().uw_gemm_variant(d.handle, px, py, m, pipeline, variant, pw, _nbytes(ws), _stream(stream)))
+
+
+def uw_gemm_noalloc(d, x, y, m, variant=-1, stream=None):
+    """Direct-palette GEMM with no workspace: the library's own device scratch holds the K-slice
+    partial sums (calls overlapping on one GPU race; see include/uw.h)."""
+    px, py, _ = _gemm_ptrs(int(d.info["n"]), int(d.info["k"]), x, y, m, None)
+    _check(lib().uw_gemm_noalloc(d.handle, px, py, m, variant, _stream(stream)))
 
 
 def uw_gemm_swiglu(d, x, gate, h, m, pipeline=UW_PIPE_AUTO, variant=-1, ws=None, stream=None):

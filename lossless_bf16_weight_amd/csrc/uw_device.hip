@@ -18,6 +18,7 @@
 #include <algorithm>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <type_traits>
 #include <vector>
@@ -2362,6 +2363,56 @@ uw_status uw_gemm_rmsnorm(const uw_dmat* d, const uint16_t* x, float* y, uint16_
                           int32_t pipeline, int32_t variant, void* ws, size_t ws_bytes, hipStream_t s) {
   if (!xn || !y) return fail(UW_E_ARG, "null y or xn");
   return gemm_entry(d, x, y, nullptr, nullptr, xn, eps, m, pipeline, variant, ws, ws_bytes, s);
+}
+
+}  // extern "C"
+
+// =========================================================================================
+// Allocation-free GEMM: the K-slice partial sums live in a device array of the library
+// (kStaticScratchBytes a device, held until the process ends) instead of a caller workspace.
+// Host code never passes the array's name to a kernel (in host code it is a stand-in, not a
+// device address): its address on each device comes from hipGetSymbolAddress, taken once per
+// device with that device current.
+// =========================================================================================
+namespace uw {
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+}
+static __device__ __align__(256) uint8_t scratch[uw::kErrBytes + uw::kStaticScratchBytes];
+
+namespace uw {
+static uw_status static_scratch(void** out) {
+  static std::mutex mu;
+  static void* ptr[64] = {nullptr};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return fail(UW_E_HIP, "cannot query the current device");
+  std::lock_guard<std::mutex> lk(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(UW_E_HIP, "device scratch of device %d: %s", dev, e != hipSuccess ? hipGetErrorString(e) : "null");
+    ptr[dev] = p;
+  }
+  *out = ptr[dev];
+  return UW_OK;
+}
+}  // namespace uw
+
+extern "C" {
+
+uw_status uw_gemm_noalloc(const uw_dmat* d, const uint16_t* x, float* y, int32_t m, int32_t variant, hipStream_t s) {
+  uw_status st = check_dmat(d);
+  if (st) return st;
+  if (m < 1 || m > UW_MAX_M) return fail(UW_E_SHAPE, "m=%d outside [1, %d]", m, UW_MAX_M);
+  size_t need = 0;
+  if ((st = uw_workspace_size(d, m, UW_PIPE_DIRECT_PALETTE, &need))) return st;
+  if (need - kErrBytes > kStaticScratchBytes)
+    return fail(UW_E_WORKSPACE, "%lldx%lld at m=%d needs %zu bytes of K-slice partial sums; the allocation-free entry "
+                "point holds %zu", (long long)d->info.n, (long long)d->info.k, m, need - kErrBytes, kStaticScratchBytes);
+  void* ws = nullptr;
+  if ((st = static_scratch(&ws))) return st;
+  return gemm_entry(d, x, y, nullptr, nullptr, nullptr, 0.f, m, UW_PIPE_DIRECT_PALETTE, variant, ws,
+                    kErrBytes + kStaticScratchBytes, s);
 }
 
 uw_status uw_gemm_bf16(const uint16_t* w, int64_t n, int64_t k, const uint16_t* x, float* y, int32_t m, int32_t variant,
