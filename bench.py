@@ -41,7 +41,7 @@ def log(*a):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("uw_device.hip", "uw_internal.h"):
+    for f in ("uw_gemm.hip", "uw_device.h", "uw_internal.h"):
         h.update(open(os.path.join(ROOT, "lossless_bf16_weight_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 

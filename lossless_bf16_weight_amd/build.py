@@ -38,19 +38,27 @@ def run(cmd):
     return out
 
 
-def build(verbose=False):
+# Device sources (each compiled on its own, in parallel) and the host codec.
+HIP_SOURCES = ("uw_gemm.hip", "uw_decode.hip", "uw_glue.hip", "uw_capi.hip")
+HOST_SOURCES = ("uw_host.cpp",)
+
+
+def build(verbose=False, jobs=None):
     os.makedirs(BUILD, exist_ok=True)
     hipcc = os.path.join(ROCM, "bin", "hipcc")
-    dev_o = os.path.join(BUILD, "uw_device.o")
-    host_o = os.path.join(BUILD, "uw_host.o")
-    jobs = [
-        [hipcc] + HIPCC_FLAGS + ["-I" + INCLUDE, "-I" + CSRC, "-c", os.path.join(CSRC, "uw_device.hip"), "-o", dev_o],
-        ["g++"] + CXX_FLAGS + ["-I" + INCLUDE, "-I" + CSRC, "-c", os.path.join(CSRC, "uw_host.cpp"), "-o", host_o],
-    ]
-    with ThreadPoolExecutor(2) as ex:
-        outs = list(ex.map(run, jobs))
+    objs, cmds = [], []
+    for src in HIP_SOURCES:
+        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+        objs.append(obj)
+        cmds.append([hipcc] + HIPCC_FLAGS + ["-I" + INCLUDE, "-I" + CSRC, "-c", os.path.join(CSRC, src), "-o", obj])
+    for src in HOST_SOURCES:
+        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+        objs.append(obj)
+        cmds.append(["g++"] + CXX_FLAGS + ["-I" + INCLUDE, "-I" + CSRC, "-c", os.path.join(CSRC, src), "-o", obj])
+    with ThreadPoolExecutor(jobs or min(len(cmds), os.cpu_count() or 1)) as ex:
+        outs = list(ex.map(run, cmds))
     tmp = LIB + ".tmp"
-    outs.append(run([hipcc, "-shared", "-fPIC", "--offload-arch=" + ARCH, dev_o, host_o, "-o", tmp, "-lpthread"]))
+    outs.append(run([hipcc, "-shared", "-fPIC", "--offload-arch=" + ARCH] + objs + ["-o", tmp, "-lpthread"]))
     os.replace(tmp, LIB)
     if verbose:
         for o in outs:
@@ -62,6 +70,7 @@ def build(verbose=False):
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("-v", "--verbose", action="store_true")
+    ap.add_argument("--jobs", type=int, default=None, help="parallel compiles (default: one per source)")
     args = ap.parse_args()
-    print(build(args.verbose))
+    print(build(args.verbose, args.jobs))
     sys.exit(0)

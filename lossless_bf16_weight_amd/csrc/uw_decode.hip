@@ -1,0 +1,450 @@
+// libuw Huffman decoder for MI355X (gfx950): chunk-parallel decode of the exponent stream into
+// 4-bit palette indices, exponent bytes or BF16 weights.
+//
+// Method: Cloudflare blog post "Unweight".
+//  - Huffman paragraph: the exponent alone is Huffman coded; per-chunk bit offsets let chunks
+//    decode in parallel.
+//  - SM-split paragraph: the decoder keeps its lookup table in on-chip memory (LDS here).
+//  - Four-pipeline paragraphs: decode to BF16 (pipeline 1), to exponent bytes (2), or to 4-bit
+//    indices (3, and the load-time transcode of the direct-palette format).
+#include "uw_device.h"
+
+namespace uw {
+
+// =========================================================================================
+// Huffman decoder.
+//
+// Chunks restart at every 64-column block of every tile, so the work splits into units of
+// whole blocks: one workgroup (one wave) per (tile, group of `nb` blocks), lane i decoding one
+// chunk of the unit (lane = block-in-unit * cpb + chunk-in-block).  A wave-level prefix sum
+// of the blocks' chunk counts places each chunk in the offset table.
+//   1. The unit's slice of the bitstream (contiguous: its chunks are consecutive) is staged
+//      in LDS with coalesced 16-byte loads, so the serial decode never waits on HBM.
+//   2. A 2^10-entry table (LDS) decodes up to four symbols per lookup: entry = four 4-bit
+//      symbols (bits 0-15), total length (16-19), first length (20-23), symbol count (29-31).
+//      A window whose first code is longer than 10 bits (rare: symbols below 2^-10
+//      frequency) has count 0 and points to a block of a secondary table indexed by the next
+//      3 bits.  The bit window is two stream words and a funnel-shift amount; the loop body
+//      is branch-free apart from the long-code case: the refill word is read every step and
+//      used or not, and every step issues a store (to its place when 8 indices are ready,
+//      else to an offset out of the buffer's range).  While four or more symbols remain,
+//      a lookup takes all the symbols of its entry; the last one to three take one a step.
+//   3. Every mode stores each finished 8-index word straight to global memory, in decode
+//      order (a lane's words are consecutive, so lines fill from one lane and the L2 does not
+//      write partial lines back): the index and exponent modes into the unit's own output
+//      range, the BF16 mode into the first 32 bytes a block of the tile's output rows (row q
+//      holds the words of each block's q-th coded row).  After a barrier the workgroup reloads
+//      its words into LDS (over the table scratch and the stage) and writes every output line
+//      once, whole: indices (verbatim and padding rows 0), exponents (verbatim rows raw), or
+//      BF16 weights merged with the sign+mantissa bytes.
+// =========================================================================================
+constexpr int kDecWin = 10;                 // lookup window, bits
+constexpr int kDecLut = 1 << kDecWin;       // primary entries
+constexpr int kDecSec = 16 * 8;             // secondary entries: 16 blocks of 8 (block 0: invalid)
+
+struct DecArgs {
+  const uint32_t* words;
+  const uint32_t* off;
+  const uint32_t* cbase;
+  const uint16_t* flags;
+  const uint32_t* vprefix;
+  const uint8_t* vexp;
+  const uint8_t* sm;
+  uint8_t* out;
+  uint32_t* err;
+  uint32_t words_cap;
+  int32_t n, k, kb;
+  int32_t spc, cpb, nb;    // coded segments per chunk, max chunks per block, blocks per unit
+  uint32_t stage_words;    // LDS words for one unit's bitstream slice (host bound)
+  uint32_t tab[4];         // palette, 16 bytes
+  uint8_t len[16];
+  uint16_t code[16];
+  uint32_t pbase;          // first 10-bit prefix of a code longer than 10 bits
+  uint32_t pmask;          // bit i: prefix pbase + i starts a long code (its block is i + 1)
+  uint32_t sec[kDecSec];   // secondary entries (same format as the primary ones)
+};
+
+
+struct DecLds {            // offsets (bytes) into the dynamic LDS block (the table is static)
+  uint32_t image, stage, blk, total;   // image: table-build scratch, then the reloaded words
+};
+constexpr uint32_t kDecTableBytes = (kDecLut + kDecSec) * 4u;
+
+// stage_words: a multiple of 256 (the bitstream slice is staged in 1 KB DMA steps).  The unit's
+// index words come back as 512 bytes a block (index and exponent modes: one run; BF16 mode: at
+// most 16 rows of 32 bytes a block, back to back), reloaded in 1 KB steps.
+__host__ __device__ inline DecLds dec_lds(int nb, uint32_t stage_words) {
+  DecLds L;
+  L.image = 0;
+  L.stage = kDecLut * 2u;
+  L.blk = L.stage + stage_words * 4;
+  L.blk = std::max<uint32_t>(L.blk, ((uint32_t)nb * 512u + 1023u) & ~1023u);
+  L.total = L.blk + 2u * 64u * 4u;   // block flags, verbatim ranks
+  return L;
+}
+
+__device__ __forceinline__ uint32_t nibbles_to_index_word(uint32_t v) {
+  // Sequential nibbles n0..n7 (n_i at bits 4i) -> index-stream word (even columns in the low
+  // half, odd columns in the high half: n_i at bit 4*(i/2) + 16*(i%2)).  Bytes 0 and 2 of px
+  // hold (n0 n2) and (n4 n6), those of py (n1 n3) and (n5 n7).
+  const uint32_t v4 = v >> 4;
+  const uint32_t px = bfi(0x0F0F0F0Fu, v, v4), py = bfi(0x0F0F0F0Fu, v4, v >> 8);
+  return perm(py, px, 0x06040200u);
+}
+
+__device__ __forceinline__ u32x2 index_word_to_exps(uint32_t iw, const uint32_t tab[4]) {
+  // 8 indices of one index-stream word -> 8 exponent bytes in column order.
+  const uint32_t e04 = lookup16(iw & 0x0F0F0F0Fu, tab);          // E0 E4 E1 E5
+  const uint32_t e26 = lookup16((iw >> 4) & 0x0F0F0F0Fu, tab);   // E2 E6 E3 E7
+  return u32x2{perm(e26, e04, 0x06040200u), perm(e26, e04, 0x07050301u)};
+}
+
+__device__ __forceinline__ uint32_t bf16_pairs_from(uint32_t s, uint32_t e, int half) {
+  // s, e: 4 sign+mantissa bytes and 4 exponent bytes; half 0 -> weights 0,1; 1 -> 2,3.
+  const uint32_t sp = perm(s, s, half ? 0x03030202u : 0x01010000u);
+  const uint32_t ep = perm(e, e, half ? 0x0C030C02u : 0x0C010C00u) << 7;
+  return (sp & 0x807F807Fu) | ep;
+}
+
+// Build the multi-symbol table.  tmp (kDecLut u16): first-symbol table, entry = symbol |
+// length << 4 | 0x100 for every window whose first code has length <= kDecWin.
+__device__ void build_dec_lut(const DecArgs& a, uint32_t* lut, uint16_t* tmp, int lane) {
+  for (int i = lane; i < kDecLut / 2; i += 64) reinterpret_cast<uint32_t*>(tmp)[i] = 0;
+  __syncthreads();
+  for (int s = 0; s < 16; ++s) {
+    const int L = a.len[s];
+    if (L == 0 || L > kDecWin) continue;
+    const uint32_t lo = (uint32_t)a.code[s] << (kDecWin - L), cnt = 1u << (kDecWin - L);
+    for (uint32_t i = lane; i < cnt; i += 64) tmp[lo + i] = (uint16_t)(s | (L << 4) | 0x100);
+  }
+  __syncthreads();
+#pragma unroll 4
+  for (int w = lane; w < kDecLut; w += 64) {
+    const uint32_t e0 = tmp[w];
+    uint32_t entry = 0;
+    if (e0 & 0x100u) {
+      const uint32_t l0 = (e0 >> 4) & 15u;
+      uint32_t used = l0, n = 1, syms = e0 & 15u;
+#pragma unroll
+      for (int j = 1; j < 4; ++j) {
+        const uint32_t ej = tmp[(w << used) & (kDecLut - 1)];
+        const uint32_t lj = (ej >> 4) & 15u;
+        const bool ok = (n == (uint32_t)j) && (ej & 0x100u) && used + lj <= (uint32_t)kDecWin;
+        syms |= ok ? (ej & 15u) << (4 * j) : 0u;
+        used += ok ? lj : 0u;
+        n += ok ? 1u : 0u;
+      }
+      entry = (n << 29) | (l0 << 20) | (used << 16) | syms;
+    } else {
+      const uint32_t i = (uint32_t)w - a.pbase;                // long code: secondary block i + 1
+      entry = (i < 15u && ((a.pmask >> i) & 1u)) ? i + 1u : 0u;
+    }
+    lut[w] = entry;
+  }
+  for (int i = lane; i < kDecSec; i += 64) lut[kDecLut + i] = a.sec[i];
+  __syncthreads();
+}
+
+template <int MODE>
+__global__ __launch_bounds__(64) void k_decode(DecArgs a) {
+  extern __shared__ __align__(16) uint8_t dsh[];
+  constexpr bool kDirect = MODE != DEC_BF16;
+  __shared__ uint32_t lut[kDecLut + kDecSec];
+  const DecLds Ls = dec_lds(a.nb, a.stage_words);
+  uint32_t* img = reinterpret_cast<uint32_t*>(dsh + Ls.image);
+  uint32_t* stage = reinterpret_cast<uint32_t*>(dsh + Ls.stage);
+  uint32_t* blk_f = reinterpret_cast<uint32_t*>(dsh + Ls.blk);       // flags per block of the unit
+  uint32_t* blk_v = blk_f + 64;                                       // verbatim rank of the block's first
+  const int lane = threadIdx.x;
+  const int t = blockIdx.y;
+  const int bA = blockIdx.x * a.nb;
+  const int nbu = min(a.nb, a.kb - bA);
+  const int rows = min(16, a.n - 16 * t);
+  const uint32_t realmask = rows == 16 ? 0xFFFFu : ((1u << rows) - 1u);
+  const uint16_t* flg = a.flags + (size_t)t * a.kb;
+
+  // Chunks and verbatim segments of the tile's blocks before this unit.
+  uint32_t ch_before = 0, v_before = 0;
+  for (int b0 = 0; b0 < bA; b0 += 64) {
+    const int b = b0 + lane;
+    uint32_t nch = 0, nv = 0;
+    if (b < bA) {
+      const uint32_t f = flg[b];
+      nch = ((uint32_t)__popc(realmask & ~f) + a.spc - 1) / a.spc;
+      nv = __popc(f);
+    }
+    ch_before += wave_sum(nch);
+    v_before += wave_sum(nv);
+  }
+  // This unit's blocks: flags, chunk counts, exclusive prefixes (lane = block in unit).
+  uint32_t f = 0, nch = 0, nv = 0;
+  if (lane < nbu) {
+    f = flg[bA + lane];
+    nch = ((uint32_t)__popc(realmask & ~f) + a.spc - 1) / a.spc;
+    nv = __popc(f);
+  }
+  const uint32_t ch_incl = wave_incl_scan(nch, lane), v_incl = wave_incl_scan(nv, lane);
+  const uint32_t unit_chunks = __shfl(ch_incl, 63, 64);
+  if (lane < nbu) {
+    blk_f[lane] = f;
+    blk_v[lane] = a.vprefix[t] + v_before + v_incl - nv;
+  }
+  const uint32_t c_first = a.cbase[t] + ch_before;
+  const uint32_t ch_pre = ch_incl - nch;                       // per block lane
+
+  // Stage the unit's bitstream slice in 1 KB LDS-DMA steps (no VGPRs, no waits until the
+  // barrier; words past the stream read as zero), and build the table meanwhile.
+  uint32_t wb = 0, nst = 0;
+  if (unit_chunks) {
+    wb = (a.off[c_first] >> 5) & ~3u;
+    const uint32_t we = (a.off[c_first + unit_chunks] >> 5) + 3u;
+    nst = min((we - wb + 255u) & ~255u, a.stage_words);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.words, a.words_cap * 4u);
+    for (uint32_t i = 0; i < nst; i += 256u)
+      lds_dma16(rs, reinterpret_cast<uint8_t*>(stage + i), (wb + i) * 4u + (uint32_t)lane * 16u);
+  }
+  build_dec_lut(a, lut, reinterpret_cast<uint16_t*>(img), lane);
+  __syncthreads();
+  // Index and exponent modes: results go straight to the unit's output range (a lane without
+  // a finished word stores out of range, which writes nothing).
+  constexpr uint32_t kOutBlk = MODE == DEC_IDX ? 512u : 1024u;   // output bytes per block (direct modes)
+  const uint32_t rowb = (uint32_t)a.k * 2u;                       // BF16 output row, bytes
+  uint8_t* const obase = kDirect ? a.out + ((size_t)t * a.kb + bA) * kOutBlk
+                                 : a.out + ((size_t)t * 16 * a.k + (size_t)bA * 64) * 2;
+  const __amdgpu_buffer_rsrc_t ors =
+      make_rsrc(obase, kDirect ? (uint32_t)nbu * kOutBlk : (uint32_t)(rows - 1) * rowb + (uint32_t)nbu * 128u);
+
+  // Decode: lane -> (block in unit, chunk in block).
+  const int bl = lane / a.cpb, j = lane % a.cpb;
+  const uint32_t bf = __shfl(f, bl < 64 ? bl : 0, 64);
+  const uint32_t bpre = __shfl(ch_pre, bl < 64 ? bl : 0, 64);
+  uint32_t cm = realmask & ~bf;                                 // coded rows of the block
+  const int ncoded = __popc(cm);
+  uint32_t bad = 0;
+  if (bl < nbu && j * a.spc < ncoded) {
+    const int nrows = min(a.spc, ncoded - j * a.spc);
+    int32_t rem4 = nrows * 256;                                 // 4 x symbols left
+    const uint32_t c = c_first + bpre + (uint32_t)j;
+    const uint32_t p0 = a.off[c] - wb * 32u, p1 = a.off[c + 1] - wb * 32u;
+    auto word = [&](uint32_t i) -> uint32_t { return i < nst ? stage[i] : 0u; };
+    // Bit window: the 32 bits starting (32 - s) bits into w0 (s = 0: w1 itself).
+    const uint32_t b0 = p0 & 31u, wi0 = p0 >> 5;
+    uint32_t w0 = b0 ? word(wi0) : 0u, w1 = word(b0 ? wi0 + 1 : wi0);
+    const uint32_t* nxp = stage + (b0 ? wi0 + 2 : wi0 + 1);     // next stream word
+    const uint32_t* const lastp = stage + (nst ? nst - 1 : 0);
+    uint32_t s = b0 ? 32u - b0 : 0u;
+    // Output, in decode order: the q-th coded row of block bl holds its 8 index words at
+    // bl * 512 + q * 32 (the chunk's rows are consecutive coded rows), so a lane fills its
+    // own run of bytes; BF16 mode: at q * rowb + bl * 32 (woff counts q * 32 + word * 4).
+    uint32_t woff = (kDirect ? (uint32_t)bl * 512u : 0u) + (uint32_t)(j * a.spc) * 32u;
+    const uint32_t lb32 = (uint32_t)bl * 32u;
+    uint64_t acc = 0;
+    uint32_t a4 = 0;                                            // 4 x indices pending in acc
+    // One lookup's worth: append `syms` (n4 / 4 indices), consume L bits, emit a finished word.
+    auto step = [&](uint32_t syms, uint32_t n4, uint32_t L, uint32_t v) {
+      acc |= (uint64_t)syms << a4;
+      a4 += n4;
+      rem4 -= (int32_t)n4;
+      const int32_t sl = (int32_t)s - (int32_t)L;
+      const bool neg = sl < 0;
+      w0 = neg ? w1 : w0;
+      w1 = neg ? v : w1;
+      nxp += (uint32_t)sl >> 31;
+      s = (uint32_t)sl & 31u;
+      // a4 < 64, so bit 5 is the flush flag; it drives the store offset (out of range when
+      // clear), the accumulator shift and the offset step without a branch.
+      const uint32_t f32 = a4 & 32u;
+      const uint32_t iw = nibbles_to_index_word((uint32_t)acc);
+      const uint32_t po = kDirect ? woff : (woff >> 5) * rowb + lb32 + (woff & 31u);
+      __builtin_amdgcn_raw_buffer_store_b32(iw, ors, po | ((f32 ^ 32u) << 26), 0, 0);
+      acc >>= f32;
+      a4 &= 31u;
+      woff += f32 >> 3;
+    };
+    // Long or invalid first code: the secondary entry, or a one-bit placeholder when invalid.
+    // (Block 0 of the secondary table is all invalid: it serves invalid primary entries.)
+    auto resolve = [&](uint32_t e, uint32_t win) -> uint32_t {
+      if (e < (1u << 29)) {
+        const uint32_t e2 = lut[kDecLut + (e & 15u) * 8u + ((win >> 19) & 7u)];
+        const bool inv = e2 < (1u << 29);
+        bad |= inv ? 1u : 0u;
+        e = inv ? (1u << 29) | (1u << 20) | (1u << 16) : e2;
+      }
+      return e;
+    };
+    while (rem4 >= 16) {
+      const uint32_t win = __builtin_amdgcn_alignbit(w0, w1, s);
+      uint32_t e = lut[win >> (32 - kDecWin)];
+      const uint32_t v = *(nxp < lastp ? nxp : lastp);           // refill candidate
+      e = resolve(e, win);
+      step(e & 0xFFFFu, e >> 27, (e >> 16) & 15u, v);
+    }
+    while (rem4 > 0) {
+      const uint32_t win = __builtin_amdgcn_alignbit(w0, w1, s);
+      uint32_t e = lut[win >> (32 - kDecWin)];
+      const uint32_t v = *(nxp < lastp ? nxp : lastp);
+      e = resolve(e, win);
+      step(e & 15u, 4u, (e >> 20) & 15u, v);
+    }
+    const uint32_t pos = (uint32_t)(nxp - stage) * 32u - 32u - s;   // bits consumed from the slice start
+    if (pos != p1) bad = 1;
+  }
+  if (bad) atomicOr(a.err, 1u);
+
+  // Write the unit's output in its final layout.  Row r of block b is coded unless flagged
+  // verbatim; a coded row's words sit at its rank among the block's coded rows.  The words
+  // went out in decode order (this workgroup's stores are complete at the barrier); they come
+  // back through the (now free) table scratch and stage in 1 KB LDS-DMA steps, bypassing the
+  // vector cache, and every line of the unit's output is written once.
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  __syncthreads();
+  uint8_t* const back = reinterpret_cast<uint8_t*>(img);
+  if constexpr (kDirect) {
+    for (uint32_t i = 0; i < (uint32_t)nbu * 512u; i += 1024u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ors, (lds_ptr_t)(back + i), 16, i + (uint32_t)lane * 16u, 0, 0, 1);
+  } else {
+    // Row q's run of nbu * 32 bytes lands at back + q * run: a 1 KB step covers several rows.
+    const uint32_t run = (uint32_t)nbu * 32u, total = (uint32_t)rows * run;
+    for (uint32_t i = 0; i < total; i += 1024u) {
+      const uint32_t o = i + (uint32_t)lane * 16u, q = o / run;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ors, (lds_ptr_t)(back + i), 16, o < total ? q * rowb + (o - q * run) : kOob,
+                                               0, 0, 1);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  __syncthreads();
+  if constexpr (MODE == DEC_IDX) {
+    // 16-byte piece p: block p / 32, sub-tile (p / 8) % 4, rows 2 (p % 8) and 2 (p % 8) + 1.
+    u32x4* dst = reinterpret_cast<u32x4*>(obase);
+    for (int p = lane; p < nbu * 32; p += 64) {
+      const int b = p >> 5, g = (p >> 3) & 3, r = (p & 7) * 2;
+      const uint32_t coded = realmask & ~blk_f[b];
+      const uint32_t q = __popc(coded & ((1u << r) - 1u));
+      const u32x2* src = reinterpret_cast<const u32x2*>(back + b * 512 + g * 8);
+      const u32x2 z{0, 0};
+      const u32x2 w0 = ((coded >> r) & 1u) ? src[q * 4] : z;
+      const u32x2 w1 = ((coded >> (r + 1)) & 1u) ? src[(q + ((coded >> r) & 1u)) * 4] : z;
+      dst[p] = u32x4{w0.x, w0.y, w1.x, w1.y};
+    }
+  } else if constexpr (MODE == DEC_EXP) {
+    // 16-byte piece p: block p / 64, sub-tile (p / 16) % 4, row p % 16.  Verbatim rows take
+    // their raw exponents, padding rows zeros.
+    u32x4* dst = reinterpret_cast<u32x4*>(obase);
+    for (int p = lane; p < nbu * 64; p += 64) {
+      const int b = p >> 6, g = (p >> 4) & 3, r = p & 15;
+      const uint32_t fb = blk_f[b];
+      u32x4 o{0, 0, 0, 0};
+      if ((fb >> r) & 1u) {
+        const uint32_t v = blk_v[b] + __popc(fb & ((1u << r) - 1u));
+        o = *reinterpret_cast<const u32x4*>(a.vexp + (size_t)v * 64 + g * 16);
+      } else if (r < rows) {
+        const uint32_t q = (uint32_t)r - __popc(fb & ((1u << r) - 1u));
+        const u32x2 iw = *reinterpret_cast<const u32x2*>(back + b * 512 + q * 32 + g * 8);
+        const u32x2 e0 = index_word_to_exps(iw.x, a.tab), e1 = index_word_to_exps(iw.y, a.tab);
+        o = u32x4{e0.x, e0.y, e1.x, e1.y};
+      }
+      dst[p] = o;
+    }
+  } else {
+    // BF16 rows: 16-byte piece p = 8 weights; row p / (nbu*8), then block, sub-tile, half.
+    // Four pieces a lane at a time: their loads all go out before the first store.
+    const uint32_t rs = (uint32_t)nbu * 32u;
+    const int per_row = nbu * 8, total = rows * per_row;
+    constexpr int kPieces = 4;
+    for (int p0 = lane; p0 < total; p0 += 64 * kPieces) {
+      u32x2 sv[kPieces], e[kPieces];
+      size_t dsto[kPieces];
+#pragma unroll
+      for (int u = 0; u < kPieces; ++u) {
+        const int p = min(p0 + 64 * u, total - 1);
+        const int r = p / per_row, q = p - r * per_row;
+        const int b = q >> 3, g = (q >> 1) & 3, h = q & 1;
+        const uint32_t fb = blk_f[b];
+        const uint32_t vb = __popc(fb & ((1u << r) - 1u));
+        if ((fb >> r) & 1u) {
+          e[u] = *reinterpret_cast<const u32x2*>(a.vexp + (size_t)(blk_v[b] + vb) * 64 + g * 16 + h * 8);
+        } else {
+          e[u] = index_word_to_exps(*reinterpret_cast<const uint32_t*>(back + ((uint32_t)r - vb) * rs + b * 32 + (g * 2 + h) * 4),
+                                    a.tab);
+        }
+        const size_t sub = ((size_t)t * a.kb * 4 + (size_t)(bA + b) * 4 + g) * 16 + r;
+        sv[u] = *reinterpret_cast<const u32x2*>(a.sm + sub * 16 + h * 8);
+        dsto[u] = ((size_t)r * a.k + (size_t)b * 64 + g * 16 + h * 8) * 2;
+      }
+#pragma unroll
+      for (int u = 0; u < kPieces; ++u) {
+        if (p0 + 64 * u >= total) break;
+        u32x4 o;
+        o.x = bf16_pairs_from(sv[u].x, e[u].x, 0);
+        o.y = bf16_pairs_from(sv[u].x, e[u].x, 1);
+        o.z = bf16_pairs_from(sv[u].y, e[u].y, 0);
+        o.w = bf16_pairs_from(sv[u].y, e[u].y, 1);
+        *reinterpret_cast<u32x4*>(obase + dsto[u]) = o;
+      }
+    }
+  }
+}
+
+uw_status run_decode(const uw_dmat* d, int mode, uint8_t* out, void* ws, size_t ws_bytes, hipStream_t s) {
+  uw_status st = check_dmat(d);
+  if (st) return st;
+  if (!out) return fail(UW_E_ARG, "null output");
+  if (!ws || ws_bytes < (size_t)kErrBytes) return fail(UW_E_WORKSPACE, "decode needs a %d-byte workspace", kErrBytes);
+  DecArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.words = d->words;
+  a.off = d->off;
+  a.cbase = d->cbase;
+  a.flags = d->flags;
+  a.vprefix = d->vprefix;
+  a.vexp = d->vexp;
+  a.sm = d->sm;
+  a.out = out;
+  a.err = reinterpret_cast<uint32_t*>(ws);
+  a.words_cap = d->words_cap;
+  a.n = (int32_t)d->info.n;
+  a.k = (int32_t)d->info.k;
+  a.kb = (int32_t)d->info.kb;
+  a.spc = d->dec_spc;
+  a.cpb = d->dec_cpb;
+  a.nb = d->dec_nb;
+  a.stage_words = d->dec_stage_words;
+  std::memcpy(a.tab, d->info.palette, 16);
+  std::memcpy(a.len, d->info.code_len, 16);
+  std::memcpy(a.code, d->info.code, 32);
+  // Codes longer than the lookup window: their 10-bit prefixes (consecutive in a canonical
+  // code) each get a block of 8 secondary entries indexed by the next 3 bits.
+  for (int i = 0; i < kDecSec; ++i) a.sec[i] = 0;               // count 0: invalid
+  a.pbase = kDecLut;
+  for (int sym = 0; sym < 16; ++sym) {
+    const int L = d->info.code_len[sym];
+    if (L > kDecWin) a.pbase = std::min<uint32_t>(a.pbase, (uint32_t)d->info.code[sym] >> (L - kDecWin));
+  }
+  for (int sym = 0; sym < 16; ++sym) {
+    const int L = d->info.code_len[sym];
+    if (L <= kDecWin) continue;
+    const uint32_t code = d->info.code[sym], pre = code >> (L - kDecWin), blk = pre - a.pbase;
+    if (blk >= 15) return fail(UW_E_FORMAT, "long codes span too many prefixes");
+    a.pmask |= 1u << blk;
+    const uint32_t low = (code << (13 - L)) & 7u, cnt = 1u << (13 - L);
+    for (uint32_t q = 0; q < cnt; ++q) a.sec[(blk + 1) * 8 + low + q] = (1u << 29) | ((uint32_t)L << 20) | ((uint32_t)L << 16) | (uint32_t)sym;
+  }
+  const DecLds L = dec_lds(a.nb, a.stage_words);
+  int dev = 0, lds_max = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+    return fail(UW_E_HIP, "cannot query the LDS size");
+  if (L.total + kDecTableBytes > (uint32_t)lds_max)
+    return fail(UW_E_SHAPE, "decoder unit needs %u bytes of LDS (device allows %d)", L.total + kDecTableBytes, lds_max);
+  const dim3 grid((unsigned)((d->info.kb + a.nb - 1) / a.nb), (unsigned)d->info.tiles);
+  switch (mode) {
+    case DEC_IDX: hipLaunchKernelGGL(k_decode<DEC_IDX>, grid, dim3(64), L.total, s, a); break;
+    case DEC_EXP: hipLaunchKernelGGL(k_decode<DEC_EXP>, grid, dim3(64), L.total, s, a); break;
+    default: hipLaunchKernelGGL(k_decode<DEC_BF16>, grid, dim3(64), L.total, s, a); break;
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(UW_E_HIP, "decode launch: %s", hipGetErrorString(e));
+  return UW_OK;
+}
+
+}  // namespace uw
