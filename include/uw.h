@@ -328,6 +328,14 @@ uw_status uw_sched_step(uw_sched* s, const uint16_t* x, uint16_t** out);
  * trace + l * m * (6 * inter + 6 * hidden).  trace: device, at least layers times that many
  * bytes (UW_E_WORKSPACE otherwise), borrowed until replaced; NULL stops the recording. */
 uw_status uw_sched_trace(uw_sched* s, void* trace, size_t bytes);
+/* Decode/GEMM split of the chip (SM-split paragraph of the post: the decoder and the matmul run
+ * on separate parts of the GPU, and the split is tuned).  decode_workgroups > 0: each hard-layer
+ * decode runs on at most that many decoder workgroups, which take the matrix's decode units in
+ * turn (the table is built once per workgroup); a workgroup of the decoder fills the LDS of a
+ * compute unit, so this is the number of compute units the decodes occupy while the main
+ * stream's GEMMs run on the others.  0 (the default): the whole chip.  Results do not depend on
+ * it.  Errors: UW_E_ARG. */
+uw_status uw_sched_split(uw_sched* s, int32_t decode_workgroups);
 /* Releases the events and host state (waits for nothing: the caller synchronises first). */
 uw_status uw_sched_release(uw_sched* s);
 

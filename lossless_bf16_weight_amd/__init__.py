@@ -33,7 +33,7 @@ EXPORTS = ("uw_last_error", "uw_version", "uw_build_palette", "uw_encode_bound",
            "uw_variant_count", "uw_variant_name", "uw_check", "uw_autotune_load", "uw_autotune_set",
            "uw_autotune_get", "uw_autotune_set_variant", "uw_autotune_get_variant", "uw_autotune_clear", "uw_swiglu",
            "uw_gemm_swiglu", "uw_gemm_rmsnorm", "uw_rmsnorm", "uw_sched_size", "uw_sched_init", "uw_sched_step",
-           "uw_sched_trace", "uw_sched_release")
+           "uw_sched_trace", "uw_sched_split", "uw_sched_release")
 
 
 class UwError(RuntimeError):
@@ -112,6 +112,7 @@ def lib():
                                  _P, _P]),
         "uw_sched_step": (_I32, [_P, _P, ctypes.POINTER(ctypes.c_void_p)]),
         "uw_sched_trace": (_I32, [_P, _P, _S]),
+        "uw_sched_split": (_I32, [_P, _I32]),
         "uw_sched_release": (_I32, [_P]),
     }
     for name, (res, args) in sig.items():
@@ -415,6 +416,10 @@ class Sched:
         device tensor of layers * m * (6 * inter + 6 * hidden) bytes), or stop with None."""
         self.trace_buf = buf
         _check(lib().uw_sched_trace(self.buf, _dev(buf, "trace", 0, optional=True), _nbytes(buf)))
+
+    def split(self, decode_workgroups):
+        """At most `decode_workgroups` decoder workgroups for hard-layer decodes (0: whole chip)."""
+        _check(lib().uw_sched_split(self.buf, int(decode_workgroups)))
 
     def release(self):
         if self.live:

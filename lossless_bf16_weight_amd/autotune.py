@@ -192,6 +192,137 @@ class Tuner:
         return table
 
 
+class StepTuner:
+    """End-to-end choice of pipeline and kernel variant per projection of an MLP stack, by
+    coordinate descent on the measured time of whole decode steps (autotuning paragraphs of the
+    Unweight post: the choices are made by end-to-end throughput, per projection and batch size,
+    and written to a per-model configuration file).
+
+    Starting from a configuration (default: every projection on the direct-palette pipeline with
+    the library's variant choice), each sweep takes gate, then up, then down: with the other two
+    fixed, every candidate (pipeline, variant) of that projection is timed on the full step and the
+    fastest kept.  Sweeps repeat until one changes nothing (or max_sweeps).  Timing: `steps`
+    back-to-back steps per measurement after a warm-up, the median of `rounds` measurements.
+    The step's weights are the stack's own resident matrices (a model's working set: gate, up and
+    down of every layer, not cache-resident between steps at the MLP sizes).
+
+    A stack with hard (bundle-only) layers adds one more coordinate, the decode/GEMM split of the
+    chip (uw_sched_split): `tune_split` sweeps the decoder workgroup count on a HardEasyStack."""
+
+    def __init__(self, stack, x, pipelines=PIPELINES, variants=None, steps=8, rounds=3):
+        self.stack, self.x = stack, x
+        self.pipelines = tuple(pipelines)
+        self.variants = list(range(uw_variant_count())) if variants is None else list(variants)
+        self.steps, self.rounds = steps, rounds
+        self.evals = []                              # (config, us) of every measurement
+
+    def candidates(self):
+        return [(p, v) for p in self.pipelines for v in self.variants]
+
+    def time_config(self, cfg):
+        import torch
+        st, x = self.stack, self.x
+        for _ in range(2):
+            st.step(x, config=cfg, check=False)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        per = []
+        for _ in range(self.rounds):
+            e0.record()
+            for _ in range(self.steps):
+                st.step(x, config=cfg, check=False)
+            e1.record()
+            e1.synchronize()
+            per.append(1e3 * e0.elapsed_time(e1) / self.steps)
+        us = float(np.median(per))
+        self.evals.append((dict(cfg), us))
+        return us
+
+    def tune(self, start=None, max_sweeps=4, log=None):
+        """Returns {"config": {proj: (pipeline, variant)}, "us": tuned us per step,
+        "default_us": the starting configuration's, "sweeps": sweeps run}."""
+        from .stack import PROJECTIONS
+        cfg = dict(start) if start else {k: (UW_PIPE_DIRECT_PALETTE, -1) for k in PROJECTIONS}
+        best = self.time_config(cfg)
+        default_us = best
+        sweeps = 0
+        for sweeps in range(1, max_sweeps + 1):
+            changed = False
+            for proj in PROJECTIONS:
+                for cand in self.candidates():
+                    if cand == tuple(cfg[proj]):
+                        continue
+                    trial = dict(cfg)
+                    trial[proj] = cand
+                    us = self.time_config(trial)
+                    if us < best:
+                        best, cfg, changed = us, trial, True
+                if log:
+                    log("sweep %d %s: %s variant %d, %.1f us a step" % (sweeps, proj, PIPELINE_NAMES[cfg[proj][0]],
+                                                                      cfg[proj][1], best))
+            if not changed:
+                break
+        return {"config": {k: tuple(v) for k, v in cfg.items()}, "us": best, "default_us": default_us,
+                "sweeps": sweeps}
+
+    @staticmethod
+    def tune_split(make_stack, x, splits, steps=8, rounds=3, log=None):
+        """The decode/GEMM split coordinate of a stack with hard layers: make_stack(split) builds a
+        HardEasyStack with that many decoder workgroups (0: the whole chip); returns
+        {"decode_workgroups": best, "us": its us per step, "all": {split: us}}."""
+        import torch
+        res = {}
+        for sp in splits:
+            st = make_stack(sp)
+            try:
+                for _ in range(2):
+                    st.step(x, check=False)
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                per = []
+                for _ in range(rounds):
+                    e0.record()
+                    for _ in range(steps):
+                        st.step(x, check=False)
+                    e1.record()
+                    e1.synchronize()
+                    per.append(1e3 * e0.elapsed_time(e1) / steps)
+                res[sp] = float(np.median(per))
+                if log:
+                    log("split %d decoder workgroups: %.1f us a step" % (sp, res[sp]))
+            finally:
+                st.close()
+        best = min(res, key=res.get)
+        return {"decode_workgroups": best, "us": res[best], "all": res}
+
+
+def save_model_config(path, model, m, result, split=None):
+    """Per-model configuration file (JSON): per projection the pipeline and variant, the
+    decode/GEMM split, and the measured step times."""
+    import json
+    from . import uw_variant_name
+    out = {"model": model, "m": m,
+           "projections": {k: {"pipeline": PIPELINE_NAMES[p], "pipeline_id": p, "variant": v,
+                               "variant_name": uw_variant_name(v) if v >= 0 else "library default"}
+                           for k, (p, v) in result["config"].items()},
+           "us_per_step": round(result["us"], 2), "default_us_per_step": round(result["default_us"], 2),
+           "sweeps": result["sweeps"]}
+    if split is not None:
+        out["decode_workgroups"] = split["decode_workgroups"]
+        out["split_us_per_step"] = {str(k): round(v, 2) for k, v in split["all"].items()}
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    return out
+
+
+def load_model_config(path):
+    """{proj: (pipeline, variant)} and the decode/GEMM split of a per-model configuration file."""
+    import json
+    d = json.load(open(path))
+    cfg = {k: (int(v["pipeline_id"]), int(v["variant"])) for k, v in d["projections"].items()}
+    return cfg, int(d.get("decode_workgroups", 0))
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description="Autotune pipelines and kernel variants for one or more weight shapes "
                                              "(synthetic N(0, std^2) BF16 weights of each shape) into one table "

@@ -362,6 +362,7 @@ struct SchedImpl {
   hipStream_t main = nullptr, side = nullptr;
   hipEvent_t dec_done[2] = {nullptr, nullptr}, use_done[2] = {nullptr, nullptr};
   uint8_t* trace = nullptr;  // per-layer copies of g, h, y and the layer output (uw_sched_trace)
+  int decode_wgs = 0;        // decoder workgroups of a hard layer's decodes (0: the whole chip)
 };
 // Bytes of one layer's record in a trace: g (fp32), h (BF16), y (fp32), layer output (BF16).
 static size_t sched_trace_layer_bytes(const SchedImpl* S) {
@@ -392,7 +393,7 @@ static uw_status sched_issue_decode(SchedImpl* S, int i) {
   for (int j = 0; j < 3; ++j) {
     if (!S->hard[3 * l + j]) continue;
     const uw_dmat* d = &S->views[3 * l + j];
-    const uw_status st = run_decode(d, DEC_IDX, d->idx, S->dws, S->dws_bytes, S->side);
+    const uw_status st = run_decode(d, DEC_IDX, d->idx, S->dws, S->dws_bytes, S->side, S->decode_wgs);
     if (st) return st;
   }
   if (hipEventRecord(S->dec_done[set], S->side) != hipSuccess) return fail(UW_E_HIP, "event record failed");
@@ -540,6 +541,14 @@ uw_status uw_sched_trace(uw_sched* s, void* trace, size_t bytes) {
   const size_t need = (size_t)S->layers * uw::sched_trace_layer_bytes(S);
   if (trace && bytes < need) return fail(UW_E_WORKSPACE, "trace needs %zu bytes, got %zu", need, bytes);
   S->trace = reinterpret_cast<uint8_t*>(trace);
+  clear_error();
+  return UW_OK;
+}
+
+uw_status uw_sched_split(uw_sched* s, int32_t decode_workgroups) {
+  if (!s || s->magic != uw::kSchedMagic || !s->impl) return fail(UW_E_ARG, "scheduler is not initialised");
+  if (decode_workgroups < 0) return fail(UW_E_ARG, "decode_workgroups %d < 0", decode_workgroups);
+  s->impl->decode_wgs = decode_workgroups;
   clear_error();
   return UW_OK;
 }

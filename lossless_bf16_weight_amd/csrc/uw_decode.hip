@@ -511,14 +511,13 @@ __device__ __forceinline__ u32x2 seq_word_to_exps(uint32_t v, const uint32_t tab
   return u32x2{perm(od, ev, 0x05010400u), perm(od, ev, 0x07030602u)};
 }
 
+// One unit (wave `wave` of the workgroup, unit u).  first: the workgroup's first unit, whose
+// stage DMA overlaps the table build (every wave of the workgroup takes part in the build, unit
+// or not); later units wait for their own stage only.
 template <int MODE>
-__global__ __launch_bounds__(512) void k_decode_rows(RowDecArgs a) {
-  __shared__ uint32_t lut[kRowLut + kRowSec];
-  extern __shared__ __align__(16) uint8_t dsh[];
+__device__ __forceinline__ void decode_unit(const RowDecArgs& a, uint32_t* lut, uint8_t* dsh, int u, int wave,
+                                            bool first) {
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int W = blockDim.x >> 6;
-  const int u = (int)blockIdx.x * W + wave;
   const bool unit_ok = u < a.units;
   const int t = unit_ok ? u / a.units_per_tile : 0;
   const int bA = unit_ok ? (u - t * a.units_per_tile) * a.nb : 0;
@@ -582,7 +581,10 @@ __global__ __launch_bounds__(512) void k_decode_rows(RowDecArgs a) {
   for (int o = 32; o > 0; o >>= 1) wmax_rows = max(wmax_rows, __shfl_xor(wmax_rows, o, 64));
   wmax_rows = __builtin_amdgcn_readfirstlane(wmax_rows);
 
-  build_row_lut(a, lut, reinterpret_cast<uint16_t*>(dsh));     // its last barrier also waits for the stage
+  if (first)
+    build_row_lut(a, lut, reinterpret_cast<uint16_t*>(dsh));   // its last barrier also waits for the stage
+  else
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));                  // this wave's stage DMA (and earlier stores)
   if (!unit_ok) return;
 
   // Bit window: the 32 bits starting (32 - s) bits into w0 (s = 0: w1 itself); nxp: next word.
@@ -774,6 +776,19 @@ __global__ __launch_bounds__(512) void k_decode_rows(RowDecArgs a) {
   }
 }
 
+// The decoder grid: gridDim.x workgroups of W waves; a grid smaller than the units (a decode
+// sharing the chip with other work) takes its units in turn, the table built once.
+template <int MODE>
+__global__ __launch_bounds__(512) void k_decode_rows(RowDecArgs a) {
+  __shared__ uint32_t lut[kRowLut + kRowSec];
+  extern __shared__ __align__(16) uint8_t dsh[];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int W = blockDim.x >> 6;
+  decode_unit<MODE>(a, lut, dsh, (int)blockIdx.x * W + wave, wave, true);
+  for (int g = (int)(blockIdx.x + gridDim.x); g * W < a.units; g += (int)gridDim.x)
+    decode_unit<MODE>(a, lut, dsh, g * W + wave, wave, false);
+}
+
 // Waves a workgroup of k_decode_rows: the fewest rounds of workgroups over the chip, then the
 // most compute units busy (the table is built once per workgroup).
 static int row_waves(uint32_t stage_words, int64_t units, int lds_wg_max, int lds_cu, int cus) {
@@ -795,7 +810,7 @@ static int row_waves(uint32_t stage_words, int64_t units, int lds_wg_max, int ld
   return best_w;
 }
 
-static uw_status run_decode_rows(const uw_dmat* d, int mode, uint8_t* out, uint32_t* err, hipStream_t s) {
+static uw_status run_decode_rows(const uw_dmat* d, int mode, uint8_t* out, uint32_t* err, int max_wgs, hipStream_t s) {
   RowDecArgs a;
   std::memset(&a, 0, sizeof(a));
   a.words = d->words;
@@ -865,7 +880,9 @@ static uw_status run_decode_rows(const uw_dmat* d, int mode, uint8_t* out, uint3
   if (W == 0) return fail(UW_E_SHAPE, "decoder unit needs more LDS than the device allows");
   a.stage_off = row_buf_area(W);
   const size_t lds = (size_t)a.stage_off + (size_t)W * a.stage_words * 4;
-  const dim3 grid((unsigned)((units + W - 1) / W));
+  int64_t wgs = (units + W - 1) / W;
+  if (max_wgs > 0) wgs = std::min<int64_t>(wgs, max_wgs);
+  const dim3 grid((unsigned)wgs);
   switch (mode) {
     case DEC_IDX: hipLaunchKernelGGL(k_decode_rows<DEC_IDX>, grid, dim3(64 * W), lds, s, a); break;
     case DEC_EXP: hipLaunchKernelGGL(k_decode_rows<DEC_EXP>, grid, dim3(64 * W), lds, s, a); break;
@@ -876,7 +893,7 @@ static uw_status run_decode_rows(const uw_dmat* d, int mode, uint8_t* out, uint3
   return UW_OK;
 }
 
-uw_status run_decode(const uw_dmat* d, int mode, uint8_t* out, void* ws, size_t ws_bytes, hipStream_t s) {
+uw_status run_decode(const uw_dmat* d, int mode, uint8_t* out, void* ws, size_t ws_bytes, hipStream_t s, int max_wgs) {
   uw_status st = check_dmat(d);
   if (st) return st;
   if (!out) return fail(UW_E_ARG, "null output");
@@ -887,7 +904,7 @@ uw_status run_decode(const uw_dmat* d, int mode, uint8_t* out, void* ws, size_t 
     // the general decoder below).  Full BF16 output stays with the general decoder (measured
     // faster: 106 against 122 us on gate_proj 14336 x 4096, where its two-phase write costs
     // less than the register image's BF16 write-out).
-    const uw_status rs = run_decode_rows(d, mode, out, reinterpret_cast<uint32_t*>(ws), s);
+    const uw_status rs = run_decode_rows(d, mode, out, reinterpret_cast<uint32_t*>(ws), max_wgs, s);
     if (rs != UW_E_SHAPE) return rs;
   }
   DecArgs a;

@@ -259,7 +259,11 @@ uw_status run_gemm(int src, const GemmArgs& a, int64_t tiles, int variant, float
 int plan_gemm(int src, const GemmArgs& a, int64_t tiles, int* variant, const float* part, size_t part_bytes);
 int64_t mt_max_slices(int64_t kb, int64_t tiles, int m);
 // uw_decode.hip: Huffman decode of a bound matrix into `out` (mode DEC_*), error word in ws.
-uw_status run_decode(const uw_dmat* d, int mode, uint8_t* out, void* ws, size_t ws_bytes, hipStream_t s);
+// max_wgs > 0: at most that many decoder workgroups (index and exponent output from chunks of
+// at most 512 symbols; they take the units in turn), so the decode occupies only part of the
+// chip; 0: as many as the units fill.
+uw_status run_decode(const uw_dmat* d, int mode, uint8_t* out, void* ws, size_t ws_bytes, hipStream_t s,
+                     int max_wgs = 0);
 // uw_glue.hip: row-wise RMS norm of an fp32 [m, n] y into BF16 x.
 bool rms_vec(const float* y, const uint16_t* x, int n);
 hipError_t launch_rmsnorm(const float* y, uint16_t* x, int32_t m, int32_t n, float eps, hipStream_t s);

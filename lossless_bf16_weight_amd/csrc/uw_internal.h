@@ -1,5 +1,5 @@
 // Internal definitions shared by the host codec (uw_host.cpp) and the device side
-// (uw_device.hip) of libuw.  Not part of the public ABI.
+// (uw_device.h and the .hip sources) of libuw.  Not part of the public ABI.
 #pragma once
 
 #include <cstddef>

@@ -17,8 +17,10 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import (UW_PIPE_AUTO, UW_PIPE_DIRECT_PALETTE, CompressedMatrix, Sched, uw_check, uw_gemm, uw_gemm_rmsnorm,
-               uw_gemm_swiglu, uw_rmsnorm, uw_swiglu, uw_workspace_size)
+from . import (UW_PIPE_AUTO, UW_PIPE_DIRECT_PALETTE, CompressedMatrix, Sched, uw_check, uw_gemm_rmsnorm, uw_gemm_swiglu,
+               uw_gemm_variant, uw_rmsnorm, uw_swiglu, uw_workspace_size)
+
+PROJECTIONS = ("gate", "up", "down")
 
 
 class MLPStack:
@@ -47,39 +49,44 @@ class MLPStack:
             mats.append(cm)
         self.layers.append(tuple(mats))
 
-    def _workspace(self, pipeline):
+    def _workspace(self, pipelines):
+        """A zeroed workspace that serves every matrix under `pipelines` (one per projection)."""
         import torch
-        need = max(uw_workspace_size(cm.d, self.m, pipeline) for lay in self.layers for cm in lay)
+        need = max(uw_workspace_size(cm.d, self.m, p) for lay in self.layers for cm, p in zip(lay, pipelines))
         if need > self.ws_bytes:
             self.ws = torch.zeros(need, dtype=torch.uint8, device=self.dev)
             self.ws_bytes = need
         return self.ws if need else None
 
-    def step(self, x, pipeline=UW_PIPE_AUTO, trace=None, check=True, fused=None):
+    def step(self, x, pipeline=UW_PIPE_AUTO, trace=None, check=True, fused=None, config=None):
         """x: device int16 [m, hidden] (BF16 bits).  Returns the device tensor holding the last
         layer's output (one of two ping-pong buffers).  trace: optional list that receives,
         per layer, host copies (x_in, g, u, h, y, x_out) -- for tests; it synchronises.
         check: wait for the step and report a corrupt stream found by a decode pipeline
         (UwError); pass False to keep the step asynchronous.  fused: SwiGLU in the up GEMM's
         epilogue and the RMS norm after the down GEMM in one call (default unless tracing,
-        which needs u itself); the outputs are identical."""
+        which needs u itself); the outputs are identical.  config: per projection
+        {"gate"|"up"|"down": (pipeline, variant)} (e.g. a tuned per-model file), overriding
+        `pipeline` and the autotuned variants."""
         fused = trace is None if fused is None else fused
         if fused and trace is not None:
             raise ValueError("a traced step needs u: use fused=False")
-        ws = self._workspace(pipeline)
+        cfg = [(pipeline, -1)] * 3 if config is None else [tuple(config[k]) for k in PROJECTIONS]
+        (pg, vg), (pu, vu), (pd, vd) = cfg
+        ws = self._workspace((pg, pu, pd))
         cur = x
         for i, (gate, up, down) in enumerate(self.layers):
             out = self.xs[i % 2]
-            uw_gemm(gate.d, cur, self.g, self.m, pipeline, ws)
+            uw_gemm_variant(gate.d, cur, self.g, self.m, pg, vg, ws)
             if fused:
-                uw_gemm_swiglu(up.d, cur, self.g, self.h, self.m, pipeline, -1, ws)
+                uw_gemm_swiglu(up.d, cur, self.g, self.h, self.m, pu, vu, ws)
             else:
-                uw_gemm(up.d, cur, self.u, self.m, pipeline, ws)
+                uw_gemm_variant(up.d, cur, self.u, self.m, pu, vu, ws)
                 uw_swiglu(self.g, self.u, self.h)
             if fused:
-                uw_gemm_rmsnorm(down.d, self.h, self.y, out, self.m, self.eps, pipeline, -1, ws)
+                uw_gemm_rmsnorm(down.d, self.h, self.y, out, self.m, self.eps, pd, vd, ws)
             else:
-                uw_gemm(down.d, self.h, self.y, self.m, pipeline, ws)
+                uw_gemm_variant(down.d, self.h, self.y, self.m, pd, vd, ws)
                 uw_rmsnorm(self.y, out, self.eps)
             if trace is not None:
                 trace.append(tuple(t.cpu().numpy().copy() for t in (cur, self.g, self.u, self.h, self.y, out)))
@@ -111,7 +118,7 @@ class HardEasyStack:
     bits).  hard_layers: the layer indices whose three matrices are hard."""
 
     def __init__(self, m, hidden, inter, matrices, hard_layers=(), device="cuda:0", eps=1e-5, chunk=0,
-                 overlap=True):
+                 overlap=True, decode_workgroups=0):
         import torch
         self.m, self.hidden, self.inter, self.eps = m, hidden, inter, eps
         self.dev = torch.device(device)
@@ -149,6 +156,8 @@ class HardEasyStack:
         self.side = torch.cuda.Stream(device=self.dev) if overlap else torch.cuda.current_stream(self.dev)
         self.sched = Sched([cm.d for cm in flat], hard, m, hidden, inter, self.slots, self.slot_bytes, self.g, self.h,
                            self.y, self.xo, self.ws, self.dws, eps, torch.cuda.current_stream(self.dev), self.side)
+        if decode_workgroups:
+            self.sched.split(decode_workgroups)
 
     def step(self, x, check=True, trace=None):
         """One decode step from x (device int16 [m, hidden], BF16 bits) on the current stream

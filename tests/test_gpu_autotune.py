@@ -109,3 +109,75 @@ def test_auto_dispatch_against_oracle(tuned, source, tmp_path):
             assert t.equal(y, y2), "m=%d: AUTO did not run pipeline %d variant %d" % (m, pipe, var)
     finally:
         uw.uw_autotune_clear()
+
+
+# ----------------------------------------------------------------------------------------------
+# End-to-end coordinate descent over an MLP stack's step (per projection), and the decode/GEMM
+# split coordinate of a stack with hard layers.
+# ----------------------------------------------------------------------------------------------
+def _small_stack(m, layers=3, seed=61):
+    from lossless_bf16_weight_amd.stack import MLPStack
+    rng = np.random.default_rng(seed)
+    hidden, inter = 256, 704
+    mats = [(synth.small_gaussian(inter, hidden, seed=seed + 3 * l, plant_frac=0.01)["w"],
+             synth.gaussian_bf16(rng, (inter, hidden), 0.03),
+             synth.student_t_bf16(rng, (hidden, inter), 3, 0.02)) for l in range(layers)]
+    st = MLPStack(m, hidden, inter)
+    for lay in mats:
+        st.add_layer(*lay)
+    x = synth.gaussian_bf16(rng, (m, hidden), 1.0)
+    return st, mats, x
+
+
+@pytest.mark.parametrize("m", [1, 16])
+def test_step_tuner_coordinate_descent(m, tmp_path):
+    """The tuned configuration is the fastest of everything the descent measured, no slower than
+    its start (the default), and the step it runs equals the oracle-checked step bit for bit:
+    every GEMM of the traced (unfused) step under the tuned configuration within the oracle
+    bound on the device's own inputs, and the fused step ending in the same bits.  The per-model
+    file round-trips."""
+    t = torch()
+    from lossless_bf16_weight_amd.stack import PROJECTIONS, as_bf16_bits
+    st, mats, x = _small_stack(m)
+    xd = t.from_numpy(x.view(np.int16)).cuda()
+    tuner = autotune.StepTuner(st, xd, variants=[-1, 5, 9, 10, 14], steps=4, rounds=3)
+    res = tuner.tune(max_sweeps=3)
+    assert res["us"] == min(us for _, us in tuner.evals)
+    assert res["us"] <= res["default_us"]
+    assert res["sweeps"] >= 1 and len(tuner.evals) >= 1 + 3 * (len(tuner.candidates()) - 1)
+    cfg = res["config"]
+    trace = []
+    st.step(xd, config=cfg, trace=trace)
+    for l, (xi, g, u, h, y, xo) in enumerate(trace):
+        xi, h = as_bf16_bits(xi), as_bf16_bits(h)
+        for (inp, out), wm in zip(((xi, g), (xi, u), (h, y)), mats[l]):
+            y_ref, s_ = gemm.gemm_ref(inp, wm)
+            ok = gemm.within_bound(out.astype(np.float64), y_ref, s_)
+            assert ok.all(), "layer %d: %d outside bound under %s" % (l, (~ok).sum(), cfg)
+    fused = st.step(xd, config=cfg)
+    assert np.array_equal(as_bf16_bits(fused), as_bf16_bits(trace[-1][5]))
+    path = tmp_path / "model.json"
+    autotune.save_model_config(str(path), "test-mlp", m, res)
+    cfg2, split = autotune.load_model_config(str(path))
+    assert cfg2 == {k: tuple(cfg[k]) for k in PROJECTIONS} and split == 0
+
+
+def test_step_tuner_split_coordinate():
+    """The decode/GEMM split of a stack with hard layers: the chosen decoder workgroup count is
+    the argmin of its own measurements, and every split gives the plain step's bits."""
+    t = torch()
+    from lossless_bf16_weight_amd.stack import HardEasyStack
+    st, mats, x = _small_stack(16, layers=4, seed=71)
+    xd = t.from_numpy(x.view(np.int16)).cuda()
+    ref = st.step(xd, pipeline=uw.UW_PIPE_DIRECT_PALETTE).clone()
+    outs = {}
+
+    def make(split):
+        hs = HardEasyStack(16, 256, 704, mats, hard_layers=(1, 3), decode_workgroups=split)
+        outs[split] = hs.step(xd).clone()
+        return hs
+
+    res = autotune.StepTuner.tune_split(make, xd, splits=(0, 1, 4), steps=4, rounds=3)
+    assert res["us"] == min(res["all"].values()) and res["all"][res["decode_workgroups"]] == res["us"]
+    for sp, o in outs.items():
+        assert t.equal(o, ref), "split %d" % sp

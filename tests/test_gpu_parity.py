@@ -589,9 +589,10 @@ def test_gemm_rmsnorm_equals_unfused(name):
                     assert t.equal(xn, xn_ref), what
 
 
+@pytest.mark.parametrize("split", [0, 2])
 @pytest.mark.parametrize("m", [1, 16])
 @pytest.mark.parametrize("hard", [(), (0,), (1, 2), (3,), (0, 1, 2, 3)], ids=["none", "first", "middle", "last", "all"])
-def test_hard_easy_stack_equals_plain(m, hard):
+def test_hard_easy_stack_equals_plain(m, hard, split):
     """The hard/easy scheduler (uw_sched_*: hard layers keep only their bundle, their index
     streams decoded on a side stream into two alternating slot sets ahead of use) gives the
     same bits as the plain fused step on the same matrices, for three steps in a row (each
@@ -605,7 +606,7 @@ def test_hard_easy_stack_equals_plain(m, hard):
     plain = MLPStack(m, hidden, inter)
     for lay in mats:
         plain.add_layer(*lay)
-    sched = HardEasyStack(m, hidden, inter, mats, hard_layers=hard)
+    sched = HardEasyStack(m, hidden, inter, mats, hard_layers=hard, decode_workgroups=split)
     for l, lay in enumerate(sched.layers):
         assert all((cm.idx is None) == (l in hard) for cm in lay)
     x = dev_u16(synth.gaussian_bf16(rng, (m, hidden), 1.0))
@@ -643,21 +644,23 @@ def check_swiglu_through_gemm_bound(h, g, x_in, w_up):
     assert ok.all(), "%d of %d SwiGLU outputs outside the interval" % ((~ok).sum(), ok.size)
 
 
-@pytest.mark.parametrize("m", [1, 16])
-@pytest.mark.parametrize("hard", [(0, 2), (0, 1, 2, 3)], ids=["alternate", "all"])
-def test_hard_easy_stack_against_oracle(m, hard):
+@pytest.mark.parametrize("m,hard,split", [(1, (0, 2), 0), (16, (0, 2), 0), (1, (0, 1, 2, 3), 0), (16, (0, 1, 2, 3), 0),
+                                          (16, (0, 2), 1), (1, (0, 1, 2, 3), 3)],
+                         ids=["alternate-1", "alternate-16", "all-1", "all-16", "alternate-16-split1", "all-1-split3"])
+def test_hard_easy_stack_against_oracle(m, hard, split):
     """Each GEMM of a scheduled step (hard layers decoded on the side stream) against the
     oracle on the inputs the device fed it (teacher-forced, from the library's per-layer
     trace): gate y = x W^T and down y = h W^T within the GEMM bound, the up GEMM through its
     fused SwiGLU epilogue within the bound's interval, the RMS norm within one BF16 ulp; two
-    steps in a row, the second from the first's output."""
+    steps in a row, the second from the first's output.  split > 0: the hard layers' decodes
+    run on that many decoder workgroups, which take the decode units in turn."""
     from lossless_bf16_weight_amd.stack import HardEasyStack
     rng = np.random.default_rng(31)
     hidden, inter, layers = 256, 704, 4
     mats = [(synth.small_gaussian(inter, hidden, seed=100 + 3 * l, plant_frac=0.01)["w"],
              synth.gaussian_bf16(rng, (inter, hidden), 0.03),
              synth.student_t_bf16(rng, (hidden, inter), 3, 0.02)) for l in range(layers)]
-    sched = HardEasyStack(m, hidden, inter, mats, hard_layers=hard)
+    sched = HardEasyStack(m, hidden, inter, mats, hard_layers=hard, decode_workgroups=split)
     x = dev_u16(synth.gaussian_bf16(rng, (m, hidden), 1.0))
     for step in range(2):
         trace = []
