@@ -267,6 +267,8 @@ def diagnostic(args):
         return stack_step(args, steps, warmup)
     if args.workload == "stack-hard":
         return stack_hard_step(args, steps, warmup)
+    if args.workload == "stack-tune":
+        return stack_tune(args, steps, warmup)
     if args.workload == "large":
         # gate_proj shape at prefill-sized batches: X drawn like the other configs' X.
         c = synth.config2()
@@ -427,14 +429,20 @@ def stack_hard_step(args, steps, warmup):
                     hard_cms[(l, j)] = uw.CompressedMatrix(None, blob=bundles[3 * l + j], keep_index=False)
         mats = [tuple(hard_cms[(l, j)] if l in hard else easy[3 * l + j] for j in range(3)) for l in range(layers)]
         row = {"hard_layers": len(hard)}
-        for overlap in (True, False) if hard else (True,):
-            st = HardEasyStack(16, 4096, 14336, mats, hard_layers=hard, overlap=overlap)
+        # (overlap, decoder workgroups): side-stream decode on the whole chip, on a persistent
+        # grid of 32 / 64 / 128 workgroups (the rest of the chip left to the GEMMs), and the
+        # decodes on the main stream.
+        runs = [(True, 0)] + ([(True, 32), (True, 64), (True, 128), (False, 0)] if hard else [])
+        for overlap, split in runs:
+            st = HardEasyStack(16, 4096, 14336, mats, hard_layers=hard, overlap=overlap, decode_workgroups=split)
             out = st.step(x, check=True)
-            assert torch.equal(out, ref), "scheduled step (%s, overlap=%s) differs from the plain step" % (name, overlap)
+            assert torch.equal(out, ref), "scheduled step (%s, overlap=%s, split=%d) differs from the plain step" % (
+                name, overlap, split)
             tot, _ = time_launches(lambda i: st.step(x, check=False), 1, steps, warmup, torch.cuda.current_stream())
             torch.cuda.synchronize()
             uw.uw_check(st.dws)
-            row["us_overlap" if overlap else "us_main_stream"] = round(tot * 1e3 / steps, 1)
+            key = ("us_overlap" if overlap else "us_main_stream") + ("_split%d" % split if split else "")
+            row[key] = round(tot * 1e3 / steps, 1)
             row["bits_per_weight"] = round(8 * st.resident_bytes() / st.weight_count(), 4)
             row["weight_gb"] = round(st.resident_bytes() / 1e9, 3)
             st.close()
@@ -442,6 +450,55 @@ def stack_hard_step(args, steps, warmup):
         res[name] = row
         log("stack-hard %s: %s" % (name, row))
     return {"diagnostic": "stack-hard", "layers": layers, "m": 16, "results": res}
+
+
+def stack_tune(args, steps, warmup):
+    """End-to-end tuning of the 32-layer stack's step at M = 1 and M = 16: coordinate descent over
+    (pipeline, kernel variant) per projection on the measured step time, the tuned step checked
+    bit-identical to the same configuration's traced step, written to a per-model file
+    (--config-out, one file per M)."""
+    import torch
+    from concurrent.futures import ThreadPoolExecutor
+    import lossless_bf16_weight_amd as uw
+    from lossless_bf16_weight_amd import autotune, synth
+    from lossless_bf16_weight_amd.stack import MLPStack
+    meta = synth.config4_meta()
+    layers = len(meta["stds"])
+    t0 = time.time()
+    jobs = [(l, j) for l in range(layers) for j in range(3)]
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        cms = list(ex.map(lambda lj: uw.CompressedMatrix(synth.config4_matrix(meta, *lj)), jobs))
+    log("stack built in %.1fs" % (time.time() - t0))
+    res = {}
+    for m in (1, 16):
+        st = MLPStack(m, 4096, 14336)
+        for l in range(layers):
+            st.add_layer(*cms[3 * l:3 * l + 3])
+        x = torch.from_numpy(np.ascontiguousarray(meta["x"][:m]).view(np.int16)).cuda()
+        tuner = autotune.StepTuner(st, x, pipelines=(uw.UW_PIPE_TRANSCODE, uw.UW_PIPE_DIRECT_PALETTE),
+                                   steps=8, rounds=3)
+        t0 = time.time()
+        r = tuner.tune(max_sweeps=3, log=log)
+        cfg = r["config"]
+        trace = []
+        st.step(x, config=cfg, trace=trace)
+        out = st.step(x, config=cfg)
+        assert np.array_equal(out.cpu().numpy(), trace[-1][5]), "tuned fused step differs from its traced step"
+        tot, _ = time_launches(lambda i: st.step(x, config=cfg, check=False), 1, steps, warmup,
+                               torch.cuda.current_stream())
+        row = {"us_per_step": round(tot * 1e3 / steps, 1), "tuner_us": round(r["us"], 1),
+               "default_us": round(r["default_us"], 1), "sweeps": r["sweeps"], "evals": len(tuner.evals),
+               "tune_s": round(time.time() - t0, 1),
+               "config": {k: [autotune.PIPELINE_NAMES[p], uw.uw_variant_name(v) if v >= 0 else "library default"]
+                          for k, (p, v) in cfg.items()}}
+        if args.config_out:
+            path = args.config_out.replace(".json", "") + "_m%d.json" % m
+            autotune.save_model_config(path, "llama-3.1-8b-mlp-32x(14336x4096,4096x14336)", m, r)
+            row["file"] = path
+        res["m%d" % m] = row
+        log("stack-tune m=%d: %s" % (m, row))
+        del st, tuner
+    return {"diagnostic": "stack-tune", "layers": layers, "results": res}
 
 
 def main():
@@ -456,11 +513,15 @@ def main():
                     help="BF16 GEMV variant with --variant (default: the library's choice for the shape)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run three device copies of 512 MiB (HBM counter calibration) and exit")
-    ap.add_argument("--workload", default="gate", choices=("gate", "down", "heavy", "stack", "stack-hard", "small", "large"),
-                    help="gate (default: the headline line); down, heavy, stack, stack-hard, small, large: "
-                         "diagnostic lines for the down_proj batch sweep, the 8192^2 heavy-tail matrix at M=128, the "
-                         "32-layer stack, the same stack with hard (bundle-only) layers decoded ahead on a side "
-                         "stream, the 1024^2 single-matrix case, and gate_proj at M = 256, 512, 1024")
+    ap.add_argument("--workload", default="gate",
+                    choices=("gate", "down", "heavy", "stack", "stack-hard", "stack-tune", "small", "large"),
+                    help="gate (default: the headline line); down, heavy, stack, stack-hard, stack-tune, small, "
+                         "large: diagnostic lines for the down_proj batch sweep, the 8192^2 heavy-tail matrix at "
+                         "M=128, the 32-layer stack, the same stack with hard (bundle-only) layers decoded ahead on a "
+                         "side stream (whole chip or a persistent decoder grid), the stack's step tuned end to end "
+                         "per projection, the 1024^2 single-matrix case, and gate_proj at M = 256, 512, 1024")
+    ap.add_argument("--config-out", default="",
+                    help="stack-tune: per-model configuration file prefix (written as <prefix>_m<M>.json)")
     args = ap.parse_args()
     if args.copy_calibration:
         import torch
