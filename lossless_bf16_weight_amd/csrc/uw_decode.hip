@@ -397,10 +397,10 @@ __global__ __launch_bounds__(64) void k_decode(DecArgs a) {
 // bitstream slices and every unit of a large matrix is resident at once; the wave writes its
 // output lines once, whole, when the unit is done (HBM traffic: the bitstream in, the output
 // out).  A VGPR cannot be indexed per lane, so words reach the image through a small LDS
-// buffer per lane, in phases of four rows: phase h ends when every lane of the wave has
-// decoded its rows 4h .. 4h + 3, and its 32 words are then copied to statically indexed VGPRs.
+// buffer per lane, in phases of two rows: phase h ends when every lane of the wave has
+// decoded its rows 2h, 2h + 1, and its 16 words are then copied to statically indexed VGPRs.
 // A lookup may run up to four symbols past a phase (less than a word), which land in the
-// buffer's 33rd word and carry over.
+// buffer's 17th word and carry over.
 //   Table entry: total code length of the entry's symbols in bits 0-3, 4 x symbol count in
 //   bits 4-8, the symbols in bits 12-31 (first in bits 12-15).  Length and count 0: the window
 //   starts a 13-bit code (bits 9-11: block of two secondary entries chosen by the 13th bit;
@@ -413,8 +413,10 @@ constexpr int kRowLut = 1 << kRowWin;       // primary entries
 constexpr int kRowSecBlocks = 8;            // secondary blocks of 2 (block 0: invalid)
 constexpr int kRowSec = 2 * kRowSecBlocks;
 constexpr int kRowMaxSyms = 5;              // symbols an entry
-constexpr int kPhaseWords = 32;             // words a phase (four rows)
-constexpr int kBufStride = kPhaseWords + 1; // words of one lane's phase buffer (33: spreads LDS banks)
+constexpr int kPhaseRows = 2;               // rows a phase
+constexpr int kPhaseWords = 8 * kPhaseRows; // words a phase
+constexpr int kPhases = 8 / kPhaseRows;     // phases of the longest chunk (eight rows)
+constexpr int kBufStride = kPhaseWords + 1; // words of one lane's phase buffer (odd: spreads LDS banks)
 constexpr uint32_t kBufBytes = 64u * kBufStride * 4u;    // one wave's phase buffers
 constexpr uint32_t kRowTmpBytes = kRowLut * 2u;          // table-build scratch (u16 a window)
 
@@ -624,10 +626,10 @@ __device__ __forceinline__ void decode_unit(const RowDecArgs& a, uint32_t* lut, 
   };
 
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    if (4 * h >= wmax_rows) break;
-    // Phase h needs symbols up to 256 (h + 1) of the chunk: rem4 down to lim.
-    const int32_t lim = max(4 * (64 * nrows - 256 * (h + 1)), 0);
+  for (int h = 0; h < kPhases; ++h) {
+    if (kPhaseRows * h >= wmax_rows) break;
+    // Phase h needs symbols up to 128 (h + 1) of the chunk: rem4 down to lim.
+    const int32_t lim = max(4 * (64 * nrows - 64 * kPhaseRows * (h + 1)), 0);
     const int32_t fast_lim = max(lim, 4 * kRowMaxSyms - 1);
     while (true) {
       // Hot loop: whole table entries while five or more symbols remain.
@@ -779,7 +781,7 @@ __device__ __forceinline__ void decode_unit(const RowDecArgs& a, uint32_t* lut, 
 // The decoder grid: gridDim.x workgroups of W waves; a grid smaller than the units (a decode
 // sharing the chip with other work) takes its units in turn, the table built once.
 template <int MODE>
-__global__ __launch_bounds__(512) void k_decode_rows(RowDecArgs a) {
+__global__ __launch_bounds__(1024) void k_decode_rows(RowDecArgs a) {
   __shared__ uint32_t lut[kRowLut + kRowSec];
   extern __shared__ __align__(16) uint8_t dsh[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -794,7 +796,7 @@ __global__ __launch_bounds__(512) void k_decode_rows(RowDecArgs a) {
 static int row_waves(uint32_t stage_words, int64_t units, int lds_wg_max, int lds_cu, int cus) {
   int best_w = 0;
   int64_t best_rounds = INT64_MAX, best_cus = -1;
-  for (int W = 8; W >= 1; --W) {
+  for (int W = 16; W >= 1; --W) {
     const int64_t lds = (int64_t)row_buf_area(W) + (int64_t)W * stage_words * 4 + (kRowLut + kRowSec) * 4;
     if (lds > lds_wg_max) continue;
     const int64_t per_cu = std::max<int64_t>(1, lds_cu / lds);
@@ -886,7 +888,7 @@ static uw_status run_decode_rows(const uw_dmat* d, int mode, uint8_t* out, uint3
   switch (mode) {
     case DEC_IDX: hipLaunchKernelGGL(k_decode_rows<DEC_IDX>, grid, dim3(64 * W), lds, s, a); break;
     case DEC_EXP: hipLaunchKernelGGL(k_decode_rows<DEC_EXP>, grid, dim3(64 * W), lds, s, a); break;
-    default: hipLaunchKernelGGL(k_decode_rows<DEC_BF16>, grid, dim3(64 * W), lds, s, a); break;
+    default: return fail(UW_E_ARG, "the row decoder writes indices or exponents");
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(UW_E_HIP, "decode launch: %s", hipGetErrorString(e));
