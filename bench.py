@@ -141,7 +141,7 @@ def cpu_baseline(w, x, seconds=2.5):
 
 class ClockSampler:
     """Samples the GPU's current sclk/mclk (sysfs pp_dpm_*, the starred line) in a thread
-    while the timed region runs; reports min / median / max MHz over the samples."""
+    while the GPU runs the measured kernel; reports min / median / max MHz over the samples."""
 
     def __init__(self, period_s=0.002):
         import threading
@@ -180,7 +180,7 @@ class ClockSampler:
         self._thread.join()
 
     def summary(self):
-        """{clock: {min, median, max MHz, samples}} over the timed region, or None."""
+        """{clock: {min, median, max MHz, samples}} over the sampled run, or None."""
         out = {}
         for name, v in self.counts.items():
             v = sorted(v)
@@ -210,18 +210,20 @@ def settle(fn, copies, stream, ms=SETTLE_MS):
 
 def time_launches(fn, copies, steps, warmup, stream):
     """fn(i) launches on `stream`.  Returns (total_ms, per-launch ms list).  The clocks are
-    settled first, then `warmup` untimed launches, then exactly `steps` timed ones."""
+    settled first; then, from an idle synchronised GPU, `warmup` untimed launches immediately
+    followed by exactly `steps` timed ones between two events.  The untimed launches are the
+    runway: the GPU is busy with them while the host queues the first timed launches, so the
+    timed region holds back-to-back kernels and not the host's latency to queue the first one
+    (with few steps that latency would otherwise be a visible share of the region)."""
     import torch
     settle(fn, copies, stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     for i in range(warmup):
         fn(i % copies)
-    torch.cuda.synchronize()
-    # back-to-back launches, events around the whole run
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     e0.record(stream)
     for i in range(steps):
-        fn(i % copies)
+        fn((warmup + i) % copies)
     e1.record(stream)
     torch.cuda.synchronize()
     total = e0.elapsed_time(e1)
@@ -600,8 +602,11 @@ def main():
     ok = ogemm.within_bound(y.cpu().numpy().astype(np.float64)[:, rows], yr, s)
     assert ok.all(), "parity failure in the timed configuration"
 
+    total_ms, per = time_launches(step, copies, args.steps, args.warmup, stream)
+    # Clocks under the same load, sampled right after the timed region (a sampling thread
+    # during it would take the interpreter lock between launches and open gaps on the GPU).
     with ClockSampler() as clk:
-        total_ms, per = time_launches(step, copies, args.steps, args.warmup, stream)
+        settle(step, copies, stream, ms=100.0)
     us = total_ms * 1e3 / args.steps
     med, p10, p90 = per[len(per) // 2] * 1e3, per[len(per) // 10] * 1e3, per[(9 * len(per)) // 10] * 1e3
     eff_gbs = 2.0 * n * k / (us * 1e-6) / 1e9
@@ -632,7 +637,7 @@ def main():
     cpu = None if args.no_cpu else cpu_baseline(w, x)
     traffic = traffic_from_profile()
     dinfo.update({k: v for k, v in device_info().items() if k != "gpu" and v is not None})
-    dinfo["clocks_during_timed_region"] = clk.summary()
+    dinfo["clocks_under_load_after_timed_region"] = clk.summary()
     out = {
         "metric": METRIC,
         "value": round(eff_gbs, 1),
