@@ -452,17 +452,26 @@ __host__ __device__ inline uint32_t row_buf_area(int W) {
   return std::max<uint32_t>(kRowTmpBytes, (uint32_t)W * kBufBytes);
 }
 
+// Workgroup barrier for LDS data only: waits for this wave's LDS accesses, not for its global
+// loads, so the stage DMAs stay in flight across it (__syncthreads() would wait for them).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(63) & ~0x0F00);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __device__ void build_row_lut(const RowDecArgs& a, uint32_t* lut, uint16_t* tmp) {
   const int tid = threadIdx.x, nt = blockDim.x;
   for (int i = tid; i < kRowLut / 2; i += nt) reinterpret_cast<uint32_t*>(tmp)[i] = 0;
-  __syncthreads();
+  lds_barrier();
   for (int s = 0; s < 16; ++s) {
     const int L = a.len[s];
     if (L == 0 || L > kRowWin) continue;
     const uint32_t lo = (uint32_t)a.code[s] << (kRowWin - L), cnt = 1u << (kRowWin - L);
     for (uint32_t i = tid; i < cnt; i += nt) tmp[lo + i] = (uint16_t)(s | (L << 4) | 0x100);
   }
-  __syncthreads();
+  lds_barrier();
   // Four windows a thread at a time (independent chains of table reads).
   constexpr int kIlp = 4;
   for (int w0 = tid; w0 < kRowLut; w0 += nt * kIlp) {
@@ -502,8 +511,12 @@ __device__ void build_row_lut(const RowDecArgs& a, uint32_t* lut, uint16_t* tmp)
       lut[w] = entry;
     }
   }
-  for (int i = tid; i < kRowSec; i += nt) lut[kRowLut + i] = a.sec[i];
-  __syncthreads();
+  // Constant indices: the entries come from the kernel arguments through scalar loads (an
+  // indexed read would be a vector load, and waiting for it would wait for the stage DMAs).
+#pragma unroll
+  for (int i = 0; i < kRowSec; ++i)
+    if (tid == i) lut[kRowLut + i] = a.sec[i];
+  lds_barrier();
 }
 
 // Sequential nibbles n0..n7 (n_i at bits 4i) -> 8 exponent bytes in column order.
@@ -555,17 +568,6 @@ __device__ __forceinline__ void decode_unit(const RowDecArgs& a, uint32_t* lut, 
   const uint32_t c_first = unit_ok ? a.cbase[t] + ch_before : 0u;
   const uint32_t vblk = unit_ok ? a.vprefix[t] + v_before + v_incl - nv : 0u;   // per block lane
 
-  // Stage the unit's bitstream slice (1 KB LDS-DMA steps; words past the stream read zero).
-  uint32_t wb = 0, nst = 0;
-  if (unit_chunks) {
-    wb = (a.off[c_first] >> 5) & ~3u;
-    const uint32_t we = (a.off[c_first + unit_chunks] >> 5) + 3u;
-    nst = min((we - wb + 255u) & ~255u, a.stage_words);
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.words, a.words_cap * 4u);
-    for (uint32_t i = 0; i < nst; i += 256u)
-      lds_dma16(rs, reinterpret_cast<uint8_t*>(stage + i), (wb + i) * 4u + (uint32_t)lane * 16u);
-  }
-
   // Lane -> (block in unit, chunk slot in block) and this lane's chunk.
   const int bl = lane / a.cpb, j = lane - (lane / a.cpb) * a.cpb;
   const int src = bl < 64 ? bl : 0;
@@ -578,15 +580,37 @@ __device__ __forceinline__ void decode_unit(const RowDecArgs& a, uint32_t* lut, 
   const bool has_chunk = lane_ok && j * a.spc < ncoded;
   const int nrows = has_chunk ? min(a.spc, ncoded - j * a.spc) : 0;
   const uint32_t c = c_first + bpre + (uint32_t)j;
-  const uint32_t p0 = has_chunk ? a.off[c] - wb * 32u : 0u, p1 = has_chunk ? a.off[c + 1] - wb * 32u : 0u;
   int wmax_rows = nrows;                                        // most rows of any chunk of the wave
   for (int o = 32; o > 0; o >>= 1) wmax_rows = max(wmax_rows, __shfl_xor(wmax_rows, o, 64));
   wmax_rows = __builtin_amdgcn_readfirstlane(wmax_rows);
 
+  // Every bit offset the unit needs (slice ends, the lane's chunk) in one round trip, then the
+  // slice staged (1 KB LDS-DMA steps; words past the stream read zero).  Nothing below waits
+  // on a global load until the decode itself: loads retire in order, so such a wait would also
+  // wait for every DMA issued before it.
+  uint32_t o_first = 0, o_end = 0, o_c0 = 0, o_c1 = 0;
+  if (unit_chunks) {
+    o_first = a.off[c_first];
+    o_end = a.off[c_first + unit_chunks];
+  }
+  if (has_chunk) {
+    o_c0 = a.off[c];
+    o_c1 = a.off[c + 1];
+  }
+  uint32_t wb = 0, nst = 0;
+  if (unit_chunks) {
+    wb = (o_first >> 5) & ~3u;
+    const uint32_t we = (o_end >> 5) + 3u;
+    nst = min((we - wb + 255u) & ~255u, a.stage_words);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.words, a.words_cap * 4u);
+    for (uint32_t i = 0; i < nst; i += 256u)
+      lds_dma16(rs, reinterpret_cast<uint8_t*>(stage + i), (wb + i) * 4u + (uint32_t)lane * 16u);
+  }
+  const uint32_t p0 = has_chunk ? o_c0 - wb * 32u : 0u, p1 = has_chunk ? o_c1 - wb * 32u : 0u;
+
   if (first)
-    build_row_lut(a, lut, reinterpret_cast<uint16_t*>(dsh));   // its last barrier also waits for the stage
-  else
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));                  // this wave's stage DMA (and earlier stores)
+    build_row_lut(a, lut, reinterpret_cast<uint16_t*>(dsh));   // LDS barriers only: the DMAs stay in flight
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));                    // this wave's stage (and earlier stores)
   if (!unit_ok) return;
 
   // Bit window: the 32 bits starting (32 - s) bits into w0 (s = 0: w1 itself); nxp: next word.
