@@ -526,6 +526,21 @@ __device__ __forceinline__ u32x2 seq_word_to_exps(uint32_t v, const uint32_t tab
   return u32x2{perm(od, ev, 0x05010400u), perm(od, ev, 0x07030602u)};
 }
 
+// 4 x symbol count of a table entry, and a slice pointer moved on by 0 or 1 words, each as the
+// single ALU instruction it is (the compiler otherwise splits them into shift-and-mask pairs
+// in the decode loop, which is bound by instruction issue).
+__device__ __forceinline__ uint32_t entry_n4(uint32_t e) {
+  uint32_t r;
+  asm("v_bfe_u32 %0, %1, 4, 5" : "=v"(r) : "v"(e));
+  return r;
+}
+typedef const __attribute__((address_space(3))) uint32_t* lds_cu32p;
+__device__ __forceinline__ lds_cu32p advance_word(lds_cu32p p, uint32_t step) {
+  uint32_t r;
+  asm("v_lshl_add_u32 %0, %1, 2, %2" : "=v"(r) : "v"(step), "v"((uint32_t)(uintptr_t)p));
+  return (lds_cu32p)(uintptr_t)r;
+}
+
 // One unit (wave `wave` of the workgroup, unit u).  first: the workgroup's first unit, whose
 // stage DMA overlaps the table build (every wave of the workgroup takes part in the build, unit
 // or not); later units wait for their own stage only.
@@ -613,40 +628,42 @@ __device__ __forceinline__ void decode_unit(const RowDecArgs& a, uint32_t* lut, 
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));                    // this wave's stage (and earlier stores)
   if (!unit_ok) return;
 
-  // Bit window: the 32 bits starting (32 - s) bits into w0 (s = 0: w1 itself); nxp: next word.
+  // Bit window: the 32 bits starting (32 - s) bits into w0 (s = 0: w1 itself); np: the next
+  // word of the slice.
   const uint32_t b0 = p0 & 31u, wi0 = p0 >> 5;
   uint32_t w0 = b0 ? stage[wi0] : 0u, w1 = stage[b0 ? wi0 + 1 : wi0];
-  uint32_t nxp = b0 ? wi0 + 2 : wi0 + 1;
+  lds_cu32p np = (lds_cu32p)(stage + (b0 ? wi0 + 2 : wi0 + 1));
   uint32_t s = b0 ? 32u - b0 : 0u;
   int32_t rem4 = nrows * 256;                                   // 4 x symbols left
-  uint64_t acc = 0;                                             // pending indices, 4 bits each
-  uint32_t a4 = 0;                                              // pending bits
-  uint32_t* wp = buf;                                           // the word in progress
-  uint32_t* pwp = buf;                                          // pending image write: address, value
-  uint32_t pv = 0;
+  uint32_t lo = 0;                                              // the word in progress (4-bit indices)
+  uint32_t a4 = 0;                                              // its bits filled
+  uint32_t* wp = buf;                                           // its place in the phase buffer
   uint32_t bad = 0;
   uint32_t img[64];
 #pragma unroll
   for (int i = 0; i < 64; ++i) img[i] = 0;
 
-  // One lookup's state change: e = (length, 4 x count, symbols) as in the table.
+  // One lookup's state change: e = (length, 4 x count, symbols) as in the table.  The word in
+  // progress is stored at every lookup (complete or not), so a finished word is already in the
+  // buffer when wp moves on; the symbols past it start the next word (a word boundary is never
+  // crossed at a4 = 0: an entry holds at most 20 bits, so the shift by 32 - a4 is then unused).
   auto apply = [&](uint32_t e, uint32_t v) {
-    const uint32_t L = e & 15u, n4 = (e >> 4) & 31u;
-    acc |= (uint64_t)(e >> 12) << a4;
-    a4 += n4;
+    const uint32_t L = e & 15u, n4 = entry_n4(e), sy = e >> 12;
+    const uint32_t lo2 = (sy << a4) | lo;
+    *wp = lo2;
+    const uint32_t a4n = a4 + n4;
+    const uint32_t carry = sy >> ((32u - a4) & 31u);
+    const bool done = a4n >= 32u;
+    lo = done ? carry : lo2;
+    a4 = a4n & 31u;
+    wp += done ? 1 : 0;
     rem4 -= (int32_t)n4;
     const int32_t sl = (int32_t)s - (int32_t)L;
     const bool neg = sl < 0;
     w0 = neg ? w1 : w0;
     w1 = neg ? v : w1;
-    nxp += neg ? 1u : 0u;
+    np = advance_word(np, (uint32_t)sl >> 31);
     s = (uint32_t)sl & 31u;
-    pwp = wp;                                                   // the word in progress, so far: written
-    pv = (uint32_t)acc;                                         // at the next lookup (off the loop's chain)
-    const uint32_t fl = a4 & 32u;                               // a word is finished
-    acc >>= fl;
-    a4 &= 31u;
-    wp += fl >> 5;
   };
 
 #pragma unroll
@@ -658,20 +675,18 @@ __device__ __forceinline__ void decode_unit(const RowDecArgs& a, uint32_t* lut, 
     while (true) {
       // Hot loop: whole table entries while five or more symbols remain.
       while (rem4 > fast_lim) {
-        *pwp = pv;
         const uint32_t win = __builtin_amdgcn_alignbit(w0, w1, s);
         const uint32_t e = lut[win >> (32 - kRowWin)];
-        const uint32_t v = stage[nxp];                          // refill candidate
+        const uint32_t v = *np;                                 // refill candidate
         apply(e, v);
-        if (((e >> 4) & 31u) == 0u) break;                      // a 13-bit code or no code
+        if (entry_n4(e) == 0u) break;                           // a 13-bit code or no code
       }
       const bool need = rem4 > lim;
       if (!__builtin_amdgcn_ballot_w64(need)) break;
       if (need) {                                               // one symbol the slow way
-        *pwp = pv;
         const uint32_t win = __builtin_amdgcn_alignbit(w0, w1, s);
         uint32_t e = lut[win >> (32 - kRowWin)];
-        const uint32_t v = stage[nxp];
+        const uint32_t v = *np;
         if (((e >> 4) & 31u) == 0u) {
           const uint32_t e2 = lut[kRowLut + ((e >> 9) & 7u) * 2u + ((win >> (31 - kRowWin)) & 1u)];
           const bool inv = ((e2 >> 4) & 31u) == 0u;
@@ -685,16 +700,14 @@ __device__ __forceinline__ void decode_unit(const RowDecArgs& a, uint32_t* lut, 
         apply(e, v);
       }
     }
-    // Phase done for every lane: its 32 words to VGPRs, the carried partial word to the front.
-    *pwp = pv;
+    // Phase done for every lane: its 16 finished words to VGPRs; the word in progress (a
+    // lookup's symbols past the phase) stays in lo and becomes the buffer's first word.
 #pragma unroll
     for (int i = 0; i < kPhaseWords; ++i) img[kPhaseWords * h + i] = buf[i];
     wp = buf;
-    pwp = buf;
-    pv = (uint32_t)acc;
   }
   if (has_chunk) {
-    const uint32_t pos = nxp * 32u - 32u - s;                   // bits consumed from the slice start
+    const uint32_t pos = (uint32_t)(np - (lds_cu32p)stage) * 32u - 32u - s;   // bits consumed from the slice start
     if (pos != p1) bad = 1;
   }
   if (bad) atomicOr(a.err, 1u);
