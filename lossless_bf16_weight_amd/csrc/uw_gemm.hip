@@ -1157,6 +1157,7 @@ static hipError_t launch_mt_c(const GemmArgs& a, int64_t tiles, int R, int U, in
   // Every wave issues the same number of X DMAs (2*CT*U a batch, a multiple of R); 128-row
   // batches use 2 blocks (64 KB of LDS, double-buffered).
   if constexpr (CT == 8) {
+    if (U <= 2 && R == 8) return launch_mt_t<SRC, 8, 1, 8>(a, tiles, S, part, s);
     return R == 8 ? launch_mt_t<SRC, 8, 2, 8>(a, tiles, S, part, s) : launch_mt_t<SRC, 8, 2, 4>(a, tiles, S, part, s);
   } else if constexpr (CT == 1) {
     return R == 8 ? launch_mt_t<SRC, 1, 4, 8>(a, tiles, S, part, s)
