@@ -401,11 +401,14 @@ def stack_hard_step(args, steps, warmup):
     t0 = time.time()
     jobs = [(l, j) for l in range(layers) for j in range(3)]
     easy, bundles = [], []
+    # Hard layers keep the bundle only; it is encoded with args.hard_chunk-symbol chunks (more,
+    # shorter chunks: more independent decode chains) -- the same weights, palette and index
+    # stream as the easy form, so every step must still equal the plain step bit for bit.
     with ThreadPoolExecutor(max_workers=8) as ex:
         for w in ex.map(lambda lj: synth.config4_matrix(meta, *lj), jobs):
             cm = uw.CompressedMatrix(w)
             easy.append(cm)
-            bundles.append(cm.blob)
+            bundles.append(uw.uw_encode(w, args.hard_chunk) if args.hard_chunk else cm.blob)
     log("stack built in %.1fs" % (time.time() - t0))
     for lj in ((0, 0), (0, 2)):
         tuner = autotune.Tuner(synth.config4_matrix(meta, *lj), bf16=False)
@@ -451,7 +454,8 @@ def stack_hard_step(args, steps, warmup):
             del st
         res[name] = row
         log("stack-hard %s: %s" % (name, row))
-    return {"diagnostic": "stack-hard", "layers": layers, "m": 16, "results": res}
+    return {"diagnostic": "stack-hard", "layers": layers, "m": 16, "hard_bundle_chunk": args.hard_chunk or 512,
+            "results": res}
 
 
 def stack_tune(args, steps, warmup):
@@ -522,6 +526,8 @@ def main():
                          "M=128, the 32-layer stack, the same stack with hard (bundle-only) layers decoded ahead on a "
                          "side stream (whole chip or a persistent decoder grid), the stack's step tuned end to end "
                          "per projection, the 1024^2 single-matrix case, and gate_proj at M = 256, 512, 1024")
+    ap.add_argument("--hard-chunk", type=int, default=256,
+                    help="stack-hard: chunk length (symbols) of the hard layers' bundles (0: the default encode)")
     ap.add_argument("--config-out", default="",
                     help="stack-tune: per-model configuration file prefix (written as <prefix>_m<M>.json)")
     args = ap.parse_args()
