@@ -620,6 +620,33 @@ def test_hard_easy_stack_equals_plain(m, hard, split):
     sched.close()
 
 
+@pytest.mark.parametrize("chunk,split", [(64, 0), (128, 2), (256, 0), (256, 3)])
+def test_hard_easy_stack_short_chunks(chunk, split):
+    """Hard layers whose bundles use shorter chunks (more, shorter decode chains: the decoder's
+    16-wave workgroups at 256-symbol chunks), on the whole chip or a persistent grid of `split`
+    workgroups: the same bits as the plain step of the default encoding, two steps in a row."""
+    t = torch()
+    from lossless_bf16_weight_amd.stack import HardEasyStack, MLPStack
+    rng = np.random.default_rng(23)
+    hidden, inter, layers, m = 256, 704, 3, 16
+    mats = [(synth.small_gaussian(inter, hidden, seed=300 + 3 * l, plant_frac=0.02)["w"],
+             synth.gaussian_bf16(rng, (inter, hidden), 0.03),
+             synth.student_t_bf16(rng, (hidden, inter), 3, 0.02)) for l in range(layers)]
+    plain = MLPStack(m, hidden, inter)
+    for lay in mats:
+        plain.add_layer(*lay)
+    sched = HardEasyStack(m, hidden, inter, mats, hard_layers=(0, 1, 2), chunk=chunk, decode_workgroups=split)
+    assert all(uw.uw_blob_info(cm.blob)["chunk"] == chunk for lay in sched.layers for cm in lay)
+    x = dev_u16(synth.gaussian_bf16(rng, (m, hidden), 1.0))
+    xa, xb = x.clone(), x.clone()
+    for step in range(2):
+        a = plain.step(xa, pipeline=uw.UW_PIPE_DIRECT_PALETTE, fused=True).clone()
+        b = sched.step(xb).clone()
+        assert t.equal(a, b), "chunk=%d split=%d step %d" % (chunk, split, step)
+        xa, xb = a, b
+    sched.close()
+
+
 def bf16_key(bits):
     """Monotone integer key of BF16 bit patterns (adjacent keys = adjacent values; +0 and -0
     share key 0)."""
