@@ -426,6 +426,10 @@ template <int CT, int U>
 struct MtCfg {
   static constexpr int kGpr = U * 8;                      // granules per X row of a batch
   static constexpr int kSwz = (kGpr - 1) < 15 ? (kGpr - 1) : 15;
+  // Position of X row m's granules: rows of 256 bytes or more span all 64 banks, so 16
+  // consecutive rows XOR their granule index with m & 15; 128-byte rows (one-block batches)
+  // cover half the banks, so rows m and m + 8 would collide: there the XOR takes m >> 1.
+  __host__ __device__ static constexpr int swz(int m) { return kGpr >= 16 ? (m & kSwz) : ((m >> 1) & kSwz); }
   static constexpr int kRows = 16 * CT;
   static constexpr int kBufBytes = kRows * kGpr * 16;     // one X batch
   static constexpr int kDmas = kRows * kGpr / 64;         // 1 KB LDS-DMA instructions per batch
@@ -512,7 +516,7 @@ __global__ __launch_bounds__(64 * R) void k_gemm_mt(GemmArgs a, float* part, int
     for (int jj = 0; jj < C::kDmas / R; ++jj) {
       const int j = wave + jj * R;
       const int m = j * kRowsPerDma + lane / C::kGpr;
-      const int q = (lane % C::kGpr) ^ (m & C::kSwz);
+      const int q = (lane % C::kGpr) ^ C::swz(m);
       const int blk = bb + (q >> 3);
       const uint32_t voff = (m < mv && blk < be) ? (uint32_t)(m * a.k + blk * 64 + (q & 7) * 8) * 2 : kOob;
       lds_dma16(xrs, buf + j * 1024, voff);
@@ -589,7 +593,7 @@ __global__ __launch_bounds__(64 * R) void k_gemm_mt(GemmArgs a, float* part, int
   for (int c = 0; c < CT; ++c) acc[c] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < (kTwo ? CT : 1); ++c) acc2[c] = floatx4{0.f, 0.f, 0.f, 0.f};
-  const int sw = r & C::kSwz;
+  const int sw = C::swz(r);
   // LDS byte offsets of this lane's X fragments in a batch (block u, MFMA step k2), column
   // tile 0: tile c adds the constant 16 * c * kGpr * 16 (the swizzle depends on r only).
   uint32_t xoff[U][2];
@@ -806,7 +810,7 @@ __global__ __launch_bounds__(64 * R) void k_gemm_wide(GemmArgs a, float* part, i
     for (int jj = 0; jj < C::kDmas / R; ++jj) {
       const int j = wave + jj * R;
       const int m = j * kRowsPerDma + lane / C::kGpr;
-      const int q = (lane % C::kGpr) ^ (m & C::kSwz);
+      const int q = (lane % C::kGpr) ^ C::swz(m);
       const int blk = bb + (q >> 3);
       const uint32_t voff = (m < mv && blk < be) ? (uint32_t)(m * a.k + blk * 64 + (q & 7) * 8) * 2 : kOob;
       lds_dma16(xrs, buf + j * 1024, voff);
@@ -875,7 +879,7 @@ __global__ __launch_bounds__(64 * R) void k_gemm_wide(GemmArgs a, float* part, i
   for (int u = 0; u < U; ++u)
 #pragma unroll
     for (int st = 0; st < 4; ++st)
-      xoff[u][st] = (uint32_t)(xr * C::kGpr + ((u * 8 + 4 * h + st) ^ (xr & C::kSwz))) * 16u;
+      xoff[u][st] = (uint32_t)(xr * C::kGpr + ((u * 8 + 4 * h + st) ^ C::swz(xr))) * 16u;
   // One block: rebuild the lane's 32 weights, then 4 * CW MFMAs (4 k-steps x CW column tiles).
   auto mma_block = [&](int b, int u, const WideSlot<SRC>& sl, const uint8_t* xbuf) {
     const uint32_t f0 = __builtin_amdgcn_readlane(wfl[0], b - bs), f1 = __builtin_amdgcn_readlane(wfl[1], b - bs);
@@ -974,6 +978,242 @@ __global__ __launch_bounds__(64 * R) void k_gemm_wide(GemmArgs a, float* part, i
   }
 }
 
+// =========================================================================================
+// Big-tile reconstructive GEMM for large batches (palette sources).
+//
+// The wide-tile kernel rebuilds a wave's weights for every 128-column X chunk, so at M in the
+// hundreds the rebuild runs M/128 times over and its X reads from LDS feed only 32 weight
+// rows.  Here a workgroup of four waves owns a BN x BM output tile (BN = 64 WN weight rows,
+// BM = 64 WM X rows) and walks K one 64-column block at a time: the block's BN weight rows are
+// rebuilt once, by the whole workgroup, into LDS as BF16, its BM X rows are staged by
+// LDS-DMA, and each wave multiplies one (BN/2) x (BM/2) quarter with 32x32x16 MFMAs, both
+// operands read from LDS.  Two blocks deep: while one block is multiplied, the next one's
+// rebuilt weights and X rows are ready or landing and the one after is requested; one barrier
+// a block.  LDS rows are 128 bytes (64 BF16), half the 64 banks; the 16-byte granule g of row
+// r sits at position g ^ ((r >> 1) & 7), so any 16 consecutive rows' reads or writes of one
+// granule hit 16 different 4-bank groups (rows r and r + 8 would share them under g ^ (r & 7)).
+// Weight rows: wave w rebuilds tiles w*TW .. w*TW+TW-1 of the workgroup's BN/16, lane
+// (r, g) the 16 weights it owns in the stored layout (row r, k = 16 g .. 16 g + 15) --
+// the same loads and rebuild as the per-tile kernel, written out row-major.
+// =========================================================================================
+template <int SRC>
+struct BigW {
+  WRegs<SRC> w;
+  u32x4 ev;
+};
+
+template <int SRC, int WN, int WM>
+__global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a, float* part, int S) {
+  static_assert(SRC <= SRC_PAL_LUT, "palette sources only");
+  constexpr int BN = 64 * WN, BM = 64 * WM;
+  constexpr int TW = BN / 64;                 // tiles a wave rebuilds
+  constexpr int ABYTES = BN * 128, BBYTES = BM * 128;
+  constexpr int XD = BM / 32;                 // X DMAs (1 KB) a wave issues per block
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const int tiles = (a.n + 15) >> 4;
+  const int rg = blockIdx.x, s = blockIdx.y;
+  const int mcol0 = blockIdx.z * BM;
+  const int mv = min(BM, a.m - mcol0);
+  const int bs = (int)((int64_t)s * a.kb / S), be = (int)((int64_t)(s + 1) * a.kb / S);
+  const int nblk = be - bs;                   // <= 64: one block per lane in the flag registers
+
+  // This wave's weight tiles: streams, flags of the slice (block bs + j in lane j), verbatim
+  // ranks of each block's first segment relative to the tile's verbatim base.
+  __amdgpu_buffer_rsrc_t srs[TW], irs[TW], vrs[TW];
+  uint32_t so[TW], io[TW], wfl[TW], wvp[TW];
+#pragma unroll
+  for (int j = 0; j < TW; ++j) {
+    const int t = rg * (BN / 16) + wave * TW + j;
+    const bool ok = t < tiles;
+    const size_t tb = ok ? (size_t)t * a.k * 16 : 0;
+    srs[j] = make_rsrc(a.sm + tb, ok ? (uint32_t)a.k * 16 : 0u);
+    irs[j] = make_rsrc(a.aux + tb / 2, ok ? (uint32_t)a.k * 8 : 0u);
+    so[j] = ok ? (uint32_t)lane * 16 : kOob;
+    io[j] = ok ? (uint32_t)lane * 8 : kOob;
+    const __amdgpu_buffer_rsrc_t frs = make_rsrc(a.flags + (ok ? (size_t)t * a.kb : 0), ok ? (uint32_t)a.kb * 2 : 0u);
+    wfl[j] = __builtin_amdgcn_raw_buffer_load_b16(frs, lane < nblk ? (uint32_t)(bs + lane) * 2 : kOob, 0, 0);
+    uint32_t before = 0;
+    for (int c0 = 0; c0 < bs; c0 += 64) {
+      const int b = c0 + lane;
+      before += __popc((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(frs, b < bs ? (uint32_t)b * 2 : kOob, 0, 0));
+    }
+    before = wave_sum(before);
+    const int tv = ok ? t : 0;
+    const uint32_t v0 = a.vprefix[tv];
+    const uint32_t nv = ok ? a.vprefix[tv + 1] - v0 : 0u;
+    vrs[j] = make_rsrc(a.vexp + (size_t)v0 * 64, nv * 64);
+    uint32_t tot;
+    wvp[j] = before + wave_excl_prefix_small<5>((uint32_t)__popc(wfl[j]), &tot);
+  }
+
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.x + (size_t)mcol0 * a.k, (uint32_t)max(mv, 0) * a.k * 2);
+  auto issue_x = [&](int b, uint8_t* buf) {
+#pragma unroll
+    for (int jj = 0; jj < XD; ++jj) {
+      const int p = (wave * XD + jj) * 64 + lane;            // destination granule
+      const int row = p >> 3, gs = (p & 7) ^ ((row >> 1) & 7);   // its source granule
+      const uint32_t voff = (row < mv && b < be) ? (uint32_t)(row * a.k + b * 64 + gs * 8) * 2 : kOob;
+      lds_dma16(xrs, buf + (wave * XD + jj) * 1024, voff);
+    }
+  };
+  // Past the slice's last block the loads are issued all the same, out of range (zeros, no
+  // traffic): every iteration issues the same NL instructions, so the compiler's and our
+  // in-order vmcnt counts hold on every path.
+  auto load_block = [&](int b, BigW<SRC> (&sl)[TW]) {
+    const bool ok = b < be;
+    const int jb = ok ? b - bs : 0;
+#pragma unroll
+    for (int j = 0; j < TW; ++j) {
+      sl[j].w.s = bload16_nt(srs[j], ok ? so[j] : kOob, b * 1024);
+      sl[j].w.i = bload8_nt(irs[j], ok ? io[j] : kOob, b * 512);
+    }
+#pragma unroll
+    for (int j = 0; j < TW; ++j) {
+      const uint32_t f = ok ? __builtin_amdgcn_readlane(wfl[j], jb) : 0u;
+      const uint32_t rank = __builtin_amdgcn_readlane(wvp[j], jb) + (uint32_t)__popc(f & ((1u << r) - 1u));
+      sl[j].ev = bload16(vrs[j], ((f >> r) & 1u) ? rank * 64 + g * 16 : kOob);
+    }
+  };
+  auto rebuild_to_lds = [&](int b, const BigW<SRC> (&sl)[TW], uint8_t* buf) {
+#pragma unroll
+    for (int j = 0; j < TW; ++j) {
+      const uint32_t f = b < be ? __builtin_amdgcn_readlane(wfl[j], b - bs) : 0u;
+      u32x4 A0, A1;
+      rebuild_block<SRC>(a, sl[j].w, f, f, r, sl[j].ev, A0, A1);
+      const int row = (wave * TW + j) * 16 + r;
+      *reinterpret_cast<u32x4*>(buf + row * 128 + (((2 * g) ^ ((row >> 1) & 7)) * 16)) = A0;
+      *reinterpret_cast<u32x4*>(buf + row * 128 + (((2 * g + 1) ^ ((row >> 1) & 7)) * 16)) = A1;
+    }
+  };
+
+  const int wn = wave >> 1, wm = wave & 1;
+  const int xr = lane & 31, hh = lane >> 5;
+  floatx16 acc[WN][WM];
+#pragma unroll
+  for (int p = 0; p < WN; ++p)
+#pragma unroll
+    for (int c = 0; c < WM; ++c)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[p][c][e] = 0.f;
+  // The operands of k-step st + 1 are read from LDS before the MFMAs of step st are issued.
+  auto load_frags = [&](const uint8_t* A, const uint8_t* B, int st, u32x4 (&av)[WN], u32x4 (&bv)[WM]) {
+    const int gr = 2 * st + hh;
+#pragma unroll
+    for (int p = 0; p < WN; ++p) {
+      const int row = wn * 32 * WN + p * 32 + xr;
+      av[p] = *reinterpret_cast<const u32x4*>(A + row * 128 + ((gr ^ ((row >> 1) & 7)) * 16));
+    }
+#pragma unroll
+    for (int c = 0; c < WM; ++c) {
+      const int row = wm * 32 * WM + c * 32 + xr;
+      bv[c] = *reinterpret_cast<const u32x4*>(B + row * 128 + ((gr ^ ((row >> 1) & 7)) * 16));
+    }
+  };
+  auto compute = [&](const uint8_t* A, const uint8_t* B) {
+    u32x4 av0[WN], bv0[WM], av1[WN], bv1[WM];
+    load_frags(A, B, 0, av0, bv0);
+    static_for<0, 4>([&](auto sc) {
+      constexpr int st = decltype(sc)::value;
+      u32x4 (&av)[WN] = (st & 1) ? av1 : av0;
+      u32x4 (&bv)[WM] = (st & 1) ? bv1 : bv0;
+      if constexpr (st + 1 < 4) {
+        if constexpr (st & 1) load_frags(A, B, st + 1, av0, bv0);
+        else load_frags(A, B, st + 1, av1, bv1);
+      }
+#pragma unroll
+      for (int p = 0; p < WN; ++p)
+#pragma unroll
+        for (int c = 0; c < WM; ++c)
+          acc[p][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[p]),
+                                                              __builtin_bit_cast(bf16x8, bv[c]), acc[p][c], 0, 0, 0);
+    });
+  };
+  // LDS-only barrier: each wave has already waited for its own loads and DMAs where needed.
+  auto barrier = [&]() {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(63) & ~0x0F00);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  // Pipeline two blocks deep: block i is multiplied from A buffer i % 2 and the current X
+  // buffer while block i + 1's weights (registers) and X rows (the next X buffer) are in
+  // flight or in place and block i + 2's are requested; three X buffers rotate, two register
+  // sets alternate (the loop is unrolled by two for them).  A wave's loads of one block are
+  // NL instructions, so before rebuilding block i + 1 it waits until at most block i + 2's
+  // NL are outstanding (loads retire in order): that also covers its X DMAs of block i + 1,
+  // which the barrier closing the half-iteration then publishes to the other waves.  Blocks
+  // past the slice are loaded out of range and rebuilt into a buffer no one multiplies.
+  constexpr int NL = XD + 3 * TW;
+  uint8_t* const abuf0 = smem;
+  uint8_t* const abuf1 = smem + ABYTES;
+  uint8_t* xcur = smem + 2 * ABYTES;
+  uint8_t* xnext = xcur + BBYTES;
+  uint8_t* xfree = xnext + BBYTES;
+  auto rotate = [&]() {
+    uint8_t* const t = xcur;
+    xcur = xnext;
+    xnext = xfree;
+    xfree = t;
+  };
+  BigW<SRC> sla[TW], slb[TW];
+  issue_x(bs, xcur);
+  load_block(bs, sla);
+  issue_x(bs + 1, xnext);
+  load_block(bs + 1, slb);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(NL));
+  rebuild_to_lds(bs, sla, abuf0);
+  barrier();
+  for (int i = 0; i < nblk; i += 2) {
+    issue_x(bs + i + 2, xfree);                 // block i + 2 (sla: block i was rebuilt)
+    load_block(bs + i + 2, sla);
+    compute(abuf0, xcur);                       // block i
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(NL));
+    rebuild_to_lds(bs + i + 1, slb, abuf1);     // block i + 1
+    barrier();
+    rotate();
+    issue_x(bs + i + 3, xfree);                 // block i + 3 (slb: block i + 1 was rebuilt)
+    load_block(bs + i + 3, slb);
+    if (i + 1 < nblk) compute(abuf1, xcur);     // block i + 1
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(NL));
+    rebuild_to_lds(bs + i + 2, sla, abuf0);     // block i + 2
+    barrier();
+    rotate();
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));    // the out-of-range requests past the slice
+
+  // D lane layout (32x32): X row (column of D) lane % 32 of column tile c; register e holds
+  // weight row 8 (e / 4) + 4 hh + e % 4 of row pair p.
+#pragma unroll
+  for (int p = 0; p < WN; ++p)
+#pragma unroll
+    for (int c = 0; c < WM; ++c) {
+      const int mm = mcol0 + wm * 32 * WM + c * 32 + xr;
+      if (mm >= a.m) continue;
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const int n0 = rg * BN + wn * 32 * WN + p * 32 + 8 * qd + 4 * hh;
+        if (n0 >= a.n) continue;
+        const floatx4 v{acc[p][c][4 * qd], acc[p][c][4 * qd + 1], acc[p][c][4 * qd + 2], acc[p][c][4 * qd + 3]};
+        if (!part) {
+          store_out4(a, mm, n0, v);
+          continue;
+        }
+        float* yp = part + (size_t)s * a.m * a.n + (size_t)mm * a.n + n0;
+        if (n0 + 3 < a.n && (a.n & 3) == 0) {
+          *reinterpret_cast<floatx4*>(yp) = v;
+        } else {
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            if (n0 + jj < a.n) yp[jj] = v[jj];
+        }
+      }
+    }
+}
+
 // y[i] = sum over s of part[s][i], in slice order.  A thread owns 4 consecutive elements
 // and requests all S slices' values before adding them, so the loads overlap.
 // With gate set, the sum goes through the SwiGLU epilogue into h instead of y.
@@ -1051,7 +1291,9 @@ __global__ __launch_bounds__(1024) void k_reduce_rmsnorm(const float* part, floa
 // blocks in LDS, K split over workgroups), kind 2 = per-tile kernel with shared X (`waves`
 // whole tiles a workgroup, all X rows in LDS once; M <= 16, k <= 4096, palette sources),
 // kind 3 = wide-tile kernel (`waves` tile pairs a workgroup, 128 X rows a chunk, batches of
-// `unroll` blocks; palette sources, other sources run the default multi-tile variant).
+// `unroll` blocks; palette sources, other sources run the default multi-tile variant),
+// kind 4 = big-tile kernel (64 * `waves` weight rows x 64 * `unroll` X rows a workgroup, W
+// rebuilt once a block into LDS; palette sources, others run the default multi-tile variant).
 struct Variant {
   int kind;
   int waves;
@@ -1059,7 +1301,7 @@ struct Variant {
 };
 static const Variant kVariants[] = {{0, 4, 8}, {0, 2, 8}, {0, 8, 8},  {0, 16, 8}, {0, 1, 8}, {0, 4, 4}, {0, 2, 4},
                                     {0, 8, 4}, {0, 16, 4}, {0, 1, 4}, {1, 8, 4},  {1, 4, 4}, {1, 8, 2}, {1, 4, 2},
-                                    {2, 2, 4}, {2, 4, 4}, {3, 4, 2}, {3, 8, 2}};
+                                    {2, 2, 4}, {2, 4, 4}, {3, 4, 2}, {3, 8, 2}, {4, 2, 2}, {4, 2, 4}};
 static constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 static constexpr int kMtDefault = 10;   // {1, 8, 4}
 
@@ -1102,10 +1344,22 @@ static int wide_slices(int64_t tiles, int R, int64_t kb, int m) {
   const int64_t groups = ((tiles + 1) / 2 + R - 1) / R;
   return (int)slices_for(groups * R * wide_chunks(m), kb);
 }
-// Upper bound of mt_slices and wide_slices over the wave counts R (groups * R >= tiles or
-// tile pairs).
+// Big-tile kernel: K slices so that the workgroups fill the chip once (one a compute unit at
+// 128 KB of LDS, two at 80 KB), at most 64 blocks a slice.
+static int big_slices(int64_t tiles, int WN, int WM, int64_t kb, int m) {
+  const int64_t wgs = ((tiles * 16 + 64 * WN - 1) / (64 * WN)) * ((m + 64 * WM - 1) / (64 * WM));
+  const int64_t per_cu = (2 * 64 * WN + 3 * 64 * WM) * 128 <= 80 * 1024 ? 2 : 1;   // LDS a workgroup
+  int64_t S = std::max<int64_t>(1, 256 * per_cu / std::max<int64_t>(wgs, 1));
+  S = std::min<int64_t>(S, std::min<int64_t>(kb, kMaxSlices));
+  return (int)std::max<int64_t>(S, (kb + 63) / 64);
+}
+// Upper bound of mt_slices, wide_slices and big_slices over the variants (groups * R >= tiles
+// or tile pairs).
 int64_t mt_max_slices(int64_t kb, int64_t tiles, int m) {
-  return std::max(slices_for(tiles * m_chunks(m), kb), slices_for((tiles + 1) / 2 * wide_chunks(m), kb));
+  int64_t S = std::max(slices_for(tiles * m_chunks(m), kb), slices_for((tiles + 1) / 2 * wide_chunks(m), kb));
+  for (int v = 0; v < kNumVariants; ++v)
+    if (kVariants[v].kind == 4) S = std::max<int64_t>(S, big_slices(tiles, kVariants[v].waves, kVariants[v].unroll, kb, m));
+  return S;
 }
 
 // Adds the S > 1 K-slice partial sums into y (or through the SwiGLU epilogue into h, or
@@ -1189,6 +1443,21 @@ static hipError_t launch_wide_t(const GemmArgs& a, int64_t tiles, int S, float* 
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
   return launch_reduce(a, S, part, s);
+}
+
+template <int SRC, int WN, int WM>
+static hipError_t launch_big_t(const GemmArgs& a, int64_t tiles, int S, float* part, hipStream_t s) {
+  const dim3 grid((unsigned)((tiles * 16 + 64 * WN - 1) / (64 * WN)), (unsigned)S, (unsigned)((a.m + 64 * WM - 1) / (64 * WM)));
+  hipLaunchKernelGGL((k_gemm_big<SRC, WN, WM>), grid, dim3(256), 128 * (2 * 64 * WN + 3 * 64 * WM), s, a,
+                     S > 1 ? part : nullptr, S);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess || S == 1) return e;
+  return launch_reduce(a, S, part, s);
+}
+
+template <int SRC>
+static hipError_t launch_big(const GemmArgs& a, int64_t tiles, int WM, int S, float* part, hipStream_t s) {
+  return WM == 4 ? launch_big_t<SRC, 2, 4>(a, tiles, S, part, s) : launch_big_t<SRC, 2, 2>(a, tiles, S, part, s);
 }
 
 // Batches of 2 blocks only: 4 would spill at 8 waves a workgroup.
@@ -1278,11 +1547,12 @@ int plan_gemm(int src, const GemmArgs& a, int64_t tiles, int* variant, const flo
   const int ct = col_tiles(a.m);
   const bool pal = src <= SRC_PAL_LUT;
   if (*variant < 0) *variant = a.m > 16 ? kMtDefault : default_variant(tiles, a.kb, ct, a.m);
-  if (kVariants[*variant].kind == 3 && !pal) *variant = kMtDefault;
+  if (kVariants[*variant].kind >= 3 && !pal) *variant = kMtDefault;
   const int kind = kVariants[*variant].kind;
-  if (kind != 1 && kind != 3) return 0;
+  if (kind != 1 && kind != 3 && kind != 4) return 0;
   const int R = kVariants[*variant].waves;
-  int S = kind == 3 ? wide_slices(tiles, R, a.kb, a.m) : mt_slices(tiles, R, a.kb, a.m);
+  int S = kind == 4 ? big_slices(tiles, R, kVariants[*variant].unroll, a.kb, a.m)
+                    : kind == 3 ? wide_slices(tiles, R, a.kb, a.m) : mt_slices(tiles, R, a.kb, a.m);
   const size_t plane = (size_t)a.m * a.n * sizeof(float);
   if (S > 1 && (!part || part_bytes < (size_t)S * plane))
     S = part ? (int)std::min<size_t>(part_bytes / plane, (size_t)S) : 1;
@@ -1311,6 +1581,13 @@ uw_status run_gemm(int src, const GemmArgs& a, int64_t tiles, int variant, float
                           size_t part_bytes, hipStream_t s) {
   int ct = col_tiles(a.m);
   const int S = plan_gemm(src, a, tiles, &variant, part, part_bytes);
+  if (S > 0 && kVariants[variant].kind == 4) {
+    const int WM = kVariants[variant].unroll;
+    const hipError_t e = src == SRC_PAL_AFFINE ? launch_big<SRC_PAL_AFFINE>(a, tiles, WM, S, part, s)
+                                               : launch_big<SRC_PAL_LUT>(a, tiles, WM, S, part, s);
+    if (e != hipSuccess) return fail(UW_E_HIP, "gemm launch: %s", hipGetErrorString(e));
+    return UW_OK;
+  }
   if (S > 0 && kVariants[variant].kind == 3) {
     const int R = kVariants[variant].waves;
     const hipError_t e = src == SRC_PAL_AFFINE ? launch_wide<SRC_PAL_AFFINE>(a, tiles, R, S, part, s)
@@ -1388,6 +1665,9 @@ const char* uw_variant_name(int32_t variant) {
   else if (kVariants[variant].kind == 3)
     snprintf(names[variant], sizeof(names[variant]), "wide pairs=%d unroll=%d", kVariants[variant].waves,
              kVariants[variant].unroll);
+  else if (kVariants[variant].kind == 4)
+    snprintf(names[variant], sizeof(names[variant]), "big tile=%dx%d", 64 * kVariants[variant].waves,
+             64 * kVariants[variant].unroll);
   else
     snprintf(names[variant], sizeof(names[variant]), "multitile tiles=%d unroll=%d", kVariants[variant].waves,
              kVariants[variant].unroll);

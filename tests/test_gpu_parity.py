@@ -178,9 +178,10 @@ def test_caller_palette_end_to_end(shift, swap):
             check_gemm(y, x, w)
 
 
-N_VARIANTS = 18
+N_VARIANTS = 20
 SHARED_X_VARIANTS = (14, 15)   # kind 2: whole tiles per wave, X rows shared in LDS
 WIDE_VARIANTS = (16, 17)       # kind 3: tile pairs per wave, 32x32 MFMAs (palette sources)
+BIG_VARIANTS = (18, 19)        # kind 4: W rebuilt once a block into LDS, 32x32 MFMAs (palette sources)
 
 
 def test_variant_count():
@@ -246,6 +247,34 @@ def test_gemm_wide_tiles(variant, case):
     assert uw.uw_variant_name(variant).startswith("wide ")
     for m in (17, 128, 129, 300):
         x = synth.gaussian_bf16(np.random.default_rng(900 + m), (m, k), 1.0)
+        for pipe in (uw.UW_PIPE_DIRECT_PALETTE, uw.UW_PIPE_TRANSCODE):
+            for ws in (None, cm.workspace(m, pipe)):
+                if pipe == uw.UW_PIPE_TRANSCODE and ws is None:
+                    continue
+                y = t.full((m, n), float("nan"), dtype=t.float32, device="cuda")
+                uw.uw_gemm_variant(cm.d, dev_u16(x), y, m, pipe, variant, ws)
+                if ws is not None:
+                    uw.uw_check(ws)
+                check_gemm(y, x, w)
+
+
+@pytest.mark.parametrize("variant", BIG_VARIANTS)
+@pytest.mark.parametrize("case", ["ragged_rows", "lut_palette", "long_k"])
+def test_gemm_big_tiles(variant, case):
+    """The big-tile kernel (the workgroup rebuilds each block's weight rows once into LDS,
+    32x32 MFMAs on LDS operands): a row count that leaves the last workgroup's rows partly
+    empty and ragged, the table-lookup palette, and k = 9216 (several K slices and flag words
+    past the first 64 blocks), with and without room for the partial sums, across one, two
+    and three column chunks of 256 X rows and ragged last chunks."""
+    t = torch()
+    w = {"ragged_rows": lambda: synth.small_gaussian(200, 2048, seed=29, plant_frac=0.05)["w"],
+         "lut_palette": lambda: bimodal(96, 512, 6),
+         "long_k": lambda: synth.small_gaussian(70, 9216, seed=31, plant_frac=0.1)["w"]}[case]()
+    n, k = w.shape
+    cm = uw.CompressedMatrix(w)
+    assert uw.uw_variant_name(variant).startswith("big ")
+    for m in (17, 256, 257, 600):
+        x = synth.gaussian_bf16(np.random.default_rng(700 + m), (m, k), 1.0)
         for pipe in (uw.UW_PIPE_DIRECT_PALETTE, uw.UW_PIPE_TRANSCODE):
             for ws in (None, cm.workspace(m, pipe)):
                 if pipe == uw.UW_PIPE_TRANSCODE and ws is None:

@@ -277,7 +277,7 @@ def test_autotune_variant_entries(tmp_path):
 def test_variant_names():
     n = uw.uw_variant_count()
     assert n >= 4
-    assert all(uw.uw_variant_name(v).startswith(("waves=", "multitile ", "shared-x ", "wide ")) for v in range(n))
+    assert all(uw.uw_variant_name(v).startswith(("waves=", "multitile ", "shared-x ", "wide ", "big ")) for v in range(n))
     assert any(uw.uw_variant_name(v).startswith("multitile ") for v in range(n))
     assert uw.uw_variant_name(n) == ""
 
