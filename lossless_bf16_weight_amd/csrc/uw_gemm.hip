@@ -438,7 +438,7 @@ struct MtCfg {
 // Rebuild the lane's 16 weights of one block as two bf16x8 MFMA operands.  fany: nonzero
 // (wave-uniform) when some row the wave rebuilds has a verbatim segment in this block; f:
 // the verbatim flags of the lane's own tile (bit r: its row).
-template <int SRC>
+template <int SRC, bool kNoBranch = false>
 __device__ __forceinline__ void rebuild_block(const GemmArgs& a, const WRegs<SRC>& w, uint32_t fany, uint32_t f,
                                               int r, const u32x4& ev, u32x4& A0, u32x4& A1) {
   if constexpr (SRC == SRC_BF16) {
@@ -457,7 +457,7 @@ __device__ __forceinline__ void rebuild_block(const GemmArgs& a, const WRegs<SRC
       exps_raw(w.e.z, w.e.w, T1);
     }
     if constexpr (SRC <= SRC_PAL_LUT) {
-      if (fany) {
+      if (kNoBranch || fany) {   // unbranched: the select keeps T where the lane's segment is coded
         uint32_t R0[4], R1[4];
         exps_raw(ev.x, ev.y, R0);
         exps_raw(ev.z, ev.w, R1);
@@ -1002,7 +1002,7 @@ struct BigW {
   u32x4 ev;
 };
 
-template <int SRC, int WN, int WM>
+template <int SRC, int WN, int WM, int D>
 __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a, float* part, int S) {
   static_assert(SRC <= SRC_PAL_LUT, "palette sources only");
   constexpr int BN = 64 * WN, BM = 64 * WM;
@@ -1020,19 +1020,25 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a, float* part, int S
   const int bs = (int)((int64_t)s * a.kb / S), be = (int)((int64_t)(s + 1) * a.kb / S);
   const int nblk = be - bs;                   // <= 64: one block per lane in the flag registers
 
-  // This wave's weight tiles: streams, flags of the slice (block bs + j in lane j), verbatim
-  // ranks of each block's first segment relative to the tile's verbatim base.
-  __amdgpu_buffer_rsrc_t srs[TW], irs[TW], vrs[TW];
+  // This wave's weight tiles t0w .. t0w + TW - 1 (nt of them inside the matrix) are
+  // consecutive, so one buffer resource covers their sm streams, one their index streams and
+  // one their verbatim exponents; per tile: stream offsets, flags of the slice (block bs + j
+  // in lane j), and the verbatim rank of each block's first segment relative to the first
+  // tile's verbatim base.
+  const int t0w = rg * (BN / 16) + wave * TW;
+  const int nt = max(0, min(TW, tiles - t0w));
+  const size_t tb0 = nt ? (size_t)t0w * a.k * 16 : 0;
+  const __amdgpu_buffer_rsrc_t srs = make_rsrc(a.sm + tb0, (uint32_t)nt * a.k * 16);
+  const __amdgpu_buffer_rsrc_t irs = make_rsrc(a.aux + tb0 / 2, (uint32_t)nt * a.k * 8);
+  const uint32_t vbase = a.vprefix[nt ? t0w : 0];
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(a.vexp + (size_t)vbase * 64, (a.vprefix[nt ? t0w + nt : 0] - vbase) * 64);
   uint32_t so[TW], io[TW], wfl[TW], wvp[TW];
 #pragma unroll
   for (int j = 0; j < TW; ++j) {
-    const int t = rg * (BN / 16) + wave * TW + j;
-    const bool ok = t < tiles;
-    const size_t tb = ok ? (size_t)t * a.k * 16 : 0;
-    srs[j] = make_rsrc(a.sm + tb, ok ? (uint32_t)a.k * 16 : 0u);
-    irs[j] = make_rsrc(a.aux + tb / 2, ok ? (uint32_t)a.k * 8 : 0u);
-    so[j] = ok ? (uint32_t)lane * 16 : kOob;
-    io[j] = ok ? (uint32_t)lane * 8 : kOob;
+    const int t = t0w + j;
+    const bool ok = j < nt;
+    so[j] = ok ? (uint32_t)(j * a.k * 16 + lane * 16) : kOob;
+    io[j] = ok ? (uint32_t)(j * a.k * 8 + lane * 8) : kOob;
     const __amdgpu_buffer_rsrc_t frs = make_rsrc(a.flags + (ok ? (size_t)t * a.kb : 0), ok ? (uint32_t)a.kb * 2 : 0u);
     wfl[j] = __builtin_amdgcn_raw_buffer_load_b16(frs, lane < nblk ? (uint32_t)(bs + lane) * 2 : kOob, 0, 0);
     uint32_t before = 0;
@@ -1041,16 +1047,13 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a, float* part, int S
       before += __popc((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(frs, b < bs ? (uint32_t)b * 2 : kOob, 0, 0));
     }
     before = wave_sum(before);
-    const int tv = ok ? t : 0;
-    const uint32_t v0 = a.vprefix[tv];
-    const uint32_t nv = ok ? a.vprefix[tv + 1] - v0 : 0u;
-    vrs[j] = make_rsrc(a.vexp + (size_t)v0 * 64, nv * 64);
+    const uint32_t v0 = ok ? a.vprefix[t] - vbase : 0u;
     uint32_t tot;
-    wvp[j] = before + wave_excl_prefix_small<5>((uint32_t)__popc(wfl[j]), &tot);
+    wvp[j] = v0 + before + wave_excl_prefix_small<5>((uint32_t)__popc(wfl[j]), &tot);
   }
 
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.x + (size_t)mcol0 * a.k, (uint32_t)max(mv, 0) * a.k * 2);
-  auto issue_x = [&](int b, uint8_t* buf) {
+  auto issue_x = [&](int b, uint8_t* buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int jj = 0; jj < XD; ++jj) {
       const int p = (wave * XD + jj) * 64 + lane;            // destination granule
@@ -1062,27 +1065,30 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a, float* part, int S
   // Past the slice's last block the loads are issued all the same, out of range (zeros, no
   // traffic): every iteration issues the same NL instructions, so the compiler's and our
   // in-order vmcnt counts hold on every path.
-  auto load_block = [&](int b, BigW<SRC> (&sl)[TW]) {
+  auto load_block = [&](int b, BigW<SRC> (&sl)[TW]) __attribute__((always_inline)) {
     const bool ok = b < be;
     const int jb = ok ? b - bs : 0;
 #pragma unroll
     for (int j = 0; j < TW; ++j) {
-      sl[j].w.s = bload16_nt(srs[j], ok ? so[j] : kOob, b * 1024);
-      sl[j].w.i = bload8_nt(irs[j], ok ? io[j] : kOob, b * 512);
+      sl[j].w.s = bload16_nt(srs, ok ? so[j] : kOob, b * 1024);
+      sl[j].w.i = bload8_nt(irs, ok ? io[j] : kOob, b * 512);
     }
+    // Masks, not branches: the multiply and rebuild of a block stay one basic block.
+    const uint32_t okm = 0u - (uint32_t)ok;
 #pragma unroll
     for (int j = 0; j < TW; ++j) {
-      const uint32_t f = ok ? __builtin_amdgcn_readlane(wfl[j], jb) : 0u;
+      const uint32_t f = __builtin_amdgcn_readlane(wfl[j], jb) & okm;
       const uint32_t rank = __builtin_amdgcn_readlane(wvp[j], jb) + (uint32_t)__popc(f & ((1u << r) - 1u));
-      sl[j].ev = bload16(vrs[j], ((f >> r) & 1u) ? rank * 64 + g * 16 : kOob);
+      const uint32_t vm = 0u - ((f >> r) & 1u);
+      sl[j].ev = bload16(vrs, ((rank * 64 + g * 16) & vm) | (kOob & ~vm));
     }
   };
-  auto rebuild_to_lds = [&](int b, const BigW<SRC> (&sl)[TW], uint8_t* buf) {
+  auto rebuild_to_lds = [&](int b, const BigW<SRC> (&sl)[TW], uint8_t* buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < TW; ++j) {
-      const uint32_t f = b < be ? __builtin_amdgcn_readlane(wfl[j], b - bs) : 0u;
+      const uint32_t f = __builtin_amdgcn_readlane(wfl[j], b < be ? b - bs : 0) & (0u - (uint32_t)(b < be));
       u32x4 A0, A1;
-      rebuild_block<SRC>(a, sl[j].w, f, f, r, sl[j].ev, A0, A1);
+      rebuild_block<SRC, true>(a, sl[j].w, f, f, r, sl[j].ev, A0, A1);
       const int row = (wave * TW + j) * 16 + r;
       *reinterpret_cast<u32x4*>(buf + row * 128 + (((2 * g) ^ ((row >> 1) & 7)) * 16)) = A0;
       *reinterpret_cast<u32x4*>(buf + row * 128 + (((2 * g + 1) ^ ((row >> 1) & 7)) * 16)) = A1;
@@ -1099,7 +1105,7 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a, float* part, int S
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[p][c][e] = 0.f;
   // The operands of k-step st + 1 are read from LDS before the MFMAs of step st are issued.
-  auto load_frags = [&](const uint8_t* A, const uint8_t* B, int st, u32x4 (&av)[WN], u32x4 (&bv)[WM]) {
+  auto load_frags = [&](const uint8_t* A, const uint8_t* B, int st, u32x4 (&av)[WN], u32x4 (&bv)[WM]) __attribute__((always_inline)) {
     const int gr = 2 * st + hh;
 #pragma unroll
     for (int p = 0; p < WN; ++p) {
@@ -1112,10 +1118,10 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a, float* part, int S
       bv[c] = *reinterpret_cast<const u32x4*>(B + row * 128 + ((gr ^ ((row >> 1) & 7)) * 16));
     }
   };
-  auto compute = [&](const uint8_t* A, const uint8_t* B) {
+  auto compute = [&](const uint8_t* A, const uint8_t* B) __attribute__((always_inline)) {
     u32x4 av0[WN], bv0[WM], av1[WN], bv1[WM];
     load_frags(A, B, 0, av0, bv0);
-    static_for<0, 4>([&](auto sc) {
+    static_for<0, 4>([&](auto sc) __attribute__((always_inline)) {
       constexpr int st = decltype(sc)::value;
       u32x4 (&av)[WN] = (st & 1) ? av1 : av0;
       u32x4 (&bv)[WM] = (st & 1) ? bv1 : bv0;
@@ -1132,86 +1138,81 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a, float* part, int S
     });
   };
   // LDS-only barrier: each wave has already waited for its own loads and DMAs where needed.
-  auto barrier = [&]() {
+  auto barrier = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(63) & ~0x0F00);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
 
-  // Pipeline two blocks deep: block i is multiplied from A buffer i % 2 and the current X
-  // buffer while block i + 1's weights (registers) and X rows (the next X buffer) are in
-  // flight or in place and block i + 2's are requested; three X buffers rotate, two register
-  // sets alternate (the loop is unrolled by two for them).  A wave's loads of one block are
-  // NL instructions, so before rebuilding block i + 1 it waits until at most block i + 2's
-  // NL are outstanding (loads retire in order): that also covers its X DMAs of block i + 1,
-  // which the barrier closing the half-iteration then publishes to the other waves.  Blocks
-  // past the slice are loaded out of range and rebuilt into a buffer no one multiplies.
+  // Pipeline D blocks deep: block i is multiplied from A buffer i % 2 and X buffer
+  // i % (D + 1) while the weights (registers) and X rows of blocks i + 1 .. i + D - 1 are in
+  // flight or in place and block i + D's are requested; D register sets take blocks in turn
+  // (the loop is unrolled by D for them).  A wave's loads of one block are NL instructions,
+  // so before rebuilding block i + 1 it waits until at most the (D - 1) NL of the blocks after
+  // it are outstanding (loads retire in order): that also covers its X DMAs of block i + 1,
+  // which the barrier closing the step then publishes to the other waves.  Blocks past the
+  // slice are loaded out of range (zeros, no traffic) and rebuilt into a buffer no one
+  // multiplies.  One block's multiply and the next one's rebuild form one branch-free
+  // region, which the scheduler is free to interleave.
   constexpr int NL = XD + 3 * TW;
-  uint8_t* const abuf0 = smem;
-  uint8_t* const abuf1 = smem + ABYTES;
-  uint8_t* xcur = smem + 2 * ABYTES;
-  uint8_t* xnext = xcur + BBYTES;
-  uint8_t* xfree = xnext + BBYTES;
-  auto rotate = [&]() {
-    uint8_t* const t = xcur;
-    xcur = xnext;
-    xnext = xfree;
-    xfree = t;
-  };
-  BigW<SRC> sla[TW], slb[TW];
-  issue_x(bs, xcur);
-  load_block(bs, sla);
-  issue_x(bs + 1, xnext);
-  load_block(bs + 1, slb);
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(NL));
-  rebuild_to_lds(bs, sla, abuf0);
+  static_assert(NL * (D - 1) <= 63, "vmcnt range");
+  uint8_t* const abase = smem;
+  uint8_t* const xbase = smem + 2 * ABYTES;
+  auto abuf = [&](int j) __attribute__((always_inline)) { return abase + (j & 1) * ABYTES; };
+  auto xbuf = [&](int j) __attribute__((always_inline)) { return xbase + (j % (D + 1)) * BBYTES; };
+  BigW<SRC> sl[D][TW];
+  static_for<0, D>([&](auto jc) __attribute__((always_inline)) {
+    constexpr int j = decltype(jc)::value;
+    issue_x(bs + j, xbuf(j));
+    load_block(bs + j, sl[j]);
+  });
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(NL * (D - 1)));
+  rebuild_to_lds(bs, sl[0], abuf(0));
   barrier();
-  for (int i = 0; i < nblk; i += 2) {
-    issue_x(bs + i + 2, xfree);                 // block i + 2 (sla: block i was rebuilt)
-    load_block(bs + i + 2, sla);
-    compute(abuf0, xcur);                       // block i
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(NL));
-    rebuild_to_lds(bs + i + 1, slb, abuf1);     // block i + 1
+  // Step for block i (j = i mod D): request block i + D into the register set block i left,
+  // multiply block i, rebuild block i + 1.
+  auto step = [&](int i, auto jc) __attribute__((always_inline)) {
+    constexpr int j = decltype(jc)::value;
+    issue_x(bs + i + D, xbuf(i + D));
+    load_block(bs + i + D, sl[j]);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(NL * (D - 1)));
+    compute(abuf(i), xbuf(i));
+    rebuild_to_lds(bs + i + 1, sl[(j + 1) % D], abuf(i + 1));
     barrier();
-    rotate();
-    issue_x(bs + i + 3, xfree);                 // block i + 3 (slb: block i + 1 was rebuilt)
-    load_block(bs + i + 3, slb);
-    if (i + 1 < nblk) compute(abuf1, xcur);     // block i + 1
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(NL));
-    rebuild_to_lds(bs + i + 2, sla, abuf0);     // block i + 2
-    barrier();
-    rotate();
-  }
+  };
+  // The loop's multiplies are unconditional (a conditional one would merge two versions of
+  // the accumulators at the loop latch, which the compiler resolves by copying all of them
+  // between register files every iteration); the last nblk % D blocks follow the loop.
+  int i = 0;
+  for (; i + D <= nblk; i += D) static_for<0, D>([&](auto jc) __attribute__((always_inline)) { step(i + decltype(jc)::value, jc); });
+  static_for<0, D - 1>([&](auto jc) __attribute__((always_inline)) {
+    if (i + decltype(jc)::value < nblk) step(i + decltype(jc)::value, jc);
+  });
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));    // the out-of-range requests past the slice
 
   // D lane layout (32x32): X row (column of D) lane % 32 of column tile c; register e holds
-  // weight row 8 (e / 4) + 4 hh + e % 4 of row pair p.
-#pragma unroll
-  for (int p = 0; p < WN; ++p)
-#pragma unroll
-    for (int c = 0; c < WM; ++c) {
-      const int mm = mcol0 + wm * 32 * WM + c * 32 + xr;
-      if (mm >= a.m) continue;
-#pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
-        const int n0 = rg * BN + wn * 32 * WN + p * 32 + 8 * qd + 4 * hh;
-        if (n0 >= a.n) continue;
-        const floatx4 v{acc[p][c][4 * qd], acc[p][c][4 * qd + 1], acc[p][c][4 * qd + 2], acc[p][c][4 * qd + 3]};
-        if (!part) {
-          store_out4(a, mm, n0, v);
-          continue;
-        }
-        float* yp = part + (size_t)s * a.m * a.n + (size_t)mm * a.n + n0;
-        if (n0 + 3 < a.n && (a.n & 3) == 0) {
-          *reinterpret_cast<floatx4*>(yp) = v;
-        } else {
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj)
-            if (n0 + jj < a.n) yp[jj] = v[jj];
-        }
-      }
+  // weight row 8 (e / 4) + 4 hh + e % 4 of row pair p.  Unrolled at compile time (static_for):
+  // an accumulator array indexed at run time would live in scratch memory.
+  static_for<0, WN * WM * 4>([&](auto ic) __attribute__((always_inline)) {
+    constexpr int p = decltype(ic)::value / (4 * WM), c = decltype(ic)::value / 4 % WM, qd = decltype(ic)::value % 4;
+    const int mm = mcol0 + wm * 32 * WM + c * 32 + xr;
+    const int n0 = rg * BN + wn * 32 * WN + p * 32 + 8 * qd + 4 * hh;
+    if (mm >= a.m || n0 >= a.n) return;
+    const floatx4 v{acc[p][c][4 * qd], acc[p][c][4 * qd + 1], acc[p][c][4 * qd + 2], acc[p][c][4 * qd + 3]};
+    if (!part) {
+      store_out4(a, mm, n0, v);
+      return;
     }
+    float* yp = part + (size_t)s * a.m * a.n + (size_t)mm * a.n + n0;
+    if (n0 + 3 < a.n && (a.n & 3) == 0) {
+      *reinterpret_cast<floatx4*>(yp) = v;
+    } else {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        if (n0 + jj < a.n) yp[jj] = v[jj];
+    }
+  });
 }
 
 // y[i] = sum over s of part[s][i], in slice order.  A thread owns 4 consecutive elements
@@ -1346,9 +1347,14 @@ static int wide_slices(int64_t tiles, int R, int64_t kb, int m) {
 }
 // Big-tile kernel: K slices so that the workgroups fill the chip once (one a compute unit at
 // 128 KB of LDS, two at 80 KB), at most 64 blocks a slice.
+// Big-tile pipeline depth and LDS bytes: two rebuilt-weight buffers and D + 1 X buffers of
+// 64-element (128-byte) rows.  Three blocks in flight measured no faster than two at
+// M = 128 .. 1024 on 14336 x 4096, so both tiles run two deep.
+static constexpr int kBigDepth = 2;
+static constexpr int big_lds(int WN, int WM, int D) { return 128 * (2 * 64 * WN + (D + 1) * 64 * WM); }
 static int big_slices(int64_t tiles, int WN, int WM, int64_t kb, int m) {
   const int64_t wgs = ((tiles * 16 + 64 * WN - 1) / (64 * WN)) * ((m + 64 * WM - 1) / (64 * WM));
-  const int64_t per_cu = (2 * 64 * WN + 3 * 64 * WM) * 128 <= 80 * 1024 ? 2 : 1;   // LDS a workgroup
+  const int64_t per_cu = big_lds(WN, WM, kBigDepth) <= 80 * 1024 ? 2 : 1;
   int64_t S = std::max<int64_t>(1, 256 * per_cu / std::max<int64_t>(wgs, 1));
   S = std::min<int64_t>(S, std::min<int64_t>(kb, kMaxSlices));
   return (int)std::max<int64_t>(S, (kb + 63) / 64);
@@ -1445,19 +1451,22 @@ static hipError_t launch_wide_t(const GemmArgs& a, int64_t tiles, int S, float* 
   return launch_reduce(a, S, part, s);
 }
 
-template <int SRC, int WN, int WM>
+template <int SRC, int WN, int WM, int D>
 static hipError_t launch_big_t(const GemmArgs& a, int64_t tiles, int S, float* part, hipStream_t s) {
   const dim3 grid((unsigned)((tiles * 16 + 64 * WN - 1) / (64 * WN)), (unsigned)S, (unsigned)((a.m + 64 * WM - 1) / (64 * WM)));
-  hipLaunchKernelGGL((k_gemm_big<SRC, WN, WM>), grid, dim3(256), 128 * (2 * 64 * WN + 3 * 64 * WM), s, a,
-                     S > 1 ? part : nullptr, S);
+  hipLaunchKernelGGL((k_gemm_big<SRC, WN, WM, D>), grid, dim3(256), big_lds(WN, WM, D), s, a, S > 1 ? part : nullptr, S);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
   return launch_reduce(a, S, part, s);
 }
 
+// 128 x 128 tiles (80 KB: two workgroups a CU) and 128 x 256 tiles (128 KB).  (256 x 256
+// tiles need 256 accumulator registers a wave and run out of scalar registers for the stream
+// descriptors.)
 template <int SRC>
 static hipError_t launch_big(const GemmArgs& a, int64_t tiles, int WM, int S, float* part, hipStream_t s) {
-  return WM == 4 ? launch_big_t<SRC, 2, 4>(a, tiles, S, part, s) : launch_big_t<SRC, 2, 2>(a, tiles, S, part, s);
+  return WM == 4 ? launch_big_t<SRC, 2, 4, kBigDepth>(a, tiles, S, part, s)
+                 : launch_big_t<SRC, 2, 2, kBigDepth>(a, tiles, S, part, s);
 }
 
 // Batches of 2 blocks only: 4 would spill at 8 waves a workgroup.

@@ -259,17 +259,20 @@ def test_gemm_wide_tiles(variant, case):
 
 
 @pytest.mark.parametrize("variant", BIG_VARIANTS)
-@pytest.mark.parametrize("case", ["ragged_rows", "lut_palette", "long_k"])
+@pytest.mark.parametrize("case", ["ragged_rows", "lut_palette", "long_k", "odd_blocks"])
 def test_gemm_big_tiles(variant, case):
     """The big-tile kernel (the workgroup rebuilds each block's weight rows once into LDS,
-    32x32 MFMAs on LDS operands): a row count that leaves the last workgroup's rows partly
-    empty and ragged, the table-lookup palette, and k = 9216 (several K slices and flag words
-    past the first 64 blocks), with and without room for the partial sums, across one, two
-    and three column chunks of 256 X rows and ragged last chunks."""
+    32x32 MFMAs on LDS operands, two or three blocks in flight): a row count that leaves the
+    last workgroup's rows partly empty and ragged, the table-lookup palette, k = 9216 (several
+    K slices and flag words past the first 64 blocks), and k = 1216 (19 blocks: every
+    remainder of a slice's block count modulo the pipeline depth, slices of one and two
+    blocks), with and without room for the partial sums, across one, two and three column
+    chunks of 256 X rows and ragged last chunks."""
     t = torch()
     w = {"ragged_rows": lambda: synth.small_gaussian(200, 2048, seed=29, plant_frac=0.05)["w"],
          "lut_palette": lambda: bimodal(96, 512, 6),
-         "long_k": lambda: synth.small_gaussian(70, 9216, seed=31, plant_frac=0.1)["w"]}[case]()
+         "long_k": lambda: synth.small_gaussian(70, 9216, seed=31, plant_frac=0.1)["w"],
+         "odd_blocks": lambda: synth.small_gaussian(150, 1216, seed=37, plant_frac=0.05)["w"]}[case]()
     n, k = w.shape
     cm = uw.CompressedMatrix(w)
     assert uw.uw_variant_name(variant).startswith("big ")
