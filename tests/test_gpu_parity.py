@@ -5,10 +5,13 @@ Bar: bit-exact for decode / transcode / exponent streams (byte work); for GEMMs
 SwiGLU / RMS-norm glue within one BF16 ulp of the oracle."""
 import numpy as np
 import pytest
+from hypothesis import HealthCheck, given, settings, strategies as st
 
 import lossless_bf16_weight_amd as uw
 from lossless_bf16_weight_amd import synth
 from oracle import codec, gemm
+
+from generated import finite, matrices
 
 pytestmark = pytest.mark.gpu
 
@@ -111,6 +114,36 @@ def test_decoders_bit_exact(name, chunk):
     uw.uw_decode_exponents(cm.d, ex, ws)
     uw.uw_check(ws)
     assert ex.cpu().numpy().tobytes() == codec.exponent_stream_blob(ref_blob).tobytes()
+
+
+@settings(max_examples=25, deadline=None, derandomize=True, suppress_health_check=[HealthCheck.too_slow])
+@given(matrices(max_rows=70, max_blocks=8), st.sampled_from([64, 256, 512]), st.integers(1, 40))
+def test_generated_matrices(w, chunk, m):
+    """Generated matrices (random shapes; Gaussian, few-exponent, many-exponent and raw-bit
+    values with signed zeros, subnormals, infinities and NaN payloads sprinkled in): the three
+    device decoders bit-exact against the oracle, and the direct-palette GEMM of the same matrix
+    with its non-finite values replaced within the bound at a random batch size."""
+    t = torch()
+    n, k = w.shape
+    ref_blob = codec.serialize(codec.encode(w, n, k, chunk=chunk))
+    cm = uw.CompressedMatrix(w, chunk=chunk)
+    assert cm.blob.tobytes() == ref_blob
+    ws = err_ws()
+    out = t.empty((n, k), dtype=t.int16, device="cuda")
+    uw.uw_decode_full(cm.d, out, ws)
+    uw.uw_check(ws)
+    assert np.array_equal(host_u16(out), w)
+    assert cm.idx.cpu().numpy().tobytes() == codec.transcode_blob(ref_blob).tobytes()
+    ex = t.empty(int(cm.info["np"]) * k, dtype=t.uint8, device="cuda")
+    uw.uw_decode_exponents(cm.d, ex, ws)
+    uw.uw_check(ws)
+    assert ex.cpu().numpy().tobytes() == codec.exponent_stream_blob(ref_blob).tobytes()
+    wf = finite(w)
+    cf = uw.CompressedMatrix(wf, chunk=chunk)
+    x = synth.gaussian_bf16(np.random.default_rng(m), (m, k), 1.0)
+    y = t.full((m, n), float("nan"), dtype=t.float32, device="cuda")
+    uw.uw_gemm(cf.d, dev_u16(x), y, m, uw.UW_PIPE_DIRECT_PALETTE, cf.workspace(m, uw.UW_PIPE_DIRECT_PALETTE))
+    check_gemm(y, x, wf)
 
 
 @pytest.mark.parametrize("name", list(CASES))

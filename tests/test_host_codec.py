@@ -6,6 +6,9 @@ import re
 
 import numpy as np
 import pytest
+from hypothesis import HealthCheck, given, settings, strategies as st
+
+from generated import matrices
 
 import lossless_bf16_weight_amd as uw
 from lossless_bf16_weight_amd import synth
@@ -58,6 +61,18 @@ def test_encoder_blob_equals_oracle(name, make, chunk):
     ref = oracle_blob(w, chunk)
     assert blob.size == ref.size
     assert np.array_equal(blob, ref)
+
+
+@settings(max_examples=40, deadline=None, derandomize=True, suppress_health_check=[HealthCheck.too_slow])
+@given(matrices(), st.sampled_from([64, 128, 512]))
+def test_encoder_blob_equals_oracle_generated(w, chunk):
+    """Generated matrices (random shapes; Gaussian, few-exponent, many-exponent and raw-bit
+    values; signed zeros, subnormals, infinities and NaN payloads sprinkled in): the C++ blob
+    equals the oracle's byte for byte, and the oracle decodes it back to W."""
+    blob = uw.uw_encode(w, chunk)
+    ref = oracle_blob(w, chunk)
+    assert np.array_equal(blob, ref)
+    assert np.array_equal(codec.decode_blob(ref.tobytes()), w)
 
 
 @pytest.mark.parametrize("threads", ["1", "3", "8"])
