@@ -279,11 +279,13 @@ __global__ __launch_bounds__((MaxThreads<CT, U>::v)) void k_gemm(GemmArgs a) {
       fpre[j] = SHX ? 0u : __builtin_amdgcn_raw_buffer_load_b16(frs, i < b0 ? (uint32_t)i * 2 : kOob, 0, 0);
     }
   }
-  // X rows, 1 KB (8 blocks of one row) a DMA; the launcher requires k % 512 == 0.  With shared
-  // X and an unrolled ring the rows are staged in parts of kXPart blocks: the first part here,
-  // the rest once the first weights are out, each part checked by a barrier before its first
-  // block (see the ring), so the start waits for 1/4 of X at k = 4096 instead of all of it.
-  constexpr bool kXParts = SHX && NB > 0 && XL;
+  // X rows, 1 KB (8 blocks of one row) a DMA; the launcher requires k % 512 == 0.  With an
+  // unrolled ring whose waves each run blocks 0 .. kb-1 in order (shared X, or one wave a tile)
+  // the rows are staged in parts of kXPart blocks: the first part here, the rest once the first
+  // weights are out, each part checked by a barrier before its first block (see the ring), so
+  // the start waits for 1/4 of X at k = 4096 instead of all of it.
+  constexpr bool kXPartsOk = NB > 0 && XL;
+  const bool xparts = kXPartsOk && (SHX || nw == 1);
   constexpr int kXPart = 16;
   const int per_row = a.k / 512;
   auto stage_x = [&](int cc0, int cc1) {  // chunks [cc0, cc1) of every valid row
@@ -293,7 +295,7 @@ __global__ __launch_bounds__((MaxThreads<CT, U>::v)) void k_gemm(GemmArgs a) {
       lds_dma16(xrs, sx + (size_t)mr * xl_stride(a.k) + cc * 1024, (uint32_t)mr * a.k * 2 + cc * 1024 + lane * 16);
     }
   };
-  if constexpr (XL) stage_x(0, kXParts ? min(kXPart / 8, per_row) : per_row);
+  if constexpr (XL) stage_x(0, xparts ? min(kXPart / 8, per_row) : per_row);
 #pragma unroll
   for (int u = 0; u < U; ++u) load_main(b0 + u, u < nblk, buf[u]);
   uint32_t vbase = 0, nvt = 0;
@@ -321,7 +323,7 @@ __global__ __launch_bounds__((MaxThreads<CT, U>::v)) void k_gemm(GemmArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) load_ev(b0 + u, u < nblk, buf[u]);
   }
-  if constexpr (kXParts) stage_x(min(kXPart / 8, per_row), per_row);
+  if (xparts) stage_x(min(kXPart / 8, per_row), per_row);
 
   if constexpr (NB > 0) {
     // A block's verbatim-exponent registers are read only when the block is flagged; the
@@ -337,8 +339,8 @@ __global__ __launch_bounds__((MaxThreads<CT, U>::v)) void k_gemm(GemmArgs a) {
       }
       if constexpr (kPal)
         if (i >= U) keep(buf[i - U].ev);
-      if constexpr (kXParts) {
-        if (i > 0 && i % kXPart == 0) {
+      if constexpr (kXPartsOk) {
+        if (xparts && i > 0 && i % kXPart == 0) {
           // X part i / kXPart was requested before block i's weights, so once this wave has
           // waited for those (the empty asm use forces the wait here) its DMAs have landed;
           // the barrier then covers every wave's.
