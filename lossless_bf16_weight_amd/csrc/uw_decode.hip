@@ -547,6 +547,7 @@ __device__ __forceinline__ lds_cu32p advance_word(lds_cu32p p, uint32_t step) {
 template <int MODE>
 __device__ __forceinline__ void decode_unit(const RowDecArgs& a, uint32_t* lut, uint8_t* dsh, int u, int wave,
                                             bool first) {
+  static_assert(MODE == DEC_IDX || MODE == DEC_EXP, "the row decoder writes indices or exponent bytes");
   const int lane = threadIdx.x & 63;
   const bool unit_ok = u < a.units;
   const int t = unit_ok ? u / a.units_per_tile : 0;
@@ -639,9 +640,49 @@ __device__ __forceinline__ void decode_unit(const RowDecArgs& a, uint32_t* lut, 
   uint32_t a4 = 0;                                              // its bits filled
   uint32_t* wp = buf;                                           // its place in the phase buffer
   uint32_t bad = 0;
-  uint32_t img[64];
+  // Index output: each phase's rows are written as soon as the phase is decoded, so the output
+  // writes overlap the decode of later phases (and no image is kept: 69 instead of 112 VGPRs).
+  // Exponent output (16-byte pieces, twice the bytes) keeps the chunk's image in VGPRs and
+  // writes it at the end, so that consecutive stores complete each output line: written a
+  // phase at a time it measured slower (77.6 against 57.3 us on the 8192 x 8192 heavy-tail
+  // matrix at 512-symbol chunks).
+  constexpr bool kPhaseWrite = MODE == DEC_IDX;
+  uint32_t img[kPhaseWrite ? 1 : 64];
+  if constexpr (!kPhaseWrite) {
 #pragma unroll
-  for (int i = 0; i < 64; ++i) img[i] = 0;
+    for (int i = 0; i < 64; ++i) img[i] = 0;
+  }
+
+  // Output places: chunk row q is the (j spc + q)-th coded row of the block; its 16-weight
+  // groups g go to sub-tile (t, 4 blk + g) of the output stream.
+  uint32_t first_rows = cm;
+  for (int i = 0; i < j * a.spc && first_rows; ++i) first_rows &= first_rows - 1u;
+  uint32_t rowq[8];
+  {
+    uint32_t mm = first_rows;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      rowq[q] = __builtin_ctz(mm | 0x10000u);
+      mm &= mm - 1u;
+    }
+  }
+  const __amdgpu_buffer_rsrc_t ors =
+      MODE == DEC_IDX ? make_rsrc(a.out + (size_t)t * a.k * 8 + (size_t)bA * 512, (uint32_t)nbu * 512u)
+                      : make_rsrc(a.out + (size_t)t * a.k * 16 + (size_t)bA * 1024, (uint32_t)nbu * 1024u);
+  // Row q (words w[0..7] of 4-bit indices in sequence order) to the output.
+  auto put_row = [&](int q, const uint32_t* w) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const uint32_t sub = ((uint32_t)(bl * 4 + g) * 16 + rowq[q]);
+      if constexpr (MODE == DEC_IDX) {
+        const u32x2 v{nibbles_to_index_word(w[2 * g]), nibbles_to_index_word(w[2 * g + 1])};
+        __builtin_amdgcn_raw_buffer_store_b64(v, ors, q < nrows ? sub * 8 : kOob, 0, 0);
+      } else {
+        const u32x2 e0 = seq_word_to_exps(w[2 * g], a.tab), e1 = seq_word_to_exps(w[2 * g + 1], a.tab);
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{e0.x, e0.y, e1.x, e1.y}, ors, q < nrows ? sub * 16 : kOob, 0, 0);
+      }
+    }
+  };
 
   // One lookup's state change: e = (length, 4 x count, symbols) as in the table.  The word in
   // progress is stored at every lookup (complete or not), so a finished word is already in the
@@ -700,10 +741,19 @@ __device__ __forceinline__ void decode_unit(const RowDecArgs& a, uint32_t* lut, 
         apply(e, v);
       }
     }
-    // Phase done for every lane: its 16 finished words to VGPRs; the word in progress (a
-    // lookup's symbols past the phase) stays in lo and becomes the buffer's first word.
+    // Phase done for every lane: its rows 2h, 2h + 1 (16 finished words) to the output or the
+    // image; the word in progress (a lookup's symbols past the phase) stays in lo and becomes
+    // the buffer's first word.
+    if constexpr (kPhaseWrite) {
+      uint32_t w[kPhaseWords];
 #pragma unroll
-    for (int i = 0; i < kPhaseWords; ++i) img[kPhaseWords * h + i] = buf[i];
+      for (int i = 0; i < kPhaseWords; ++i) w[i] = buf[i];
+#pragma unroll
+      for (int qq = 0; qq < kPhaseRows; ++qq) put_row(kPhaseRows * h + qq, w + 8 * qq);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kPhaseWords; ++i) img[kPhaseWords * h + i] = buf[i];
+    }
     wp = buf;
   }
   if (has_chunk) {
@@ -712,44 +762,8 @@ __device__ __forceinline__ void decode_unit(const RowDecArgs& a, uint32_t* lut, 
   }
   if (bad) atomicOr(a.err, 1u);
 
-  // Write-out: coded rows from the VGPR image (row q of the chunk is the (j spc + q)-th coded
-  // row of the block); the lane's share of the other rows (rows j spc .. (j + 1) spc - 1 that
-  // are verbatim or padding) from the verbatim exponents or zeros.  Each output line is
-  // completed by consecutive store instructions of the wave.
-  uint32_t first_rows = cm;
-  for (int i = 0; i < j * a.spc && first_rows; ++i) first_rows &= first_rows - 1u;
-  uint32_t rowq[8];
-  {
-    uint32_t mm = first_rows;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      rowq[q] = __builtin_ctz(mm | 0x10000u);
-      mm &= mm - 1u;
-    }
-  }
-  const uint32_t blk = (uint32_t)(bA + bl);
-  uint32_t other = lane_ok ? ~cm & (((1u << a.spc) - 1u) << (j * a.spc)) & 0xFFFFu : 0u;
-  if constexpr (MODE == DEC_IDX) {
-    // Index stream: row r of sub-tile (t, 4 blk + g) at ((t k/16 + 4 blk + g) 16 + r) 8.
-    const __amdgpu_buffer_rsrc_t ors = make_rsrc(a.out + (size_t)t * a.k * 8 + (size_t)bA * 512, (uint32_t)nbu * 512u);
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const u32x2 v{nibbles_to_index_word(img[8 * q + 2 * g]), nibbles_to_index_word(img[8 * q + 2 * g + 1])};
-        __builtin_amdgcn_raw_buffer_store_b64(v, ors, q < nrows ? ((uint32_t)(bl * 4 + g) * 16 + rowq[q]) * 8 : kOob, 0, 0);
-      }
-    }
-    while (other) {
-      const uint32_t r = __builtin_ctz(other);
-      other &= other - 1u;
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        __builtin_amdgcn_raw_buffer_store_b64(u32x2{0, 0}, ors, ((uint32_t)(bl * 4 + g) * 16 + r) * 8, 0, 0);
-    }
-  } else if constexpr (MODE == DEC_EXP) {
-    // Exponent bytes in the sign+mantissa sub-tile layout.
-    const __amdgpu_buffer_rsrc_t ors = make_rsrc(a.out + (size_t)t * a.k * 16 + (size_t)bA * 1024, (uint32_t)nbu * 1024u);
+  if constexpr (!kPhaseWrite) {
+    // The coded rows, sub-tile by sub-tile: consecutive stores complete each output line.
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
 #pragma unroll
@@ -759,6 +773,21 @@ __device__ __forceinline__ void decode_unit(const RowDecArgs& a, uint32_t* lut, 
                                                q < nrows ? ((uint32_t)(bl * 4 + g) * 16 + rowq[q]) * 16 : kOob, 0, 0);
       }
     }
+  }
+  // The lane's share of the block's other rows (rows j spc .. (j + 1) spc - 1 that are verbatim
+  // or padding): the verbatim exponents or zeros.
+  uint32_t other = lane_ok ? ~cm & (((1u << a.spc) - 1u) << (j * a.spc)) & 0xFFFFu : 0u;
+  if constexpr (MODE == DEC_IDX) {
+    // Index stream: row r of sub-tile (t, 4 blk + g) at ((t k/16 + 4 blk + g) 16 + r) 8.
+    while (other) {
+      const uint32_t r = __builtin_ctz(other);
+      other &= other - 1u;
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{0, 0}, ors, ((uint32_t)(bl * 4 + g) * 16 + r) * 8, 0, 0);
+    }
+  } else {
+    // Exponent bytes in the sign+mantissa sub-tile layout.
     while (other) {
       const uint32_t r = __builtin_ctz(other);
       other &= other - 1u;
@@ -768,48 +797,6 @@ __device__ __forceinline__ void decode_unit(const RowDecArgs& a, uint32_t* lut, 
       for (int g = 0; g < 4; ++g) {
         const u32x4 o = verb ? *reinterpret_cast<const u32x4*>(ve + g * 16) : u32x4{0, 0, 0, 0};
         __builtin_amdgcn_raw_buffer_store_b128(o, ors, ((uint32_t)(bl * 4 + g) * 16 + r) * 16, 0, 0);
-      }
-    }
-  } else {
-    // BF16 rows: row r of the tile, columns 64 blk .. + 63 = 128 contiguous bytes, with the
-    // row's sign+mantissa bytes (4 sub-tiles of 16) loaded two rows ahead.
-    const uint32_t rowb = (uint32_t)a.k * 2u;
-    const __amdgpu_buffer_rsrc_t ors =
-        make_rsrc(a.out + (size_t)t * 16 * a.k * 2, (uint32_t)(rows - 1) * rowb + (uint32_t)a.k * 2u);
-    const uint8_t* const smt = a.sm + (size_t)t * a.k * 16;
-    auto load_sm = [&](uint32_t row, bool ok, u32x4 sv[4]) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        sv[g] = ok ? *reinterpret_cast<const u32x4*>(smt + ((size_t)(blk * 4 + g) * 16 + row) * 16) : u32x4{0, 0, 0, 0};
-    };
-    auto put = [&](uint32_t row, bool ok, const u32x4 sv[4], int p, u32x2 e) {
-      const uint32_t s0 = (p & 1) ? sv[p >> 1].z : sv[p >> 1].x, s1 = (p & 1) ? sv[p >> 1].w : sv[p >> 1].y;
-      const u32x4 o{bf16_pairs_from(s0, e.x, 0), bf16_pairs_from(s0, e.x, 1), bf16_pairs_from(s1, e.y, 0),
-                    bf16_pairs_from(s1, e.y, 1)};
-      __builtin_amdgcn_raw_buffer_store_b128(o, ors, ok ? row * rowb + blk * 128u + (uint32_t)p * 16u : kOob, 0, 0);
-    };
-    u32x4 sva[4], svb[4];
-    load_sm(rowq[0], 0 < nrows, sva);
-    load_sm(rowq[1], 1 < nrows, svb);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      u32x4* cur = (q & 1) ? svb : sva;
-#pragma unroll
-      for (int p = 0; p < 8; ++p) put(rowq[q], q < nrows, cur, p, seq_word_to_exps(img[8 * q + p], a.tab));
-      if (q + 2 < 8) load_sm(rowq[q + 2], q + 2 < nrows, cur);
-    }
-    while (other) {
-      const uint32_t r = __builtin_ctz(other);
-      other &= other - 1u;
-      if (r >= (uint32_t)rows) continue;                       // padding rows are not part of W
-      const uint8_t* ve = a.vexp + (size_t)(bvr + __popc(bf & ((1u << r) - 1u))) * 64;
-      u32x4 sv[4];
-      load_sm(r, true, sv);
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const u32x4 ev = *reinterpret_cast<const u32x4*>(ve + g * 16);
-        put(r, true, sv, 2 * g, u32x2{ev.x, ev.y});
-        put(r, true, sv, 2 * g + 1, u32x2{ev.z, ev.w});
       }
     }
   }
