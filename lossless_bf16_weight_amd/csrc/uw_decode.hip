@@ -547,7 +547,6 @@ __device__ __forceinline__ lds_cu32p advance_word(lds_cu32p p, uint32_t step) {
 template <int MODE>
 __device__ __forceinline__ void decode_unit(const RowDecArgs& a, uint32_t* lut, uint8_t* dsh, int u, int wave,
                                             bool first) {
-  static_assert(MODE == DEC_IDX || MODE == DEC_EXP, "the row decoder writes indices or exponent bytes");
   const int lane = threadIdx.x & 63;
   const bool unit_ok = u < a.units;
   const int t = unit_ok ? u / a.units_per_tile : 0;
@@ -640,14 +639,21 @@ __device__ __forceinline__ void decode_unit(const RowDecArgs& a, uint32_t* lut, 
   uint32_t a4 = 0;                                              // its bits filled
   uint32_t* wp = buf;                                           // its place in the phase buffer
   uint32_t bad = 0;
-  // Index output: each phase's rows are written as soon as the phase is decoded, so the output
-  // writes overlap the decode of later phases (and no image is kept: 69 instead of 112 VGPRs).
+  // Index output: every two phases (four rows) are written as soon as they are decoded, so the
+  // output writes overlap the decode of later phases and only two phases' words are held in
+  // VGPRs.  A lane's four rows of one sub-tile are 32 contiguous bytes written by consecutive
+  // stores (one phase at a time, 16-byte pieces, the output took 2.8x its bytes in HBM writes).
   // Exponent output (16-byte pieces, twice the bytes) keeps the chunk's image in VGPRs and
   // writes it at the end, so that consecutive stores complete each output line: written a
   // phase at a time it measured slower (77.6 against 57.3 us on the 8192 x 8192 heavy-tail
   // matrix at 512-symbol chunks).
+  // BF16 output: a row is 128 contiguous bytes of W, whole lines, so it is written a phase (two
+  // rows) at a time, with the rows' sign+mantissa bytes loaded a phase ahead.
   constexpr bool kPhaseWrite = MODE == DEC_IDX;
-  uint32_t img[kPhaseWrite ? 1 : 64];
+  constexpr bool kBf16 = MODE == DEC_BF16;
+  uint32_t img[kPhaseWrite || kBf16 ? 1 : 64];
+  uint32_t grp[kPhaseWrite ? kPhaseWords : 1];   // the even phase's words, written with the odd one's
+  int hdone = 0;
   if constexpr (!kPhaseWrite) {
 #pragma unroll
     for (int i = 0; i < 64; ++i) img[i] = 0;
@@ -666,20 +672,37 @@ __device__ __forceinline__ void decode_unit(const RowDecArgs& a, uint32_t* lut, 
       mm &= mm - 1u;
     }
   }
+  const uint32_t rowb = (uint32_t)a.k * 2u;                   // a BF16 output row, bytes
   const __amdgpu_buffer_rsrc_t ors =
       MODE == DEC_IDX ? make_rsrc(a.out + (size_t)t * a.k * 8 + (size_t)bA * 512, (uint32_t)nbu * 512u)
-                      : make_rsrc(a.out + (size_t)t * a.k * 16 + (size_t)bA * 1024, (uint32_t)nbu * 1024u);
-  // Row q (words w[0..7] of 4-bit indices in sequence order) to the output.
-  auto put_row = [&](int q, const uint32_t* w) {
+      : MODE == DEC_EXP ? make_rsrc(a.out + (size_t)t * a.k * 16 + (size_t)bA * 1024, (uint32_t)nbu * 1024u)
+                        : make_rsrc(a.out + (size_t)t * 16 * rowb, (uint32_t)(rows - 1) * rowb + rowb);
+  // BF16: the tile's sign+mantissa sub-tiles; row r's 16 bytes of sub-tile (t, 4 blk + g).
+  const uint32_t blk = (uint32_t)(bA + bl);
+  const __amdgpu_buffer_rsrc_t srs = make_rsrc(a.sm + (size_t)t * a.k * 16, (uint32_t)a.k * 16u);
+  auto load_sm = [&](uint32_t row, bool ok, u32x4 sv[4]) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) sv[g] = bload16(srs, ok ? ((blk * 4 + g) * 16 + row) * 16 : kOob);
+  };
+  // 16-byte piece p (weights 8p .. 8p + 7) of BF16 row `row`: sign+mantissa from sv, exponents e.
+  auto put_bf16 = [&](uint32_t row, bool ok, const u32x4 sv[4], int p, u32x2 e) {
+    const uint32_t s0 = (p & 1) ? sv[p >> 1].z : sv[p >> 1].x, s1 = (p & 1) ? sv[p >> 1].w : sv[p >> 1].y;
+    const u32x4 o{bf16_pairs_from(s0, e.x, 0), bf16_pairs_from(s0, e.x, 1), bf16_pairs_from(s1, e.y, 0),
+                  bf16_pairs_from(s1, e.y, 1)};
+    __builtin_amdgcn_raw_buffer_store_b128(o, ors, ok ? row * rowb + blk * 128u + (uint32_t)p * 16u : kOob, 0, 0);
+  };
+  u32x4 svp[kBf16 ? kPhaseRows : 1][4];         // the current phase's rows' sign+mantissa bytes
+  // Index rows q0 .. q0 + nq - 1 (words w[8 i .. 8 i + 7] of 4-bit indices in sequence order for
+  // row q0 + i) to the output, sub-tile by sub-tile.
+  auto put_rows = [&](int q0, int nq, const uint32_t* w) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const uint32_t sub = ((uint32_t)(bl * 4 + g) * 16 + rowq[q]);
-      if constexpr (MODE == DEC_IDX) {
-        const u32x2 v{nibbles_to_index_word(w[2 * g]), nibbles_to_index_word(w[2 * g + 1])};
-        __builtin_amdgcn_raw_buffer_store_b64(v, ors, q < nrows ? sub * 8 : kOob, 0, 0);
-      } else {
-        const u32x2 e0 = seq_word_to_exps(w[2 * g], a.tab), e1 = seq_word_to_exps(w[2 * g + 1], a.tab);
-        __builtin_amdgcn_raw_buffer_store_b128(u32x4{e0.x, e0.y, e1.x, e1.y}, ors, q < nrows ? sub * 16 : kOob, 0, 0);
+#pragma unroll
+      for (int i = 0; i < nq; ++i) {
+        const int q = q0 + i;
+        const u32x2 v{nibbles_to_index_word(w[8 * i + 2 * g]), nibbles_to_index_word(w[8 * i + 2 * g + 1])};
+        __builtin_amdgcn_raw_buffer_store_b64(v, ors, q < nrows ? ((uint32_t)(bl * 4 + g) * 16 + rowq[q]) * 8 : kOob,
+                                              0, 0);
       }
     }
   };
@@ -707,6 +730,10 @@ __device__ __forceinline__ void decode_unit(const RowDecArgs& a, uint32_t* lut, 
     s = (uint32_t)sl & 31u;
   };
 
+  if constexpr (kBf16) {
+#pragma unroll
+    for (int qq = 0; qq < kPhaseRows; ++qq) load_sm(rowq[qq], qq < nrows, svp[qq]);
+  }
 #pragma unroll
   for (int h = 0; h < kPhases; ++h) {
     if (kPhaseRows * h >= wmax_rows) break;
@@ -745,11 +772,36 @@ __device__ __forceinline__ void decode_unit(const RowDecArgs& a, uint32_t* lut, 
     // image; the word in progress (a lookup's symbols past the phase) stays in lo and becomes
     // the buffer's first word.
     if constexpr (kPhaseWrite) {
+      if (h & 1) {
+        uint32_t w[2 * kPhaseWords];
+#pragma unroll
+        for (int i = 0; i < kPhaseWords; ++i) {
+          w[i] = grp[i];
+          w[kPhaseWords + i] = buf[i];
+        }
+        put_rows(kPhaseRows * (h - 1), 2 * kPhaseRows, w);
+      } else {
+#pragma unroll
+        for (int i = 0; i < kPhaseWords; ++i) grp[i] = buf[i];
+      }
+      hdone = h + 1;
+    } else if constexpr (kBf16) {
       uint32_t w[kPhaseWords];
 #pragma unroll
       for (int i = 0; i < kPhaseWords; ++i) w[i] = buf[i];
 #pragma unroll
-      for (int qq = 0; qq < kPhaseRows; ++qq) put_row(kPhaseRows * h + qq, w + 8 * qq);
+      for (int qq = 0; qq < kPhaseRows; ++qq) {
+        const int q = kPhaseRows * h + qq;
+#pragma unroll
+        for (int pc = 0; pc < 8; ++pc) put_bf16(rowq[q], q < nrows, svp[qq], pc, seq_word_to_exps(w[8 * qq + pc], a.tab));
+      }
+      if (h + 1 < kPhases) {   // the next phase's rows, loaded while it is decoded
+#pragma unroll
+        for (int qq = 0; qq < kPhaseRows; ++qq) {
+          const int q = kPhaseRows * (h + 1) + qq;
+          load_sm(rowq[q], q < nrows, svp[qq]);
+        }
+      }
     } else {
 #pragma unroll
       for (int i = 0; i < kPhaseWords; ++i) img[kPhaseWords * h + i] = buf[i];
@@ -762,7 +814,14 @@ __device__ __forceinline__ void decode_unit(const RowDecArgs& a, uint32_t* lut, 
   }
   if (bad) atomicOr(a.err, 1u);
 
-  if constexpr (!kPhaseWrite) {
+  if constexpr (kBf16) {
+  } else if constexpr (kPhaseWrite) {
+    // A last, unpaired phase (constant row numbers: rowq is indexed at compile time).
+    static_for<0, kPhases / 2>([&](auto pc) {
+      constexpr int hp = 2 * decltype(pc)::value;
+      if (hdone == hp + 1) put_rows(kPhaseRows * hp, kPhaseRows, grp);
+    });
+  } else {
     // The coded rows, sub-tile by sub-tile: consecutive stores complete each output line.
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -786,7 +845,7 @@ __device__ __forceinline__ void decode_unit(const RowDecArgs& a, uint32_t* lut, 
       for (int g = 0; g < 4; ++g)
         __builtin_amdgcn_raw_buffer_store_b64(u32x2{0, 0}, ors, ((uint32_t)(bl * 4 + g) * 16 + r) * 8, 0, 0);
     }
-  } else {
+  } else if constexpr (MODE == DEC_EXP) {
     // Exponent bytes in the sign+mantissa sub-tile layout.
     while (other) {
       const uint32_t r = __builtin_ctz(other);
@@ -797,6 +856,22 @@ __device__ __forceinline__ void decode_unit(const RowDecArgs& a, uint32_t* lut, 
       for (int g = 0; g < 4; ++g) {
         const u32x4 o = verb ? *reinterpret_cast<const u32x4*>(ve + g * 16) : u32x4{0, 0, 0, 0};
         __builtin_amdgcn_raw_buffer_store_b128(o, ors, ((uint32_t)(bl * 4 + g) * 16 + r) * 16, 0, 0);
+      }
+    }
+  } else {
+    // BF16 rows: verbatim rows from their raw exponents; padding rows are not part of W.
+    while (other) {
+      const uint32_t r = __builtin_ctz(other);
+      other &= other - 1u;
+      if (r >= (uint32_t)rows) continue;
+      const uint8_t* ve = a.vexp + (size_t)(bvr + __popc(bf & ((1u << r) - 1u))) * 64;
+      u32x4 sv[4];
+      load_sm(r, true, sv);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const u32x4 ev = *reinterpret_cast<const u32x4*>(ve + g * 16);
+        put_bf16(r, true, sv, 2 * g, u32x2{ev.x, ev.y});
+        put_bf16(r, true, sv, 2 * g + 1, u32x2{ev.z, ev.w});
       }
     }
   }
@@ -912,7 +987,8 @@ static uw_status run_decode_rows(const uw_dmat* d, int mode, uint8_t* out, uint3
   switch (mode) {
     case DEC_IDX: hipLaunchKernelGGL(k_decode_rows<DEC_IDX>, grid, dim3(64 * W), lds, s, a); break;
     case DEC_EXP: hipLaunchKernelGGL(k_decode_rows<DEC_EXP>, grid, dim3(64 * W), lds, s, a); break;
-    default: return fail(UW_E_ARG, "the row decoder writes indices or exponents");
+    case DEC_BF16: hipLaunchKernelGGL(k_decode_rows<DEC_BF16>, grid, dim3(64 * W), lds, s, a); break;
+    default: return fail(UW_E_ARG, "unknown decode target %d", mode);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(UW_E_HIP, "decode launch: %s", hipGetErrorString(e));
@@ -924,12 +1000,9 @@ uw_status run_decode(const uw_dmat* d, int mode, uint8_t* out, void* ws, size_t 
   if (st) return st;
   if (!out) return fail(UW_E_ARG, "null output");
   if (!ws || ws_bytes < (size_t)kErrBytes) return fail(UW_E_WORKSPACE, "decode needs a %d-byte workspace", kErrBytes);
-  if (d->dec_spc <= 8 && mode != DEC_BF16) {
-    // Index and exponent output from chunks of at most eight rows: the register-image decoder,
-    // unless the code's 13-bit codes span more prefixes than its secondary table holds (then
-    // the general decoder below).  Full BF16 output stays with the general decoder (measured
-    // faster: 106 against 122 us on gate_proj 14336 x 4096, where its two-phase write costs
-    // less than the register image's BF16 write-out).
+  if (d->dec_spc <= 8) {
+    // Chunks of at most eight rows: the row decoder, unless the code's 13-bit codes span more
+    // prefixes than its secondary table holds (then the general decoder below).
     const uw_status rs = run_decode_rows(d, mode, out, reinterpret_cast<uint32_t*>(ws), max_wgs, s);
     if (rs != UW_E_SHAPE) return rs;
   }
