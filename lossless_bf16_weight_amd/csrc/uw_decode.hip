@@ -639,25 +639,19 @@ __device__ __forceinline__ void decode_unit(const RowDecArgs& a, uint32_t* lut, 
   uint32_t a4 = 0;                                              // its bits filled
   uint32_t* wp = buf;                                           // its place in the phase buffer
   uint32_t bad = 0;
-  // Index output: every two phases (four rows) are written as soon as they are decoded, so the
-  // output writes overlap the decode of later phases and only two phases' words are held in
-  // VGPRs.  A lane's four rows of one sub-tile are 32 contiguous bytes written by consecutive
-  // stores (one phase at a time, 16-byte pieces, the output took 2.8x its bytes in HBM writes).
-  // Exponent output (16-byte pieces, twice the bytes) keeps the chunk's image in VGPRs and
-  // writes it at the end, so that consecutive stores complete each output line: written a
-  // phase at a time it measured slower (77.6 against 57.3 us on the 8192 x 8192 heavy-tail
-  // matrix at 512-symbol chunks).
-  // BF16 output: a row is 128 contiguous bytes of W, whole lines, so it is written a phase (two
-  // rows) at a time, with the rows' sign+mantissa bytes loaded a phase ahead.
-  constexpr bool kPhaseWrite = MODE == DEC_IDX;
+  // Index and exponent output: every two phases (four rows) are written as soon as they are
+  // decoded, so the output writes overlap the decode of later phases and only two phases' words
+  // are held in VGPRs.  A lane's four rows of one sub-tile are contiguous: 64 bytes of exponents
+  // (a whole 64-byte segment: 1.01x the output bytes in HBM writes) or 32 bytes of indices (half
+  // a segment, the other half two phases later: 1.47x).  Written a phase at a time (16 or 32
+  // bytes) the output took 2.8x its bytes; written at the end of the chunk from an eight-row
+  // register image, 1.0x but slower (gate transcode 53.6 against 49.5 us, exponents 54.4 against
+  // 51.0 at 512-symbol chunks).  BF16 output: a row is 128 contiguous bytes of W, whole lines, so
+  // it is written a phase (two rows) at a time, with the rows' sign+mantissa bytes loaded a phase
+  // ahead.
   constexpr bool kBf16 = MODE == DEC_BF16;
-  uint32_t img[kPhaseWrite || kBf16 ? 1 : 64];
-  uint32_t grp[kPhaseWrite ? kPhaseWords : 1];   // the even phase's words, written with the odd one's
+  uint32_t grp[kBf16 ? 1 : kPhaseWords];         // the even phase's words, written with the odd one's
   int hdone = 0;
-  if constexpr (!kPhaseWrite) {
-#pragma unroll
-    for (int i = 0; i < 64; ++i) img[i] = 0;
-  }
 
   // Output places: chunk row q is the (j spc + q)-th coded row of the block; its 16-weight
   // groups g go to sub-tile (t, 4 blk + g) of the output stream.
@@ -692,17 +686,22 @@ __device__ __forceinline__ void decode_unit(const RowDecArgs& a, uint32_t* lut, 
     __builtin_amdgcn_raw_buffer_store_b128(o, ors, ok ? row * rowb + blk * 128u + (uint32_t)p * 16u : kOob, 0, 0);
   };
   u32x4 svp[kBf16 ? kPhaseRows : 1][4];         // the current phase's rows' sign+mantissa bytes
-  // Index rows q0 .. q0 + nq - 1 (words w[8 i .. 8 i + 7] of 4-bit indices in sequence order for
-  // row q0 + i) to the output, sub-tile by sub-tile.
+  // Rows q0 .. q0 + nq - 1 (words w[8 i .. 8 i + 7] of 4-bit indices in sequence order for row
+  // q0 + i) to the index or exponent output, sub-tile by sub-tile.
   auto put_rows = [&](int q0, int nq, const uint32_t* w) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
 #pragma unroll
       for (int i = 0; i < nq; ++i) {
         const int q = q0 + i;
-        const u32x2 v{nibbles_to_index_word(w[8 * i + 2 * g]), nibbles_to_index_word(w[8 * i + 2 * g + 1])};
-        __builtin_amdgcn_raw_buffer_store_b64(v, ors, q < nrows ? ((uint32_t)(bl * 4 + g) * 16 + rowq[q]) * 8 : kOob,
-                                              0, 0);
+        const uint32_t sub = (uint32_t)(bl * 4 + g) * 16 + rowq[q];
+        if constexpr (MODE == DEC_IDX) {
+          const u32x2 v{nibbles_to_index_word(w[8 * i + 2 * g]), nibbles_to_index_word(w[8 * i + 2 * g + 1])};
+          __builtin_amdgcn_raw_buffer_store_b64(v, ors, q < nrows ? sub * 8 : kOob, 0, 0);
+        } else {
+          const u32x2 e0 = seq_word_to_exps(w[8 * i + 2 * g], a.tab), e1 = seq_word_to_exps(w[8 * i + 2 * g + 1], a.tab);
+          __builtin_amdgcn_raw_buffer_store_b128(u32x4{e0.x, e0.y, e1.x, e1.y}, ors, q < nrows ? sub * 16 : kOob, 0, 0);
+        }
       }
     }
   };
@@ -771,7 +770,7 @@ __device__ __forceinline__ void decode_unit(const RowDecArgs& a, uint32_t* lut, 
     // Phase done for every lane: its rows 2h, 2h + 1 (16 finished words) to the output or the
     // image; the word in progress (a lookup's symbols past the phase) stays in lo and becomes
     // the buffer's first word.
-    if constexpr (kPhaseWrite) {
+    if constexpr (!kBf16) {
       if (h & 1) {
         uint32_t w[2 * kPhaseWords];
 #pragma unroll
@@ -785,7 +784,7 @@ __device__ __forceinline__ void decode_unit(const RowDecArgs& a, uint32_t* lut, 
         for (int i = 0; i < kPhaseWords; ++i) grp[i] = buf[i];
       }
       hdone = h + 1;
-    } else if constexpr (kBf16) {
+    } else {
       uint32_t w[kPhaseWords];
 #pragma unroll
       for (int i = 0; i < kPhaseWords; ++i) w[i] = buf[i];
@@ -802,9 +801,6 @@ __device__ __forceinline__ void decode_unit(const RowDecArgs& a, uint32_t* lut, 
           load_sm(rowq[q], q < nrows, svp[qq]);
         }
       }
-    } else {
-#pragma unroll
-      for (int i = 0; i < kPhaseWords; ++i) img[kPhaseWords * h + i] = buf[i];
     }
     wp = buf;
   }
@@ -814,24 +810,12 @@ __device__ __forceinline__ void decode_unit(const RowDecArgs& a, uint32_t* lut, 
   }
   if (bad) atomicOr(a.err, 1u);
 
-  if constexpr (kBf16) {
-  } else if constexpr (kPhaseWrite) {
+  if constexpr (!kBf16) {
     // A last, unpaired phase (constant row numbers: rowq is indexed at compile time).
     static_for<0, kPhases / 2>([&](auto pc) {
       constexpr int hp = 2 * decltype(pc)::value;
       if (hdone == hp + 1) put_rows(kPhaseRows * hp, kPhaseRows, grp);
     });
-  } else {
-    // The coded rows, sub-tile by sub-tile: consecutive stores complete each output line.
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const u32x2 e0 = seq_word_to_exps(img[8 * q + 2 * g], a.tab), e1 = seq_word_to_exps(img[8 * q + 2 * g + 1], a.tab);
-        __builtin_amdgcn_raw_buffer_store_b128(u32x4{e0.x, e0.y, e1.x, e1.y}, ors,
-                                               q < nrows ? ((uint32_t)(bl * 4 + g) * 16 + rowq[q]) * 16 : kOob, 0, 0);
-      }
-    }
   }
   // The lane's share of the block's other rows (rows j spc .. (j + 1) spc - 1 that are verbatim
   // or padding): the verbatim exponents or zeros.
