@@ -13,6 +13,12 @@
 
 using namespace uw;
 
+namespace uw {
+// The row decoder's lookup table for a matrix's code, built on the host and copied to the
+// current device's table cache (uw_decode.hip).  Does nothing without a device.
+void register_row_lut(const uw_info& info);
+}  // namespace uw
+
 extern "C" {
 
 size_t uw_dmat_size(void) { return sizeof(uw_dmat); }
@@ -63,6 +69,7 @@ uw_status uw_dmat_bind(uw_dmat* d, const void* blob_host, size_t bytes, const vo
     }
   }
   d->dec_stage_words = stage;
+  register_row_lut(info);
   d->magic = kDmatMagic;
   clear_error();
   return UW_OK;

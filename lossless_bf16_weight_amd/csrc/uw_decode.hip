@@ -8,6 +8,9 @@
 //  - Four-pipeline paragraphs: decode to BF16 (pipeline 1), to exponent bytes (2), or to 4-bit
 //    indices (3, and the load-time transcode of the direct-palette format).
 #include <climits>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
 
 #include "uw_device.h"
 
@@ -444,6 +447,7 @@ struct RowDecArgs {
   uint32_t pbase;           // first 12-bit prefix of a 13-bit code
   uint32_t nblk;            // prefixes of 13-bit codes (consecutive from pbase), <= 7
   uint32_t sec[kRowSec];    // secondary entries (same format as the primary ones)
+  const uint32_t* lut_src;  // the primary table, built on the host at bind time, or null (built here)
 };
 
 // Dynamic LDS of one workgroup of W waves: [phase buffers (before the decode: the table-build
@@ -519,6 +523,23 @@ __device__ void build_row_lut(const RowDecArgs& a, uint32_t* lut, uint16_t* tmp)
   lds_barrier();
 }
 
+// Smallest value v (< 2^BITS) over the lanes where act is set, 2^BITS when there are none; the
+// result is wave-uniform.  Bit slices from the top: the candidates keep the lanes whose bits
+// so far equal the minimum's (ballots only, no LDS round trips).
+template <int BITS>
+__device__ __forceinline__ uint32_t wave_min_small(uint32_t v, bool act) {
+  uint64_t cand = __builtin_amdgcn_ballot_w64(act);
+  if (!cand) return 1u << BITS;
+  uint32_t r = 0;
+#pragma unroll
+  for (int p = BITS - 1; p >= 0; --p) {
+    const uint64_t z = cand & __builtin_amdgcn_ballot_w64(((v >> p) & 1u) == 0u);
+    if (z) cand = z;
+    else r |= 1u << p;
+  }
+  return r;
+}
+
 // Sequential nibbles n0..n7 (n_i at bits 4i) -> 8 exponent bytes in column order.
 __device__ __forceinline__ u32x2 seq_word_to_exps(uint32_t v, const uint32_t tab[4]) {
   const uint32_t ev = lookup16(v & 0x0F0F0F0Fu, tab);          // E0 E2 E4 E6
@@ -557,6 +578,14 @@ __device__ __forceinline__ void decode_unit(const RowDecArgs& a, uint32_t* lut, 
   const uint16_t* flg = a.flags + (size_t)t * a.kb;
   uint32_t* stage = reinterpret_cast<uint32_t*>(dsh + a.stage_off + (uint32_t)wave * a.stage_words * 4u);
   uint32_t* const buf = reinterpret_cast<uint32_t*>(dsh + (uint32_t)wave * kBufBytes) + lane * kBufStride;
+  // A table built at bind time: its 16 one-kilobyte pieces go to LDS by LDS-DMA before any
+  // other load (wave w takes pieces w, w + W, ...), so they arrive with the first round trips.
+  if (first && a.lut_src) {
+    const int W = (int)(blockDim.x >> 6);
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.lut_src, kRowLut * 4u);
+    for (int pc = wave; pc < kRowLut * 4 / 1024; pc += W)
+      lds_dma16(rl, reinterpret_cast<uint8_t*>(lut) + pc * 1024, (uint32_t)pc * 1024u + (uint32_t)lane * 16u);
+  }
 
   // Chunks and verbatim segments of the tile's blocks before this unit; then this unit's
   // blocks (lane = block in unit): flags, chunk counts and exclusive prefixes.
@@ -623,8 +652,20 @@ __device__ __forceinline__ void decode_unit(const RowDecArgs& a, uint32_t* lut, 
   }
   const uint32_t p0 = has_chunk ? o_c0 - wb * 32u : 0u, p1 = has_chunk ? o_c1 - wb * 32u : 0u;
 
-  if (first)
-    build_row_lut(a, lut, reinterpret_cast<uint16_t*>(dsh));   // LDS barriers only: the DMAs stay in flight
+  if (first) {
+    if (a.lut_src) {
+      // The secondary entries from the kernel arguments; then every wave's table pieces (and
+      // stage) landed before any wave reads the table.
+      const int tid = (int)threadIdx.x;
+#pragma unroll
+      for (int i = 0; i < kRowSec; ++i)
+        if (tid == i) lut[kRowLut + i] = a.sec[i];
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      lds_barrier();
+    } else {
+      build_row_lut(a, lut, reinterpret_cast<uint16_t*>(dsh));   // LDS barriers only: the DMAs stay in flight
+    }
+  }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));                    // this wave's stage (and earlier stores)
   if (!unit_ok) return;
 
@@ -736,11 +777,38 @@ __device__ __forceinline__ void decode_unit(const RowDecArgs& a, uint32_t* lut, 
 #pragma unroll
   for (int h = 0; h < kPhases; ++h) {
     if (kPhaseRows * h >= wmax_rows) break;
-    // Phase h needs symbols up to 128 (h + 1) of the chunk: rem4 down to lim.
+    // Phase h needs symbols up to 128 (h + 1) of the chunk: rem4 down to lim.  Whole table
+    // entries are taken while rem4 is above fast_lim: in a phase that ends inside the chunk a
+    // lookup may run up to four symbols into the next phase (they start the next word), so
+    // fast_lim keeps five symbols' room; in the chunk's last phase entries run to the chunk's
+    // end, and the symbols a lookup takes past it stay in the word in progress, which is never
+    // written out (the chunk ends on a word boundary); the end check below takes their bits off.
     const int32_t lim = max(4 * (64 * nrows - 64 * kPhaseRows * (h + 1)), 0);
-    const int32_t fast_lim = max(lim, 4 * kRowMaxSyms - 1);
+    const int32_t fast_lim = lim > 0 ? max(lim, 4 * kRowMaxSyms - 1) : 0;
     while (true) {
-      // Hot loop: whole table entries while five or more symbols remain.
+      // A run of lookups that every lane still in the hot loop needs: a lookup takes at most
+      // five symbols, so a lane with rem4 above fast_lim takes at least ceil((rem4 - fast_lim)
+      // / 20) more.  The run has a wave-uniform trip count and no per-lookup exit test, which
+      // costs about 40 % of a lookup's time (a compare, mask updates and a branch that waits
+      // for them).  An entry of count 0 (a 13-bit code) changes no state, so a lane that meets
+      // one waits in place until the checked loop below.
+      {
+        const bool act = rem4 > fast_lim;
+        const uint32_t want = act ? min((uint32_t)(rem4 - fast_lim + 4 * kRowMaxSyms - 1) / (4u * kRowMaxSyms), 31u) : 0u;
+        const uint32_t run = wave_min_small<5>(want, act);
+        if (run < 32u && act) {
+          // LDS reads still in flight here would otherwise make the compiler wait for them at
+          // the top of every lookup (the wait sits at the loop header, where the paths merge).
+          __builtin_amdgcn_s_waitcnt(waitcnt_vm(63) & ~0x0F00);
+          for (uint32_t i = 0; i < run; ++i) {
+            const uint32_t win = __builtin_amdgcn_alignbit(w0, w1, s);
+            const uint32_t e = lut[win >> (32 - kRowWin)];
+            const uint32_t v = *np;
+            apply(e, v);
+          }
+        }
+      }
+      // Hot loop: whole table entries, each lane until its own limit.
       while (rem4 > fast_lim) {
         const uint32_t win = __builtin_amdgcn_alignbit(w0, w1, s);
         const uint32_t e = lut[win >> (32 - kRowWin)];
@@ -805,7 +873,16 @@ __device__ __forceinline__ void decode_unit(const RowDecArgs& a, uint32_t* lut, 
     wp = buf;
   }
   if (has_chunk) {
-    const uint32_t pos = (uint32_t)(np - (lds_cu32p)stage) * 32u - 32u - s;   // bits consumed from the slice start
+    // Bits consumed from the slice start, less the codes of the symbols taken past the chunk's
+    // end (-rem4 / 4 of them, in the low nibbles of the word in progress).
+    uint32_t over = 0;
+#pragma unroll
+    for (int i = 0; i < kRowMaxSyms - 1; ++i) {
+      const uint32_t sym = (lo >> (4 * i)) & 15u;
+      const uint32_t L = ((sym < 8 ? a.len_lo : a.len_hi) >> ((sym & 7u) * 4u)) & 15u;
+      over += 4 * i < -rem4 ? L : 0u;
+    }
+    const uint32_t pos = (uint32_t)(np - (lds_cu32p)stage) * 32u - 32u - s - over;
     if (pos != p1) bad = 1;
   }
   if (bad) atomicOr(a.err, 1u);
@@ -895,6 +972,116 @@ static int row_waves(uint32_t stage_words, int64_t units, int lds_wg_max, int ld
   return best_w;
 }
 
+// 13-bit codes: their 12-bit prefixes (consecutive in a canonical code) each get a block of two
+// secondary entries chosen by the 13th bit.  False when they span more prefixes than the
+// secondary table holds (then the general decoder takes the matrix).
+static bool row_code_prefixes(const uw_info& info, uint32_t* pbase, uint32_t* nblk) {
+  uint32_t lo = kRowLut, hi = 0;
+  for (int sym = 0; sym < 16; ++sym) {
+    const int L = info.code_len[sym];
+    if (L > kRowWin) {
+      lo = std::min<uint32_t>(lo, (uint32_t)info.code[sym] >> (L - kRowWin));
+      hi = std::max<uint32_t>(hi, (uint32_t)info.code[sym] >> (L - kRowWin));
+    }
+  }
+  *pbase = lo;
+  *nblk = lo < (uint32_t)kRowLut ? hi - lo + 1 : 0u;
+  return *nblk <= (uint32_t)kRowSecBlocks - 1;
+}
+
+// The primary table on the host, entry for entry as build_row_lut makes it: the greedy parse
+// of each 12-bit window into up to five whole codes.
+static void build_row_lut_host(const uw_info& info, uint32_t pbase, uint32_t nblk, uint32_t* lut) {
+  uint16_t first[kRowLut];
+  std::memset(first, 0, sizeof(first));
+  for (int s = 0; s < 16; ++s) {
+    const int L = info.code_len[s];
+    if (L == 0 || L > kRowWin) continue;
+    const uint32_t lo = (uint32_t)info.code[s] << (kRowWin - L), cnt = 1u << (kRowWin - L);
+    for (uint32_t i = 0; i < cnt; ++i) first[lo + i] = (uint16_t)(s | (L << 4) | 0x100);
+  }
+  for (uint32_t w = 0; w < (uint32_t)kRowLut; ++w) {
+    if (!(first[w] & 0x100u)) {
+      const uint32_t i = w - pbase;
+      lut[w] = i < nblk ? (i + 1u) << 9 : 0u;
+      continue;
+    }
+    uint32_t used = (first[w] >> 4) & 15u, n = 1, syms = first[w] & 15u;
+    while (n < (uint32_t)kRowMaxSyms) {
+      const uint32_t ej = first[(w << used) & (kRowLut - 1)], lj = (ej >> 4) & 15u;
+      if (!(ej & 0x100u) || used + lj > (uint32_t)kRowWin) break;
+      syms |= (ej & 15u) << (4 * n);
+      used += lj;
+      ++n;
+    }
+    lut[w] = (syms << 12) | (4u * n << 4) | used;
+  }
+}
+
+// Tables built at bind time, one per code, in a per-device array of fixed size (no allocation;
+// each GPU holds its copy until the process ends).  The key is the 16 code lengths (the table
+// depends on nothing else).  A full cache, or a call on another device than the bind's, leaves
+// the kernel to build the table itself, and so does the environment variable
+// UW_ROW_TABLE_IN_KERNEL (set to anything; read at every bind and call; for tests of that path).
+constexpr int kLutSlots = 128;
+static __device__ __align__(256) uint32_t g_row_luts[kLutSlots * kRowLut];
+namespace {
+struct LutCache {
+  std::mutex mu;
+  bool init = false;
+  uint32_t* base = nullptr;
+  int used = 0;
+  uint8_t key[kLutSlots][16];
+};
+LutCache g_lut_cache[64];
+}  // namespace
+
+static const uint32_t* row_lut_find(LutCache& c, const uw_info& info) {
+  for (int i = 0; i < c.used; ++i)
+    if (std::memcmp(c.key[i], info.code_len, 16) == 0) return c.base + (size_t)i * kRowLut;
+  return nullptr;
+}
+
+static bool row_table_in_kernel() { return std::getenv("UW_ROW_TABLE_IN_KERNEL") != nullptr; }
+
+void register_row_lut(const uw_info& info) {
+  if (row_table_in_kernel()) return;
+  uint32_t pbase = 0, nblk = 0;
+  if (info.chunk / kSeg > 8 || !row_code_prefixes(info, &pbase, &nblk)) return;   // the general decoder's case
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return;
+  }
+  LutCache& c = g_lut_cache[dev];
+  std::lock_guard<std::mutex> lock(c.mu);
+  if (!c.init) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_row_luts)) != hipSuccess) {
+      (void)hipGetLastError();
+      p = nullptr;
+    }
+    c.base = reinterpret_cast<uint32_t*>(p);
+    c.init = true;
+  }
+  if (!c.base || c.used == kLutSlots || row_lut_find(c, info)) return;
+  static thread_local uint32_t table[kRowLut];
+  build_row_lut_host(info, pbase, nblk, table);
+  if (hipMemcpy(c.base + (size_t)c.used * kRowLut, table, sizeof(table), hipMemcpyHostToDevice) != hipSuccess) {
+    (void)hipGetLastError();
+    return;
+  }
+  std::memcpy(c.key[c.used], info.code_len, 16);
+  ++c.used;
+}
+
+static const uint32_t* row_lut_lookup(const uw_info& info, int dev) {
+  if (dev < 0 || dev >= 64 || row_table_in_kernel()) return nullptr;
+  LutCache& c = g_lut_cache[dev];
+  std::lock_guard<std::mutex> lock(c.mu);
+  return c.base ? row_lut_find(c, info) : nullptr;
+}
+
 static uw_status run_decode_rows(const uw_dmat* d, int mode, uint8_t* out, uint32_t* err, int max_wgs, hipStream_t s) {
   RowDecArgs a;
   std::memset(&a, 0, sizeof(a));
@@ -927,19 +1114,7 @@ static uw_status run_decode_rows(const uw_dmat* d, int mode, uint8_t* out, uint3
     const uint32_t L = d->info.code_len[sym];
     if (sym < 8) a.len_lo |= L << (4 * sym); else a.len_hi |= L << (4 * (sym - 8));
   }
-  // 13-bit codes: their 12-bit prefixes (consecutive in a canonical code) each get a block of
-  // two secondary entries chosen by the 13th bit.
-  a.pbase = kRowLut;
-  uint32_t plast = 0;
-  for (int sym = 0; sym < 16; ++sym) {
-    const int L = d->info.code_len[sym];
-    if (L > kRowWin) {
-      a.pbase = std::min<uint32_t>(a.pbase, (uint32_t)d->info.code[sym] >> (L - kRowWin));
-      plast = std::max<uint32_t>(plast, (uint32_t)d->info.code[sym] >> (L - kRowWin));
-    }
-  }
-  a.nblk = a.pbase < (uint32_t)kRowLut ? plast - a.pbase + 1 : 0u;
-  if (a.nblk > (uint32_t)kRowSecBlocks - 1) return UW_E_SHAPE;   // the general decoder takes it
+  if (!row_code_prefixes(d->info, &a.pbase, &a.nblk)) return UW_E_SHAPE;   // the general decoder takes it
   for (int sym = 0; sym < 16; ++sym) {
     const int L = d->info.code_len[sym];
     if (L <= kRowWin) continue;
@@ -961,6 +1136,7 @@ static uw_status run_decode_rows(const uw_dmat* d, int mode, uint8_t* out, uint3
     cache[dev][3] = std::max(v[2], 1);
     cache[dev][0] = 1;
   }
+  a.lut_src = row_lut_lookup(d->info, dev);
   const int W = row_waves(a.stage_words, units, cache[dev][1], cache[dev][2], cache[dev][3]);
   if (W == 0) return fail(UW_E_SHAPE, "decoder unit needs more LDS than the device allows");
   a.stage_off = row_buf_area(W);

@@ -116,6 +116,38 @@ def test_decoders_bit_exact(name, chunk):
     assert ex.cpu().numpy().tobytes() == codec.exponent_stream_blob(ref_blob).tobytes()
 
 
+@pytest.mark.parametrize("name", ["tiles_160x1024", "student_t_48x1024", "ragged_37x192"] + list(DECODE_ONLY))
+@pytest.mark.parametrize("chunk", [256, 512])
+@pytest.mark.parametrize("in_kernel", [True, False])
+def test_row_decoder_table_source(name, chunk, in_kernel, monkeypatch):
+    """The row decoder's lookup table either comes from the table built on the host at bind
+    time (LDS-DMA) or is built by each workgroup (UW_ROW_TABLE_IN_KERNEL, also the path when the
+    per-device table cache is full): both decode bit-exact against the oracle."""
+    if in_kernel:
+        monkeypatch.setenv("UW_ROW_TABLE_IN_KERNEL", "1")
+    else:
+        monkeypatch.delenv("UW_ROW_TABLE_IN_KERNEL", raising=False)
+    t = torch()
+    w = {**CASES, **DECODE_ONLY}[name]()
+    n, k = w.shape
+    blob = uw.uw_encode(w, chunk)
+    ref_blob = codec.serialize(codec.encode(w, n, k, chunk=chunk))
+    cm = uw.CompressedMatrix(w, chunk=chunk, blob=blob)
+    ws = err_ws()
+    out = t.empty((n, k), dtype=t.int16, device="cuda")
+    uw.uw_decode_full(cm.d, out, ws)
+    uw.uw_check(ws)
+    assert np.array_equal(host_u16(out), w)
+    idx = t.empty(int(cm.info["idx_bytes"]), dtype=t.uint8, device="cuda")
+    uw.uw_transcode_palette(cm.d, idx, ws)
+    uw.uw_check(ws)
+    assert idx.cpu().numpy().tobytes() == codec.transcode_blob(ref_blob).tobytes()
+    ex = t.empty(int(cm.info["np"]) * k, dtype=t.uint8, device="cuda")
+    uw.uw_decode_exponents(cm.d, ex, ws)
+    uw.uw_check(ws)
+    assert ex.cpu().numpy().tobytes() == codec.exponent_stream_blob(ref_blob).tobytes()
+
+
 @settings(max_examples=25, deadline=None, derandomize=True, suppress_health_check=[HealthCheck.too_slow])
 @given(matrices(max_rows=70, max_blocks=8), st.sampled_from([64, 256, 512]), st.integers(1, 40))
 def test_generated_matrices(w, chunk, m):
