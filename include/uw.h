@@ -222,8 +222,8 @@ uw_status uw_gemm_bf16(const uint16_t* w, int64_t n, int64_t k, const uint16_t* 
 
 /* Kernel variants: count, and a description string of one: "waves=W unroll=U" (per-tile
  * kernel), "multitile tiles=W unroll=U", "shared-x tiles=W unroll=U" (M <= 16),
- * "wide pairs=W unroll=U" or "big tile=NxM" (large batches, palette sources; others run the
- * default multi-tile variant).  Every variant computes any shape and batch size the entry
+ * "wide pairs=W unroll=U", "big tile=NxM" or "big tile=NxM waves=8" (large batches, palette
+ * sources; others run the default multi-tile variant).  Every variant computes any shape and batch size the entry
  * points accept; a variant whose conditions a call does not meet runs a default instead. */
 int32_t uw_variant_count(void);
 const char* uw_variant_name(int32_t variant);

@@ -1004,13 +1004,16 @@ struct BigW {
   u32x4 ev;
 };
 
-template <int SRC, int WN, int WM, int D>
-__global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a, float* part, int S) {
+template <int SRC, int WN, int WM, int D, int NWM>
+__global__ __launch_bounds__(128 * NWM) void k_gemm_big(GemmArgs a, float* part, int S) {
   static_assert(SRC <= SRC_PAL_LUT, "palette sources only");
   constexpr int BN = 64 * WN, BM = 64 * WM;
-  constexpr int TW = BN / 64;                 // tiles a wave rebuilds
+  constexpr int NW = 2 * NWM;                 // waves: 2 along the weight rows, NWM along X
+  constexpr int CM = 2 * WM / NWM;            // 32-row X tiles a wave multiplies
+  constexpr int TW = BN / 16 / NW;            // tiles a wave rebuilds
   constexpr int ABYTES = BN * 128, BBYTES = BM * 128;
-  constexpr int XD = BM / 32;                 // X DMAs (1 KB) a wave issues per block
+  constexpr int XD = BBYTES / 1024 / NW;      // X DMAs (1 KB) a wave issues per block
+  static_assert(TW >= 1 && TW * 16 * NW == BN && XD >= 1 && XD * 1024 * NW == BBYTES && CM * NWM == 2 * WM, "tile split");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1097,17 +1100,17 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a, float* part, int S
     }
   };
 
-  const int wn = wave >> 1, wm = wave & 1;
+  const int wn = wave / NWM, wm = wave % NWM;
   const int xr = lane & 31, hh = lane >> 5;
-  floatx16 acc[WN][WM];
+  floatx16 acc[WN][CM];
 #pragma unroll
   for (int p = 0; p < WN; ++p)
 #pragma unroll
-    for (int c = 0; c < WM; ++c)
+    for (int c = 0; c < CM; ++c)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[p][c][e] = 0.f;
   // The operands of k-step st + 1 are read from LDS before the MFMAs of step st are issued.
-  auto load_frags = [&](const uint8_t* A, const uint8_t* B, int st, u32x4 (&av)[WN], u32x4 (&bv)[WM]) __attribute__((always_inline)) {
+  auto load_frags = [&](const uint8_t* A, const uint8_t* B, int st, u32x4 (&av)[WN], u32x4 (&bv)[CM]) __attribute__((always_inline)) {
     const int gr = 2 * st + hh;
 #pragma unroll
     for (int p = 0; p < WN; ++p) {
@@ -1115,18 +1118,18 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a, float* part, int S
       av[p] = *reinterpret_cast<const u32x4*>(A + row * 128 + ((gr ^ ((row >> 1) & 7)) * 16));
     }
 #pragma unroll
-    for (int c = 0; c < WM; ++c) {
-      const int row = wm * 32 * WM + c * 32 + xr;
+    for (int c = 0; c < CM; ++c) {
+      const int row = wm * 32 * CM + c * 32 + xr;
       bv[c] = *reinterpret_cast<const u32x4*>(B + row * 128 + ((gr ^ ((row >> 1) & 7)) * 16));
     }
   };
   auto compute = [&](const uint8_t* A, const uint8_t* B) __attribute__((always_inline)) {
-    u32x4 av0[WN], bv0[WM], av1[WN], bv1[WM];
+    u32x4 av0[WN], bv0[CM], av1[WN], bv1[CM];
     load_frags(A, B, 0, av0, bv0);
     static_for<0, 4>([&](auto sc) __attribute__((always_inline)) {
       constexpr int st = decltype(sc)::value;
       u32x4 (&av)[WN] = (st & 1) ? av1 : av0;
-      u32x4 (&bv)[WM] = (st & 1) ? bv1 : bv0;
+      u32x4 (&bv)[CM] = (st & 1) ? bv1 : bv0;
       if constexpr (st + 1 < 4) {
         if constexpr (st & 1) load_frags(A, B, st + 1, av0, bv0);
         else load_frags(A, B, st + 1, av1, bv1);
@@ -1134,7 +1137,7 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a, float* part, int S
 #pragma unroll
       for (int p = 0; p < WN; ++p)
 #pragma unroll
-        for (int c = 0; c < WM; ++c)
+        for (int c = 0; c < CM; ++c)
           acc[p][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[p]),
                                                               __builtin_bit_cast(bf16x8, bv[c]), acc[p][c], 0, 0, 0);
     });
@@ -1196,9 +1199,9 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a, float* part, int S
   // D lane layout (32x32): X row (column of D) lane % 32 of column tile c; register e holds
   // weight row 8 (e / 4) + 4 hh + e % 4 of row pair p.  Unrolled at compile time (static_for):
   // an accumulator array indexed at run time would live in scratch memory.
-  static_for<0, WN * WM * 4>([&](auto ic) __attribute__((always_inline)) {
-    constexpr int p = decltype(ic)::value / (4 * WM), c = decltype(ic)::value / 4 % WM, qd = decltype(ic)::value % 4;
-    const int mm = mcol0 + wm * 32 * WM + c * 32 + xr;
+  static_for<0, WN * CM * 4>([&](auto ic) __attribute__((always_inline)) {
+    constexpr int p = decltype(ic)::value / (4 * CM), c = decltype(ic)::value / 4 % CM, qd = decltype(ic)::value % 4;
+    const int mm = mcol0 + wm * 32 * CM + c * 32 + xr;
     const int n0 = rg * BN + wn * 32 * WN + p * 32 + 8 * qd + 4 * hh;
     if (mm >= a.m || n0 >= a.n) return;
     const floatx4 v{acc[p][c][4 * qd], acc[p][c][4 * qd + 1], acc[p][c][4 * qd + 2], acc[p][c][4 * qd + 3]};
@@ -1296,7 +1299,8 @@ __global__ __launch_bounds__(1024) void k_reduce_rmsnorm(const float* part, floa
 // kind 3 = wide-tile kernel (`waves` tile pairs a workgroup, 128 X rows a chunk, batches of
 // `unroll` blocks; palette sources, other sources run the default multi-tile variant),
 // kind 4 = big-tile kernel (64 * `waves` weight rows x 64 * `unroll` X rows a workgroup, W
-// rebuilt once a block into LDS; palette sources, others run the default multi-tile variant).
+// rebuilt once a block into LDS; palette sources, others run the default multi-tile variant);
+// kind 5 = the big-tile kernel with the same tile split over eight waves (two a SIMD).
 struct Variant {
   int kind;
   int waves;
@@ -1304,7 +1308,7 @@ struct Variant {
 };
 static const Variant kVariants[] = {{0, 4, 8}, {0, 2, 8}, {0, 8, 8},  {0, 16, 8}, {0, 1, 8}, {0, 4, 4}, {0, 2, 4},
                                     {0, 8, 4}, {0, 16, 4}, {0, 1, 4}, {1, 8, 4},  {1, 4, 4}, {1, 8, 2}, {1, 4, 2},
-                                    {2, 2, 4}, {2, 4, 4}, {3, 4, 2}, {3, 8, 2}, {4, 2, 2}, {4, 2, 4}};
+                                    {2, 2, 4}, {2, 4, 4}, {3, 4, 2}, {3, 8, 2}, {4, 2, 2}, {4, 2, 4}, {5, 2, 4}};
 static constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 static constexpr int kMtDefault = 10;   // {1, 8, 4}
 
@@ -1366,7 +1370,7 @@ static int big_slices(int64_t tiles, int WN, int WM, int64_t kb, int m) {
 int64_t mt_max_slices(int64_t kb, int64_t tiles, int m) {
   int64_t S = std::max(slices_for(tiles * m_chunks(m), kb), slices_for((tiles + 1) / 2 * wide_chunks(m), kb));
   for (int v = 0; v < kNumVariants; ++v)
-    if (kVariants[v].kind == 4) S = std::max<int64_t>(S, big_slices(tiles, kVariants[v].waves, kVariants[v].unroll, kb, m));
+    if (kVariants[v].kind >= 4) S = std::max<int64_t>(S, big_slices(tiles, kVariants[v].waves, kVariants[v].unroll, kb, m));
   return S;
 }
 
@@ -1453,10 +1457,10 @@ static hipError_t launch_wide_t(const GemmArgs& a, int64_t tiles, int S, float* 
   return launch_reduce(a, S, part, s);
 }
 
-template <int SRC, int WN, int WM, int D>
+template <int SRC, int WN, int WM, int D, int NWM>
 static hipError_t launch_big_t(const GemmArgs& a, int64_t tiles, int S, float* part, hipStream_t s) {
   const dim3 grid((unsigned)((tiles * 16 + 64 * WN - 1) / (64 * WN)), (unsigned)S, (unsigned)((a.m + 64 * WM - 1) / (64 * WM)));
-  hipLaunchKernelGGL((k_gemm_big<SRC, WN, WM, D>), grid, dim3(256), big_lds(WN, WM, D), s, a, S > 1 ? part : nullptr, S);
+  hipLaunchKernelGGL((k_gemm_big<SRC, WN, WM, D, NWM>), grid, dim3(128 * NWM), big_lds(WN, WM, D), s, a, S > 1 ? part : nullptr, S);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
   return launch_reduce(a, S, part, s);
@@ -1466,9 +1470,10 @@ static hipError_t launch_big_t(const GemmArgs& a, int64_t tiles, int S, float* p
 // tiles need 256 accumulator registers a wave and run out of scalar registers for the stream
 // descriptors.)
 template <int SRC>
-static hipError_t launch_big(const GemmArgs& a, int64_t tiles, int WM, int S, float* part, hipStream_t s) {
-  return WM == 4 ? launch_big_t<SRC, 2, 4, kBigDepth>(a, tiles, S, part, s)
-                 : launch_big_t<SRC, 2, 2, kBigDepth>(a, tiles, S, part, s);
+static hipError_t launch_big(const GemmArgs& a, int64_t tiles, int WM, bool eight, int S, float* part, hipStream_t s) {
+  if (eight) return launch_big_t<SRC, 2, 4, kBigDepth, 4>(a, tiles, S, part, s);
+  return WM == 4 ? launch_big_t<SRC, 2, 4, kBigDepth, 2>(a, tiles, S, part, s)
+                 : launch_big_t<SRC, 2, 2, kBigDepth, 2>(a, tiles, S, part, s);
 }
 
 // Batches of 2 blocks only: 4 would spill at 8 waves a workgroup.
@@ -1560,9 +1565,9 @@ int plan_gemm(int src, const GemmArgs& a, int64_t tiles, int* variant, const flo
   if (*variant < 0) *variant = a.m > 16 ? kMtDefault : default_variant(tiles, a.kb, ct, a.m);
   if (kVariants[*variant].kind >= 3 && !pal) *variant = kMtDefault;
   const int kind = kVariants[*variant].kind;
-  if (kind != 1 && kind != 3 && kind != 4) return 0;
+  if (kind != 1 && kind != 3 && kind < 4) return 0;
   const int R = kVariants[*variant].waves;
-  int S = kind == 4 ? big_slices(tiles, R, kVariants[*variant].unroll, a.kb, a.m)
+  int S = kind >= 4 ? big_slices(tiles, R, kVariants[*variant].unroll, a.kb, a.m)
                     : kind == 3 ? wide_slices(tiles, R, a.kb, a.m) : mt_slices(tiles, R, a.kb, a.m);
   const size_t plane = (size_t)a.m * a.n * sizeof(float);
   if (S > 1 && (!part || part_bytes < (size_t)S * plane))
@@ -1592,10 +1597,11 @@ uw_status run_gemm(int src, const GemmArgs& a, int64_t tiles, int variant, float
                           size_t part_bytes, hipStream_t s) {
   int ct = col_tiles(a.m);
   const int S = plan_gemm(src, a, tiles, &variant, part, part_bytes);
-  if (S > 0 && kVariants[variant].kind == 4) {
+  if (S > 0 && kVariants[variant].kind >= 4) {
     const int WM = kVariants[variant].unroll;
-    const hipError_t e = src == SRC_PAL_AFFINE ? launch_big<SRC_PAL_AFFINE>(a, tiles, WM, S, part, s)
-                                               : launch_big<SRC_PAL_LUT>(a, tiles, WM, S, part, s);
+    const bool eight = kVariants[variant].kind == 5;
+    const hipError_t e = src == SRC_PAL_AFFINE ? launch_big<SRC_PAL_AFFINE>(a, tiles, WM, eight, S, part, s)
+                                               : launch_big<SRC_PAL_LUT>(a, tiles, WM, eight, S, part, s);
     if (e != hipSuccess) return fail(UW_E_HIP, "gemm launch: %s", hipGetErrorString(e));
     return UW_OK;
   }
@@ -1678,6 +1684,9 @@ const char* uw_variant_name(int32_t variant) {
              kVariants[variant].unroll);
   else if (kVariants[variant].kind == 4)
     snprintf(names[variant], sizeof(names[variant]), "big tile=%dx%d", 64 * kVariants[variant].waves,
+             64 * kVariants[variant].unroll);
+  else if (kVariants[variant].kind == 5)
+    snprintf(names[variant], sizeof(names[variant]), "big tile=%dx%d waves=8", 64 * kVariants[variant].waves,
              64 * kVariants[variant].unroll);
   else
     snprintf(names[variant], sizeof(names[variant]), "multitile tiles=%d unroll=%d", kVariants[variant].waves,

@@ -243,10 +243,10 @@ def test_caller_palette_end_to_end(shift, swap):
             check_gemm(y, x, w)
 
 
-N_VARIANTS = 20
+N_VARIANTS = 21
 SHARED_X_VARIANTS = (14, 15)   # kind 2: whole tiles per wave, X rows shared in LDS
 WIDE_VARIANTS = (16, 17)       # kind 3: tile pairs per wave, 32x32 MFMAs (palette sources)
-BIG_VARIANTS = (18, 19)        # kind 4: W rebuilt once a block into LDS, 32x32 MFMAs (palette sources)
+BIG_VARIANTS = (18, 19, 20)    # kinds 4, 5: W rebuilt once a block into LDS, 32x32 MFMAs (palette sources)
 
 
 def test_variant_count():
