@@ -150,6 +150,12 @@ size_t uw_dmat_size(void);
  * blob_dev:  device copy of the same bytes (must stay valid while d is used).
  * idx_dev:   device buffer of uw_info.idx_bytes for the direct-palette index stream, or NULL
  *            (then UW_PIPE_DIRECT_PALETTE is refused with UW_E_ARG).
+ * With a current device, the call also builds the Huffman decoder's 16 KB lookup table for the
+ * blob's code lengths and copies it (synchronously, once per distinct code) into a fixed
+ * per-device table cache of 128 codes; decode calls on that device then load the table instead
+ * of building it in every workgroup.  Without a device, with a full cache, on another device or
+ * with UW_ROW_TABLE_IN_KERNEL set in the environment, the decoder builds the table itself
+ * (same results).  A failed copy is not an error.
  * Errors: UW_E_ARG, UW_E_FORMAT. */
 uw_status uw_dmat_bind(uw_dmat* d, const void* blob_host, size_t bytes, const void* blob_dev,
                        void* idx_dev);
