@@ -1100,14 +1100,21 @@ __global__ __launch_bounds__(128 * NWM) void k_gemm_big(GemmArgs a, float* part,
       sl[j].w.s = bload16_nt(srs, ok ? so[j] : kOob, b * 1024);
       sl[j].w.i = bload8_nt(irs, ok ? io[j] : kOob, b * 512);
     }
-    // Masks, not branches: the multiply and rebuild of a block stay one basic block.
+    // Masks, not branches, inside: the multiply and rebuild of a block stay one basic block.
+    // The verbatim-exponent loads go out only when one of the wave's tiles has a verbatim row
+    // in the block (a wave-uniform test); the waits count none of them.
     const uint32_t okm = 0u - (uint32_t)ok;
+    uint32_t fv = 0;
 #pragma unroll
-    for (int j = 0; j < TW; ++j) {
-      const uint32_t f = __builtin_amdgcn_readlane(wfl[j], jb) & okm;
-      const uint32_t rank = __builtin_amdgcn_readlane(wvp[j], jb) + (uint32_t)__popc(f & ((1u << r) - 1u));
-      const uint32_t vm = 0u - ((f >> r) & 1u);
-      sl[j].ev = bload16(vrs, ((rank * 64 + g * 16) & vm) | (kOob & ~vm));
+    for (int j = 0; j < TW; ++j) fv |= __builtin_amdgcn_readlane(wfl[j], jb) & okm;
+    if (fv) {
+#pragma unroll
+      for (int j = 0; j < TW; ++j) {
+        const uint32_t f = __builtin_amdgcn_readlane(wfl[j], jb) & okm;
+        const uint32_t rank = __builtin_amdgcn_readlane(wvp[j], jb) + (uint32_t)__popc(f & ((1u << r) - 1u));
+        const uint32_t vm = 0u - ((f >> r) & 1u);
+        sl[j].ev = bload16(vrs, ((rank * 64 + g * 16) & vm) | (kOob & ~vm));
+      }
     }
   };
   auto rebuild_to_lds = [&](int b, const BigW<SRC> (&sl)[TW], uint8_t* buf) __attribute__((always_inline)) {
@@ -1182,13 +1189,19 @@ __global__ __launch_bounds__(128 * NWM) void k_gemm_big(GemmArgs a, float* part,
   // slice are loaded out of range (zeros, no traffic) and rebuilt into a buffer no one
   // multiplies.  One block's multiply and the next one's rebuild form one branch-free
   // region, which the scheduler is free to interleave.
-  constexpr int NL = XD + 3 * TW;
+  constexpr int NL = XD + 2 * TW;            // loads a wave issues per block, verbatim exponents aside
   static_assert(NL * (D - 1) <= 63, "vmcnt range");
   uint8_t* const abase = smem;
   uint8_t* const xbase = smem + 2 * ABYTES;
   auto abuf = [&](int j) __attribute__((always_inline)) { return abase + (j & 1) * ABYTES; };
   auto xbuf = [&](int j) __attribute__((always_inline)) { return xbase + (j % (D + 1)) * BBYTES; };
   BigW<SRC> sl[D][TW];
+  // A block without verbatim rows loads no exponents and the rebuild's select masks them out:
+  // start them defined.
+#pragma unroll
+  for (int jd = 0; jd < D; ++jd)
+#pragma unroll
+    for (int j = 0; j < TW; ++j) sl[jd][j].ev = u32x4{0, 0, 0, 0};
   static_for<0, D>([&](auto jc) __attribute__((always_inline)) {
     constexpr int j = decltype(jc)::value;
     issue_x(bs + j, xbuf(j));
