@@ -1007,11 +1007,12 @@ __global__ __launch_bounds__(64 * R) void k_gemm_wide(GemmArgs a, float* part, i
 //
 // The wide-tile kernel rebuilds a wave's weights for every 128-column X chunk, so at M in the
 // hundreds the rebuild runs M/128 times over and its X reads from LDS feed only 32 weight
-// rows.  Here a workgroup of four waves owns a BN x BM output tile (BN = 64 WN weight rows,
+// rows.  Here a workgroup of 2 x NWM waves owns a BN x BM output tile (BN = 64 WN weight rows,
 // BM = 64 WM X rows) and walks K one 64-column block at a time: the block's BN weight rows are
 // rebuilt once, by the whole workgroup, into LDS as BF16, its BM X rows are staged by
-// LDS-DMA, and each wave multiplies one (BN/2) x (BM/2) quarter with 32x32x16 MFMAs, both
-// operands read from LDS.  Two blocks deep: while one block is multiplied, the next one's
+// LDS-DMA, and each wave multiplies one (BN/2) x (BM/NWM) part with 32x32x16 MFMAs, both
+// operands read from LDS (NWM = 4: two waves a SIMD, so one wave's issue stalls overlap the
+// other's MFMAs).  Two blocks deep: while one block is multiplied, the next one's
 // rebuilt weights and X rows are ready or landing and the one after is requested; one barrier
 // a block.  LDS rows are 128 bytes (64 BF16), half the 64 banks; the 16-byte granule g of row
 // r sits at position g ^ ((r >> 1) & 7), so any 16 consecutive rows' reads or writes of one
