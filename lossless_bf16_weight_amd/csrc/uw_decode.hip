@@ -409,7 +409,11 @@ __global__ __launch_bounds__(64) void k_decode(DecArgs a) {
 //   starts a 13-bit code (bits 9-11: block of two secondary entries chosen by the 13th bit;
 //   block 0 is all invalid) or no code; such an entry changes nothing, and the lane leaves the
 //   hot loop for one slow step, which also takes the last one to four symbols of a chunk one
-//   at a time (a lookup must not take symbols of the next chunk).
+//   at a time (a lookup must not take symbols of the next chunk).  The encoders limit codes to
+//   12 bits, so their blobs never take that path for a code; a blob written at the format's
+//   13-bit limit does, and each such code costs its wave dearly: the lane waits in place until
+//   every other lane has finished the phase, then decodes the rest of it alone (on gate_proj
+//   written at 13 bits, where a wave meets one in most phases: transcode 40.7 against 33.4 us).
 // =========================================================================================
 constexpr int kRowWin = 12;                 // lookup window, bits
 constexpr int kRowLut = 1 << kRowWin;       // primary entries
@@ -751,10 +755,23 @@ __device__ __forceinline__ void decode_unit(const RowDecArgs& a, uint32_t* lut, 
   // progress is stored at every lookup (complete or not), so a finished word is already in the
   // buffer when wp moves on; the symbols past it start the next word (a word boundary is never
   // crossed at a4 = 0: an entry holds at most 20 bits, so the shift by 32 - a4 is then unused).
-  auto apply = [&](uint32_t e, uint32_t v) {
-    const uint32_t L = e & 15u, n4 = entry_n4(e), sy = e >> 12;
+  // The two halves are separate so that a loop can move the window and send the next lookup's
+  // table read before it places this entry's symbols: the wave issues in order, so symbols
+  // placed first would sit on the serial chain from one table read to the next.
+  auto step = [&](uint32_t e, uint32_t v) {                    // the bit window
+    const int32_t sl = (int32_t)s - (int32_t)(e & 15u);
+    const bool neg = sl < 0;
+    s = (uint32_t)sl & 31u;
+    w0 = neg ? w1 : w0;
+    w1 = neg ? v : w1;
+    np = advance_word(np, (uint32_t)sl >> 31);
+  };
+  // The symbols: put stores the word in progress with them (first in a pipelined lookup, so the
+  // store is not the LDS operation the next lookup's wait ends on), place moves on.
+  auto put = [&](uint32_t e) { *wp = ((e >> 12) << a4) | lo; };
+  auto place = [&](uint32_t e) {
+    const uint32_t n4 = entry_n4(e), sy = e >> 12;
     const uint32_t lo2 = (sy << a4) | lo;
-    *wp = lo2;
     const uint32_t a4n = a4 + n4;
     const uint32_t carry = sy >> ((32u - a4) & 31u);
     const bool done = a4n >= 32u;
@@ -762,13 +779,17 @@ __device__ __forceinline__ void decode_unit(const RowDecArgs& a, uint32_t* lut, 
     a4 = a4n & 31u;
     wp += done ? 1 : 0;
     rem4 -= (int32_t)n4;
-    const int32_t sl = (int32_t)s - (int32_t)L;
-    const bool neg = sl < 0;
-    w0 = neg ? w1 : w0;
-    w1 = neg ? v : w1;
-    np = advance_word(np, (uint32_t)sl >> 31);
-    s = (uint32_t)sl & 31u;
   };
+  auto apply = [&](uint32_t e, uint32_t v) {
+    put(e);
+    step(e, v);
+    place(e);
+  };
+  // The compiler would otherwise fold a loop's two reads of the next entry (before the loop and
+  // at its end) into one read at the top of the loop, which undoes the pipelining: a barrier to
+  // memory motion (no instruction) after the end-of-loop read prevents it.
+  auto keep_reads_here = []() { asm volatile("" ::: "memory"); };
+  auto lookup = [&]() { return lut[__builtin_amdgcn_alignbit(w0, w1, s) >> (32 - kRowWin)]; };
 
   if constexpr (kBf16) {
 #pragma unroll
@@ -800,21 +821,33 @@ __device__ __forceinline__ void decode_unit(const RowDecArgs& a, uint32_t* lut, 
           // LDS reads still in flight here would otherwise make the compiler wait for them at
           // the top of every lookup (the wait sits at the loop header, where the paths merge).
           __builtin_amdgcn_s_waitcnt(waitcnt_vm(63) & ~0x0F00);
+          // Pipelined by one lookup: the reads after the last one are not used (LDS reads past
+          // the stage stay inside the workgroup's LDS or read zeros).
+          uint32_t e = lookup(), v = *np;
           for (uint32_t i = 0; i < run; ++i) {
-            const uint32_t win = __builtin_amdgcn_alignbit(w0, w1, s);
-            const uint32_t e = lut[win >> (32 - kRowWin)];
-            const uint32_t v = *np;
-            apply(e, v);
+            put(e);
+            step(e, v);
+            const uint32_t en = lookup(), vn = *np;
+            keep_reads_here();
+            place(e);
+            e = en;
+            v = vn;
           }
         }
       }
-      // Hot loop: whole table entries, each lane until its own limit.
-      while (rem4 > fast_lim) {
-        const uint32_t win = __builtin_amdgcn_alignbit(w0, w1, s);
-        const uint32_t e = lut[win >> (32 - kRowWin)];
-        const uint32_t v = *np;                                 // refill candidate
-        apply(e, v);
-        if (entry_n4(e) == 0u) break;                           // a 13-bit code or no code
+      // Hot loop: whole table entries, each lane until its own limit (pipelined the same way).
+      if (rem4 > fast_lim) {
+        uint32_t e = lookup(), v = *np;                         // entry, refill candidate
+        while (true) {
+          put(e);
+          step(e, v);
+          const uint32_t en = lookup(), vn = *np;
+          keep_reads_here();
+          place(e);
+          if (entry_n4(e) == 0u || rem4 <= fast_lim) break;     // a 13-bit code or no code; or done
+          e = en;
+          v = vn;
+        }
       }
       const bool need = rem4 > lim;
       if (!__builtin_amdgcn_ballot_w64(need)) break;
