@@ -42,7 +42,9 @@
  *   - vexp:    64 raw exponent bytes per verbatim segment, in segment order.
  *   - words:   Huffman stream of the palette indices of every non-verbatim segment (segment
  *              order, column ascending), codes MSB-first in uint32 words, two zero words after.
- *              Code: optimal length-limited (13 bits) prefix code, canonical.
+ *              Code: canonical prefix code, at most 13 bits a code (the format's limit);
+ *              uw_encode writes the optimal code limited to 12 bits (lmax = 12 in the header),
+ *              so that every code fits the decoders' 2^12-entry, 16 KB lookup table.
  *   - off:     uint32 start bit of every chunk, then the total bit count.  A chunk is at most
  *              `chunk` coded symbols (a multiple of 64); chunks restart at every 64-column
  *              block of every tile, so block b of a tile holds ceil(64*coded rows/chunk).

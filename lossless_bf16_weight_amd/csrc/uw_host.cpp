@@ -66,10 +66,15 @@ static void parallel_ranges(int64_t n, int nthreads, F&& fn) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Huffman code construction (Huffman paragraph): package-merge with a 13-bit limit.
+// Huffman code construction (Huffman paragraph): package-merge with a 12-bit limit, so that
+// every code fits the decoder's 2^12-entry lookup table (16 KB: the size the SM-split
+// paragraph gives the decode kernel's table).  Blobs may hold codes up to kLmax = 13 bits;
+// the decoders take those too (the row decoder through a few secondary table entries).
 // Tie rules: leaves ordered by (weight, symbol); when merging, a leaf precedes a package of
 // equal weight; a trailing odd item is dropped when packaging.
 // ---------------------------------------------------------------------------------------
+constexpr int kLmaxEncode = 12;
+
 struct PMItem {
   uint64_t w;
   uint8_t cnt[16];  // how many times each symbol occurs inside this item
@@ -341,7 +346,7 @@ static uw_status encode_impl(const uint16_t* w, int64_t n, int64_t k, const uw_p
     for (int s = 0; s < 16; ++s) freq[s] += tile_freq[(size_t)t * 16 + s];
   uint8_t len[16];
   uint16_t code[16];
-  package_merge(freq, kLmax, len);
+  package_merge(freq, kLmaxEncode, len);
   canonical_codes(len, code);
 
   // Per-tile prefix sums: verbatim segments, bits, chunks.
@@ -378,7 +383,7 @@ static uw_status encode_impl(const uint16_t* w, int64_t n, int64_t k, const uw_p
   h->tile_rows = kTileRows;
   h->seg = kSeg;
   h->chunk = (uint32_t)chunk;
-  h->lmax = kLmax;
+  h->lmax = kLmaxEncode;
   h->n_pal = pal.n;
   h->n_verb = (uint32_t)n_verb;
   h->n_coded = n_coded;
@@ -465,14 +470,14 @@ uw_status validate_blob(const void* blob, size_t bytes, uw_info* info) {
   if (h->n < 1 || h->k < (uint32_t)kSeg || h->k % kSeg || h->k > kMaxK || h->n > (1u << 24))
     return fail(UW_E_FORMAT, "bad shape %u x %u", h->n, h->k);
   if (h->chunk < (uint32_t)kSeg || h->chunk > UW_MAX_CHUNK || h->chunk % kSeg) return fail(UW_E_FORMAT, "bad chunk %u", h->chunk);
-  if (h->lmax != kLmax) return fail(UW_E_FORMAT, "unsupported code length limit %u", h->lmax);
+  if (h->lmax < 1 || h->lmax > (uint32_t)kLmax) return fail(UW_E_FORMAT, "unsupported code length limit %u", h->lmax);
   if (h->n_pal < 1 || h->n_pal > 16) return fail(UW_E_FORMAT, "bad palette size %u", h->n_pal);
   for (uint32_t i = 1; i < h->n_pal; ++i)
     if (h->palette[i] <= h->palette[i - 1]) return fail(UW_E_FORMAT, "palette not strictly ascending");
   uint64_t kraft = 0;
   int nsym = 0;
   for (int s = 0; s < 16; ++s) {
-    if (h->code_len[s] > kLmax) return fail(UW_E_FORMAT, "code length > 13");
+    if (h->code_len[s] > h->lmax) return fail(UW_E_FORMAT, "code length %u above the limit %u", (unsigned)h->code_len[s], h->lmax);
     if (h->code_len[s] && s >= (int)h->n_pal) return fail(UW_E_FORMAT, "code for a symbol outside the palette");
     if (h->code_len[s]) {
       kraft += 1ull << (kLmax - h->code_len[s]);

@@ -54,7 +54,8 @@ import numpy as np
 TILE_ROWS = 16          # rows per tile (R8)
 SEG = 64                # weights per verbatim segment along K (R1)
 KSUB = 16               # columns per sub-tile (R8)
-LMAX = 13               # maximum Huffman code length (R5)
+LMAX = 12               # the encoder's Huffman code length limit (R5)
+LMAX_FORMAT = 13        # the longest code a blob may hold: decoders take codes up to this (R5)
 DEFAULT_CHUNK = 512     # coded symbols per chunk (R7)
 PALETTE_SIZE = 16       # top-16 exponents (exponent-distribution paragraph)
 NONE = 0xFF             # index_of[] value for an exponent outside the palette
@@ -425,6 +426,8 @@ def parse(blob):
              total_bits=total_bits, n_chunks=n_chunks, n_words=n_words,
              palette=np.frombuffer(blob, np.uint8, n_pal, 64).copy(),
              lengths=list(blob[80:96]), codes=list(struct.unpack_from("<16H", blob, 96)))
+    if not 1 <= lmax <= LMAX_FORMAT or max(d["lengths"]) > lmax:
+        raise ValueError("code lengths above the limit")
     dtypes = dict(sm=np.uint8, flags="<u2", vprefix="<u4", vexp=np.uint8, cbase="<u4", off="<u4", words="<u4")
     for i, name in enumerate(SECTION_NAMES):
         o, sz = struct.unpack_from("<QQ", blob, 128 + 16 * i)
@@ -440,14 +443,14 @@ def parse(blob):
 def canonical_decode_tables(lengths):
     """Textbook canonical decoding tables: count[L], first code of length L, position in
     (length, symbol) order of the first symbol of length L."""
-    count = [0] * (LMAX + 2)
+    count = [0] * (LMAX_FORMAT + 2)
     for L in lengths:
         if L:
             count[L] += 1
     order = sorted((s for s, L in enumerate(lengths) if L > 0), key=lambda s: (lengths[s], s))
-    first, first_pos = [0] * (LMAX + 2), [0] * (LMAX + 2)
+    first, first_pos = [0] * (LMAX_FORMAT + 2), [0] * (LMAX_FORMAT + 2)
     code, pos = 0, 0
-    for L in range(1, LMAX + 1):
+    for L in range(1, LMAX_FORMAT + 1):
         code = (code + count[L - 1]) << 1 if L > 1 else 0
         first[L], first_pos[L] = code, pos
         pos += count[L]
@@ -468,7 +471,7 @@ def decode_sequential(words, n_symbols, lengths, codes):
             if (L, code) in table:
                 out.append(table[(L, code)])
                 break
-            if L > LMAX:
+            if L > LMAX_FORMAT:
                 raise ValueError("invalid code at bit %d" % pos)
     return np.array(out, dtype=np.int64), pos
 
@@ -489,13 +492,13 @@ def decode_chunks(words, off, chunk_len, lengths):
         p = pos[act]
         wi = p >> 5
         pair = (words64[wi] << np.uint64(32)) | words64[wi + 1]
-        window = ((pair >> (np.uint64(64 - LMAX) - (p & 31).astype(np.uint64))) & np.uint64((1 << LMAX) - 1)).astype(np.int64)
+        window = ((pair >> (np.uint64(64 - LMAX_FORMAT) - (p & 31).astype(np.uint64))) & np.uint64((1 << LMAX_FORMAT) - 1)).astype(np.int64)
         sym = np.full(len(act), -1, dtype=np.int64)
         ln = np.zeros(len(act), dtype=np.int64)
-        for L in range(1, LMAX + 1):
+        for L in range(1, LMAX_FORMAT + 1):
             if count[L] == 0:
                 continue
-            c = window >> (LMAX - L)
+            c = window >> (LMAX_FORMAT - L)
             hit = (sym < 0) & (c >= first[L]) & (c < first[L] + count[L])
             sym[hit] = order[first_pos[L] + c[hit] - first[L]]
             ln[hit] = L

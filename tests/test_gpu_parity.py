@@ -148,6 +148,41 @@ def test_row_decoder_table_source(name, chunk, in_kernel, monkeypatch):
     assert ex.cpu().numpy().tobytes() == codec.exponent_stream_blob(ref_blob).tobytes()
 
 
+@pytest.mark.parametrize("name", ["tiles_160x1024", "ragged_37x192"])
+@pytest.mark.parametrize("chunk", [256, 512, 1024])
+@pytest.mark.parametrize("in_kernel", [True, False])
+def test_decoders_13_bit_codes(name, chunk, in_kernel, monkeypatch):
+    """The encoders limit codes to 12 bits, but a blob may hold codes of up to 13 (the format's
+    limit).  Oracle blobs written at that limit hold 13-bit codes for these inputs; every decoder
+    (the row decoder through its secondary table entries, with either table source; the general
+    decoder at 1024-symbol chunks) decodes them bit-exact."""
+    if in_kernel:
+        monkeypatch.setenv("UW_ROW_TABLE_IN_KERNEL", "1")
+    else:
+        monkeypatch.delenv("UW_ROW_TABLE_IN_KERNEL", raising=False)
+    t = torch()
+    w = CASES[name]()
+    n, k = w.shape
+    enc = codec.encode(w, n, k, chunk=chunk, lmax=13)
+    assert max(enc["lengths"]) == 13
+    ref_blob = codec.serialize(enc)
+    cm = uw.CompressedMatrix(w, chunk=chunk, blob=np.frombuffer(ref_blob, np.uint8).copy())
+    assert cm.info["lmax"] == 13
+    ws = err_ws()
+    out = t.empty((n, k), dtype=t.int16, device="cuda")
+    uw.uw_decode_full(cm.d, out, ws)
+    uw.uw_check(ws)
+    assert np.array_equal(host_u16(out), w)
+    idx = t.empty(int(cm.info["idx_bytes"]), dtype=t.uint8, device="cuda")
+    uw.uw_transcode_palette(cm.d, idx, ws)
+    uw.uw_check(ws)
+    assert idx.cpu().numpy().tobytes() == codec.transcode_blob(ref_blob).tobytes()
+    ex = t.empty(int(cm.info["np"]) * k, dtype=t.uint8, device="cuda")
+    uw.uw_decode_exponents(cm.d, ex, ws)
+    uw.uw_check(ws)
+    assert ex.cpu().numpy().tobytes() == codec.exponent_stream_blob(ref_blob).tobytes()
+
+
 @settings(max_examples=25, deadline=None, derandomize=True, suppress_health_check=[HealthCheck.too_slow])
 @given(matrices(max_rows=70, max_blocks=8), st.sampled_from([64, 256, 512]), st.integers(1, 40))
 def test_generated_matrices(w, chunk, m):

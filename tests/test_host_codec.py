@@ -159,6 +159,20 @@ def test_blob_info_fields():
     assert info["affine"] == int(all(enc["palette"][i] == enc["palette"][0] + i for i in range(len(enc["palette"]))))
 
 
+def test_code_length_limits():
+    """The encoders limit codes to 12 bits (every code fits the decoder's 2^12-entry table); a
+    blob may hold codes up to the format's 13 bits, and such a blob (the oracle writes one when
+    asked for that limit) parses with its limit reported."""
+    w = synth.small_gaussian(160, 1024, seed=4, plant_frac=0.02)["w"]
+    blob = uw.uw_encode(w)
+    info = uw.uw_blob_info(blob)
+    assert info["lmax"] == 12 and max(codec.parse(blob)["lengths"]) <= 12
+    enc13 = codec.encode(w, 160, 1024, lmax=13)
+    assert max(enc13["lengths"]) == 13
+    info13 = uw.uw_blob_info(np.frombuffer(codec.serialize(enc13), np.uint8).copy())
+    assert info13["lmax"] == 13 and info13["total_bits"] == enc13["total_bits"]
+
+
 def test_encode_bound_covers_worst_case():
     for w in (CASES[7][1](), CASES[4][1](), synth.small_gaussian(40, 128, seed=1)["w"]):
         n, k = w.shape
@@ -195,6 +209,8 @@ def test_blob_validation_rejects_corruption():
         corrupt(blob, 12, (100).to_bytes(4, "little")),                    # k not a multiple of 64
         corrupt(blob, 24, (100).to_bytes(4, "little")),                    # chunk
         corrupt(blob, 80, bytes([1, 1, 1] + [0] * 13)),                     # Kraft violated
+        corrupt(blob, 28, (14).to_bytes(4, "little")),                     # limit above the format's 13
+        corrupt(blob, 28, (2).to_bytes(4, "little")),                      # a code above the stated limit
         corrupt(blob, 96, (5).to_bytes(2, "little")),                      # non-canonical code
         corrupt(blob, 128 + 16 * 6 + 8, (10 ** 9).to_bytes(8, "little")),  # words section size
         blob[: blob.size - 512],                                           # truncated
