@@ -733,16 +733,32 @@ __device__ __forceinline__ void decode_unit(const RowDecArgs& a, uint32_t* lut, 
   u32x4 svp[kBf16 ? kPhaseRows : 1][4];         // the current phase's rows' sign+mantissa bytes
   // Rows q0 .. q0 + nq - 1 (words w[8 i .. 8 i + 7] of 4-bit indices in sequence order for row
   // q0 + i) to the index or exponent output, sub-tile by sub-tile.
+  // Index rows go out in pairs: two adjacent rows of a sub-tile are 16 contiguous bytes, one
+  // store instead of two (the scattered output stores, not the decode, had become the larger
+  // cost: half the store instructions and twice the bytes a lane-request).  A pair split by a
+  // verbatim or padding row takes two 8-byte stores, in a branch the wave skips when no lane
+  // needs it.
   auto put_rows = [&](int q0, int nq, const uint32_t* w) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
 #pragma unroll
-      for (int i = 0; i < nq; ++i) {
+      for (int i = 0; i < nq; i += (MODE == DEC_IDX ? 2 : 1)) {
         const int q = q0 + i;
         const uint32_t sub = (uint32_t)(bl * 4 + g) * 16 + rowq[q];
         if constexpr (MODE == DEC_IDX) {
           const u32x2 v{nibbles_to_index_word(w[8 * i + 2 * g]), nibbles_to_index_word(w[8 * i + 2 * g + 1])};
-          __builtin_amdgcn_raw_buffer_store_b64(v, ors, q < nrows ? sub * 8 : kOob, 0, 0);
+          if (i + 1 < nq) {
+            const u32x2 v1{nibbles_to_index_word(w[8 * (i + 1) + 2 * g]), nibbles_to_index_word(w[8 * (i + 1) + 2 * g + 1])};
+            const bool pair = q + 1 < nrows && rowq[q + 1] == rowq[q] + 1u;
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4{v.x, v.y, v1.x, v1.y}, ors, pair ? sub * 8 : kOob, 0, 0);
+            if (!pair && q < nrows) {
+              __builtin_amdgcn_raw_buffer_store_b64(v, ors, sub * 8, 0, 0);
+              const uint32_t sub1 = (uint32_t)(bl * 4 + g) * 16 + rowq[q + 1];
+              __builtin_amdgcn_raw_buffer_store_b64(v1, ors, q + 1 < nrows ? sub1 * 8 : kOob, 0, 0);
+            }
+          } else {
+            __builtin_amdgcn_raw_buffer_store_b64(v, ors, q < nrows ? sub * 8 : kOob, 0, 0);
+          }
         } else {
           const u32x2 e0 = seq_word_to_exps(w[8 * i + 2 * g], a.tab), e1 = seq_word_to_exps(w[8 * i + 2 * g + 1], a.tab);
           __builtin_amdgcn_raw_buffer_store_b128(u32x4{e0.x, e0.y, e1.x, e1.y}, ors, q < nrows ? sub * 16 : kOob, 0, 0);
